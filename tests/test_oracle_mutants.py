@@ -1,0 +1,51 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins
+catch every one (CPU only; the copy is built in a temporary folder and the pin
+suite runs against it in a child process, so a crash counts as caught)."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("sign", "dst[c] += v * src[c];", "dst[c] -= v * src[c];"),
+    ("dropped_last_entry", "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1]; ++p) {\n"
+     "                int64_t r = layout", "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1] - 1; ++p) {\n"
+     "                int64_t r = layout"),
+    ("transposed_layout", "int64_t r = layout == 1 ? s : indices[p];\n                int64_t c = layout == 1 ? indices[p] : s;",
+     "int64_t r = layout == 2 ? s : indices[p];\n                int64_t c = layout == 2 ? indices[p] : s;"),
+    ("first_group_value", "entry(dir, r, c, values[k], B, w, out, want);",
+     "entry(dir, r, c, values[major_ptr[s]], B, w, out, want);"),
+    ("transposed_operand", "if (!want || want[r]) axpy(v, B + c * w, out + r * w, w);",
+     "if (!want || want[r]) axpy(v, B + c * w, out + c * w, w);"),
+    ("csr_value_index", "entry(dir, r, col[p], val[p], B, w, out, want);",
+     "entry(dir, r, col[p], val[r], B, w, out, want);"),
+    ("transpose_count_offset", "cursor[idx[p] + 1] += 1;", "cursor[idx[p]] += 1;"),
+    ("transpose_reverse_order", "for (int64_t s = 0; s < n_major; ++s)\n        for (int64_t p = ptr[s]; p < ptr[s + 1]; ++p) {\n            int64_t at",
+     "for (int64_t s = n_major - 1; s >= 0; --s)\n        for (int64_t p = ptr[s]; p < ptr[s + 1]; ++p) {\n            int64_t at"),
+    ("raw_bit_order", "return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);", "return bits;"),
+    ("expand_ptr", "ptr[s] = value_ptr[major_ptr[s]];", "ptr[s] = major_ptr[s];"),
+    ("validate_monotone", "if (ptr[i + 1] < ptr[i]) return ORC_BAD_MONOTONE;",
+     "if (ptr[i + 1] < ptr[i] - 1) return ORC_BAD_MONOTONE;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = oracle.build(str(mutant), str(tmp_path / "liboracle_mutant.so"))
+    env = dict(os.environ, ORACLE_LIB=lib)
+    res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                          "-k", "not footprint"], cwd=ROOT, env=env, capture_output=True,
+                         text=True, timeout=600)
+    assert res.returncode != 0, f"planted mistake '{name}' passed every pin:\n{res.stdout[-2000:]}"
