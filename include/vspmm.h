@@ -1,0 +1,204 @@
+/*
+ * libvspmm: row-segmented sparse x dense products (SpMM, and SpMV at width 1)
+ * over CSR and the value-grouped VCSR/VCSC layouts, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Layouts
+ *  - VCSR / VCSC, defined on the vsparse page ("Add CUDA transfer and matmul
+ *    kernels for the normalized views", section "The layout stays
+ *    compressed"): for major slice i (row i of a VCSR, column i of a VCSC) the
+ *    distinct values are values[major_ptr[i] .. major_ptr[i+1]) and value k is
+ *    shared by the minor indices indices[value_ptr[k] .. value_ptr[k+1]).
+ *    Values are float32 on the device (same page, opening paragraph).
+ *  - CSR, the single-matrix operator of the regridding page ("Regridder",
+ *    sections "How it is built" and "API"): row i holds col[row_ptr[i] ..
+ *    row_ptr[i+1]) with one value each, float32 or float64.
+ *  Every stored entry (r, c, v) adds v to A[r][c]: repeated indices, empty
+ *  groups and explicit zeros are legal and sum. The matrix is never expanded:
+ *  a handle borrows the caller's arrays as they are.
+ *
+ * Directions (vsparse page, section "The kernels"): out = A @ B (VSPMM_AB) and
+ * out = B @ A (VSPMM_BA). Dense operands are row-major with the width
+ * contiguous and indexed by the sparse axis they meet:
+ *  - VSPMM_AB: B is n_cols x width, out is n_rows x width.
+ *  - VSPMM_BA: B is passed transposed, n_rows x width, and out is written
+ *    transposed, n_cols x width.
+ * A direction is "aligned" when the output's rows are the layout's major
+ * slices (VCSR @ B, B @ VCSC, CSR @ B) and "misaligned" otherwise (B @ VCSR,
+ * VCSC @ B, B @ CSR). Aligned products accumulate per slice in registers and
+ * repeat bit for bit. Misaligned products scatter with hardware float atomics
+ * (VSPMM_ATOMIC; last bits vary run to run) or, with VSPMM_DETERMINISTIC, first
+ * build the matrix in the opposite layout in a caller-owned workspace and then
+ * run the aligned walk over it, which repeats bit for bit.
+ *
+ * Conventions
+ *  - All pointers passed as "device" must be device memory of the current HIP
+ *    device (e.g. torch CUDA tensors); host pointers are marked "host".
+ *  - Index and pointer arrays are int32. Pointer arrays start at 0 and do not
+ *    decrease; indices lie in [0, n_minor). Those rules are only checked by
+ *    vspmm_validate (or VSPMM_VALIDATE at create); a product over a structure
+ *    that breaks them is undefined.
+ *  - out is overwritten, never accumulated into. width == 0 or an empty
+ *    output returns VSPMM_OK without a launch; nnz == 0 zero-fills out.
+ *  - Every call returns a status; nothing throws across this interface.
+ *    Argument checks run on the host before anything is enqueued; a failed
+ *    check enqueues nothing. Launch errors return VSPMM_ERR_HIP.
+ *  - Work is enqueued on the given stream and returns before it finishes,
+ *    except vspmm_validate, which waits for its result.
+ *  - Handles are immutable after creation apart from the workspace cache
+ *    tag (guarded by a lock), so products on different streams may run
+ *    concurrently if their outputs and workspaces are distinct.
+ */
+#ifndef VSPMM_H
+#define VSPMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct vspmm_matrix_s *vspmm_matrix; /* opaque handle */
+
+typedef enum {
+    VSPMM_OK = 0,
+    VSPMM_ERR_NULL = 1,        /* a required pointer is NULL */
+    VSPMM_ERR_DIM = 2,         /* negative or inconsistent extent, or above int32 */
+    VSPMM_ERR_ENUM = 3,        /* unknown layout, direction, dtype, mode or flag */
+    VSPMM_ERR_STRUCTURE = 4,   /* vspmm_validate found a malformed structure */
+    VSPMM_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+    VSPMM_ERR_UNSUPPORTED = 6, /* valid request this library does not serve */
+    VSPMM_ERR_HIP = 7,         /* a HIP call or kernel launch failed */
+    VSPMM_ERR_ALLOC = 8        /* host allocation failed */
+} vspmm_status;
+
+typedef enum { VSPMM_CSR = 0, VSPMM_VCSR = 1, VSPMM_VCSC = 2 } vspmm_layout;
+typedef enum { VSPMM_AB = 0, VSPMM_BA = 1 } vspmm_direction;
+typedef enum { VSPMM_F32 = 0, VSPMM_F64 = 1 } vspmm_dtype;
+typedef enum { VSPMM_ATOMIC = 0, VSPMM_DETERMINISTIC = 1 } vspmm_mode;
+
+/* Creation flags. The lane split (vsparse page, section "The kernels";
+ * regridding page, section "How it is built") picks, per product, how many
+ * lanes of a 64-lane wave cover the dense width and how many walk the slice's
+ * entries.
+ *  - VSPMM_SPLIT_WIDTH: the split follows the width (the default for VCS).
+ *  - VSPMM_SPLIT_MATRIX: the number of entry lanes follows the matrix, the
+ *    power of two at or below its mean entries per slice, at most 64 (the
+ *    default for CSR). It does not depend on the width, so each column of a
+ *    batch gets exactly the bits it gets alone.
+ *  - VSPMM_VALIDATE: run vspmm_validate during creation. */
+enum { VSPMM_SPLIT_WIDTH = 1u, VSPMM_SPLIT_MATRIX = 2u, VSPMM_VALIDATE = 4u };
+
+/* Create a handle over a VCSR or VCSC held in device memory.
+ *  layout      VSPMM_VCSR (major = rows) or VSPMM_VCSC (major = columns).
+ *  n_rows, n_cols  shape of A; n_groups = length of values; nnz = length of
+ *              indices. All must fit in int32.
+ *  major_ptr   device int32[n_major + 1]; values device float[n_groups];
+ *  value_ptr   device int32[n_groups + 1]; indices device int32[nnz].
+ *              Borrowed: they must stay alive and unchanged until
+ *              vspmm_destroy. May be NULL only when their length is 0.
+ *  flags       VSPMM_SPLIT_* / VSPMM_VALIDATE.
+ *  force_group 0, or a power of two 1..64 fixing the number of entry lanes
+ *              per slice (tests use it to cover every split).
+ *  stream      stream used by VSPMM_VALIDATE.
+ * Errors: VSPMM_ERR_NULL, _DIM, _ENUM, _STRUCTURE (with VSPMM_VALIDATE),
+ * _HIP, _ALLOC. *h is set only on success. */
+vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_rows,
+                              int64_t n_cols, int64_t n_groups, int64_t nnz,
+                              const int32_t *major_ptr, const float *values,
+                              const int32_t *value_ptr, const int32_t *indices,
+                              uint32_t flags, int32_t force_group, hipStream_t stream);
+
+/* Create a handle over a CSR held in device memory (rows are the major axis).
+ *  row_ptr device int32[n_rows + 1]; col device int32[nnz];
+ *  val device float[nnz] (VSPMM_F32) or double[nnz] (VSPMM_F64).
+ *  The dense operands of every product on this handle have the same dtype
+ *  and the sums are carried in it. Other arguments as vspmm_create_vcs. */
+vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                              const int32_t *row_ptr, const int32_t *col, const void *val,
+                              vspmm_dtype dtype, uint32_t flags, int32_t force_group,
+                              hipStream_t stream);
+
+/* Release the handle (host memory only; the borrowed arrays are untouched). */
+vspmm_status vspmm_destroy(vspmm_matrix h);
+
+/* out = A @ B or B @ A (see Directions), atomic mode for misaligned
+ * directions, no workspace. B and out: device arrays of the handle's dtype,
+ * row-major with `width` contiguous elements per row; they must not overlap.
+ * Errors: _NULL, _DIM (width < 0), _ENUM, _HIP. */
+vspmm_status vspmm_spmm(vspmm_matrix h, const void *B, void *out, int64_t width,
+                        vspmm_direction dir, hipStream_t stream);
+
+/* Bytes of workspace vspmm_spmm_ex needs for (dir, mode) (0 when none).
+ * bytes: host. */
+vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
+                                  size_t *bytes);
+
+/* vspmm_spmm with a mode. VSPMM_DETERMINISTIC on a misaligned direction
+ * builds, on the first call with a given workspace, the matrix in the opposite
+ * layout (CSR: its exact transpose; VCSR/VCSC: the same matrix regrouped by
+ * the other axis) inside ws, and runs the aligned walk over it. Later calls
+ * with the same handle, direction and ws reuse what is there: the caller must
+ * not write into ws between them, or must call vspmm_workspace_invalidate.
+ * ws: device, 256-byte aligned, at least vspmm_workspace_size bytes; unused
+ * (may be NULL) when the size is 0. Errors: as vspmm_spmm, plus
+ * _WORKSPACE. */
+vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t width,
+                           vspmm_direction dir, vspmm_mode mode, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* Forget any schedule cached in the workspace at ws (call before reusing
+ * that memory for anything else). */
+vspmm_status vspmm_workspace_invalidate(void *ws);
+
+/* Check the structure on the device: pointer arrays start at 0, do not
+ * decrease and end at their array's length; every index is in range. Waits
+ * on `stream` for the answer. Returns VSPMM_OK or VSPMM_ERR_STRUCTURE. */
+vspmm_status vspmm_validate(vspmm_matrix h, hipStream_t stream);
+
+/* The exact transpose of a CSR handle by a stable counting sort (regridding
+ * page, section "How it is built": counts per row, then placement at the rows'
+ * cursors in source order), equal bit for bit to a sequential counting sort.
+ * Outputs (device): t_row_ptr int32[n_cols + 1], t_col int32[nnz], t_val of
+ * the handle's dtype [nnz]. ws: device, vspmm_workspace_size(h, VSPMM_BA,
+ * VSPMM_DETERMINISTIC) bytes. Errors: _NULL, _ENUM (not CSR), _WORKSPACE,
+ * _HIP. */
+vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_col,
+                                 void *t_val, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The matrix of a VCSR handle as a VCSC, or of a VCSC handle as a VCSR,
+ * canonical for the input: each new slice groups its entries by value, the
+ * groups in ascending value (IEEE total order on the bits, -0 before +0) and
+ * the entries of a group in stored order (ascending old slice). Outputs
+ * (device): t_major_ptr int32[n_minor + 1], t_values float[nnz],
+ * t_value_ptr int32[nnz + 1], t_indices int32[nnz], t_n_groups int32[1] (the
+ * number of groups written). ws as for the deterministic misaligned product.
+ * Errors: _NULL, _ENUM (not VCS), _WORKSPACE, _HIP. */
+vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_values,
+                               int32_t *t_value_ptr, int32_t *t_indices,
+                               int32_t *t_n_groups, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* Device bytes the handle's arrays occupy, and what the same matrix would take
+ * expanded to one value per entry in the same major order (int32 pointers and
+ * indices). Both host. */
+vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_bytes);
+
+/* The lane split a product would use (host outputs, any may be NULL):
+ * entry lanes per slice, width lanes, elements per lane, slices per wave and
+ * whether the gathered operand is staged in LDS. */
+vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
+                             vspmm_mode mode, int32_t *entry_lanes, int32_t *width_lanes,
+                             int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged);
+
+/* A static string naming the status. */
+const char *vspmm_status_string(vspmm_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSPMM_H */

@@ -1,0 +1,327 @@
+"""Python binding of libvspmm (sparse x dense products over CSR, VCSR and VCSC
+on MI355X).
+
+Argument marshalling only: every product, transpose and regrouping runs in the
+HIP kernels of ``libvspmm.so``. torch supplies device memory and the current
+stream. There is no fallback: importing this package without the built library
+raises ImportError, and a call that the library rejects raises VspmmError.
+
+    A = VcsMatrix.from_arrays("vcsr", (m, n), major_ptr, values, value_ptr, indices)
+    out = A @ B          # B: n x w (cuda, float32) -> m x w
+    out = B @ A          # B: w x m -> w x n
+    A.T                  # the transpose, a VCSC over the same arrays
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["VcsMatrix", "CsrMatrix", "VspmmError", "lib", "LIB_PATH", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvspmm.so")
+
+LAYOUTS = {"csr": 0, "vcsr": 1, "vcsc": 2}
+DIRECTIONS = {"AB": 0, "BA": 1}
+MODES = {"atomic": 0, "deterministic": 1}
+SPLIT_WIDTH, SPLIT_MATRIX, VALIDATE = 1, 2, 4
+
+_vp, _i64, _i32, _u32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                              ctypes.c_size_t)
+_P = ctypes.POINTER
+
+# name -> (argtypes, restype); mirrors include/vspmm.h
+EXPORTS = {
+    "vspmm_create_vcs": ([_P(_vp), ctypes.c_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _u32,
+                          _i32, _vp], ctypes.c_int),
+    "vspmm_create_csr": ([_P(_vp), _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_int, _u32, _i32, _vp],
+                         ctypes.c_int),
+    "vspmm_destroy": ([_vp], ctypes.c_int),
+    "vspmm_spmm": ([_vp, _vp, _vp, _i64, ctypes.c_int, _vp], ctypes.c_int),
+    "vspmm_workspace_size": ([_vp, ctypes.c_int, ctypes.c_int, _P(_sz)], ctypes.c_int),
+    "vspmm_spmm_ex": ([_vp, _vp, _vp, _i64, ctypes.c_int, ctypes.c_int, _vp, _sz, _vp],
+                      ctypes.c_int),
+    "vspmm_workspace_invalidate": ([_vp], ctypes.c_int),
+    "vspmm_validate": ([_vp, _vp], ctypes.c_int),
+    "vspmm_transpose_csr": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_regroup_vcs": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_footprint": ([_vp, _P(_sz), _P(_sz)], ctypes.c_int),
+    "vspmm_plan_info": ([_vp, _i64, ctypes.c_int, ctypes.c_int, _P(_i32), _P(_i32), _P(_i32),
+                         _P(_i32), _P(_i32)], ctypes.c_int),
+    "vspmm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m sparse_dense_matmul_amd.build`")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (argtypes, restype) in EXPORTS.items():
+        fn = getattr(handle, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return handle
+
+
+lib = _load()
+
+
+class VspmmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.vspmm_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise VspmmError(status, where)
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _dev_tensor(t, dtype, device, name):
+    t = torch.as_tensor(t)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.contiguous()
+
+
+class SparseMatrix:
+    """A handle over device arrays that it keeps alive (never copied)."""
+
+    layout: str
+    dtype: torch.dtype
+
+    def __init__(self, handle, arrays, shape, layout, dtype, device, flags, force_group):
+        self._h = handle
+        self._arrays = arrays
+        self.shape = tuple(int(x) for x in shape)
+        self.layout = layout
+        self.dtype = dtype
+        self.device = device
+        self.flags = flags
+        self.force_group = force_group
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib.vspmm_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    # ----------------------------------------------------------- products
+
+    def _dense_in(self, B, rows, name="B"):
+        B = _dev_tensor(B, self.dtype, self.device, name)
+        if B.dim() == 1:
+            B = B.unsqueeze(1)
+        if B.dim() != 2 or B.shape[0] != rows:
+            raise ValueError(f"{name} has shape {tuple(B.shape)}, expected ({rows}, width)")
+        return B
+
+    def spmm(self, B: torch.Tensor, direction: str = "AB", mode: str = "atomic",
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+        """``A @ B`` for ``direction="AB"`` (B: n x w, returns m x w), or
+        ``(B @ A)`` transposed for ``direction="BA"`` (B given transposed,
+        m x w; returns n x w). ``mode="deterministic"`` makes the misaligned
+        directions repeat bit for bit (needs ``workspace``, see
+        :meth:`workspace_size`)."""
+        m, n = self.shape
+        n_in, n_out = (n, m) if direction == "AB" else (m, n)
+        B = self._dense_in(B, n_in)
+        w = B.shape[1]
+        if out is None:
+            out = torch.empty((n_out, w), dtype=self.dtype, device=self.device)
+        elif out.shape != (n_out, w) or not out.is_contiguous() or out.dtype != self.dtype:
+            raise ValueError("out must be a contiguous (n_out, width) tensor of the matrix dtype")
+        d, md = DIRECTIONS[direction], MODES[mode]
+        if md == 0:
+            st = lib.vspmm_spmm(self._h, _ptr(B), _ptr(out), w, d, _stream(self.device))
+        else:
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            st = lib.vspmm_spmm_ex(self._h, _ptr(B), _ptr(out), w, d, md, _ptr(workspace),
+                                   ws_bytes, _stream(self.device))
+        _check(st, "vspmm_spmm")
+        return out
+
+    def __matmul__(self, B):
+        B = torch.as_tensor(B)
+        if B.dim() == 1:
+            return self.spmm(B.unsqueeze(1), "AB")[:, 0]
+        return self.spmm(B, "AB")
+
+    def __rmatmul__(self, B):
+        B = torch.as_tensor(B)
+        if B.dim() == 1:
+            return self.spmm(B.unsqueeze(1), "BA")[:, 0]
+        return self.spmm(B.t().contiguous(), "BA").t()
+
+    def workspace_size(self, direction: str = "BA", mode: str = "deterministic") -> int:
+        n = _sz(0)
+        _check(lib.vspmm_workspace_size(self._h, DIRECTIONS[direction], MODES[mode],
+                                        ctypes.byref(n)), "vspmm_workspace_size")
+        return int(n.value)
+
+    def workspace(self, direction: str = "BA", mode: str = "deterministic") -> torch.Tensor:
+        """A fresh device workspace of the required size (256-byte aligned)."""
+        nbytes = self.workspace_size(direction, mode)
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+
+    def validate(self) -> bool:
+        st = lib.vspmm_validate(self._h, _stream(self.device))
+        if st == 4:
+            return False
+        _check(st, "vspmm_validate")
+        return True
+
+    def footprint(self) -> tuple[int, int]:
+        a, b = _sz(0), _sz(0)
+        _check(lib.vspmm_footprint(self._h, ctypes.byref(a), ctypes.byref(b)), "vspmm_footprint")
+        return int(a.value), int(b.value)
+
+    def plan_info(self, width: int, direction: str = "AB", mode: str = "atomic") -> dict:
+        vals = [_i32(0) for _ in range(5)]
+        _check(lib.vspmm_plan_info(self._h, width, DIRECTIONS[direction], MODES[mode],
+                                   *[ctypes.byref(v) for v in vals]), "vspmm_plan_info")
+        keys = ("entry_lanes", "width_lanes", "vec", "slices_per_wave", "lds_staged")
+        return {k: int(v.value) for k, v in zip(keys, vals)}
+
+
+class VcsMatrix(SparseMatrix):
+    """VCSR (``layout="vcsr"``) or VCSC over device arrays: for major slice i
+    the distinct values are ``values[major_ptr[i]:major_ptr[i+1]]`` and value k
+    is shared by ``indices[value_ptr[k]:value_ptr[k+1]]``."""
+
+    @classmethod
+    def from_arrays(cls, layout, shape, major_ptr, values, value_ptr, indices, flags=0,
+                    force_group=0, validate=False):
+        if layout not in ("vcsr", "vcsc"):
+            raise ValueError(layout)
+        dev = torch.as_tensor(major_ptr).device
+        major_ptr = _dev_tensor(major_ptr, torch.int32, dev, "major_ptr")
+        values = _dev_tensor(values, torch.float32, dev, "values")
+        value_ptr = _dev_tensor(value_ptr, torch.int32, dev, "value_ptr")
+        indices = _dev_tensor(indices, torch.int32, dev, "indices")
+        m, n = (int(x) for x in shape)
+        flags = flags | (VALIDATE if validate else 0)
+        h = _vp()
+        with torch.cuda.device(dev):
+            st = lib.vspmm_create_vcs(ctypes.byref(h), LAYOUTS[layout], m, n, values.numel(),
+                                      indices.numel(), _ptr(major_ptr), _ptr(values),
+                                      _ptr(value_ptr), _ptr(indices), flags, force_group,
+                                      _stream(dev))
+        _check(st, "vspmm_create_vcs")
+        return cls(h, (major_ptr, values, value_ptr, indices), (m, n), layout, torch.float32, dev,
+                   flags, force_group)
+
+    @property
+    def major_ptr(self):
+        return self._arrays[0]
+
+    @property
+    def values(self):
+        return self._arrays[1]
+
+    @property
+    def value_ptr(self):
+        return self._arrays[2]
+
+    @property
+    def indices(self):
+        return self._arrays[3]
+
+    @property
+    def T(self) -> "VcsMatrix":
+        """The transpose: the same arrays read as the other layout."""
+        other = "vcsc" if self.layout == "vcsr" else "vcsr"
+        return VcsMatrix.from_arrays(other, (self.shape[1], self.shape[0]), *self._arrays,
+                                     flags=self.flags & ~VALIDATE, force_group=self.force_group)
+
+    def regroup(self, workspace: torch.Tensor | None = None) -> "VcsMatrix":
+        """The same matrix in the opposite layout (VCSR <-> VCSC), canonical."""
+        m, n = self.shape
+        n_minor = n if self.layout == "vcsr" else m
+        nnz = self.indices.numel()
+        dev = self.device
+        t_mp = torch.empty(n_minor + 1, dtype=torch.int32, device=dev)
+        t_v = torch.empty(max(nnz, 1), dtype=torch.float32, device=dev)
+        t_vp = torch.empty(nnz + 1, dtype=torch.int32, device=dev)
+        t_i = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        t_g = torch.empty(1, dtype=torch.int32, device=dev)
+        ws = workspace if workspace is not None else self.workspace("BA" if self.layout == "vcsr"
+                                                                    else "AB")
+        st = lib.vspmm_regroup_vcs(self._h, _ptr(t_mp), _ptr(t_v), _ptr(t_vp), _ptr(t_i),
+                                   _ptr(t_g), _ptr(ws), ws.numel(), _stream(dev))
+        _check(st, "vspmm_regroup_vcs")
+        g = int(t_g.item())
+        other = "vcsc" if self.layout == "vcsr" else "vcsr"
+        return VcsMatrix.from_arrays(other, self.shape, t_mp, t_v[:g].clone(),
+                                     t_vp[:g + 1].clone(), t_i[:nnz].clone(), flags=self.flags,
+                                     force_group=self.force_group)
+
+
+class CsrMatrix(SparseMatrix):
+    """CSR over device arrays, float32 or float64."""
+
+    @classmethod
+    def from_arrays(cls, shape, row_ptr, col, val, flags=0, force_group=0, validate=False):
+        dev = torch.as_tensor(row_ptr).device
+        val = torch.as_tensor(val)
+        if val.dtype not in (torch.float32, torch.float64):
+            raise TypeError(f"val must be float32 or float64, got {val.dtype}")
+        row_ptr = _dev_tensor(row_ptr, torch.int32, dev, "row_ptr")
+        col = _dev_tensor(col, torch.int32, dev, "col")
+        val = _dev_tensor(val, val.dtype, dev, "val")
+        m, n = (int(x) for x in shape)
+        flags = flags | (VALIDATE if validate else 0)
+        h = _vp()
+        with torch.cuda.device(dev):
+            st = lib.vspmm_create_csr(ctypes.byref(h), m, n, col.numel(), _ptr(row_ptr),
+                                      _ptr(col), _ptr(val), 1 if val.dtype == torch.float64 else 0,
+                                      flags, force_group, _stream(dev))
+        _check(st, "vspmm_create_csr")
+        return cls(h, (row_ptr, col, val), (m, n), "csr", val.dtype, dev, flags, force_group)
+
+    @property
+    def row_ptr(self):
+        return self._arrays[0]
+
+    @property
+    def col(self):
+        return self._arrays[1]
+
+    @property
+    def val(self):
+        return self._arrays[2]
+
+    def transpose(self, workspace: torch.Tensor | None = None) -> "CsrMatrix":
+        """The exact transpose (each new row lists its entries by ascending
+        source row), bit-identical to a sequential counting sort."""
+        m, n = self.shape
+        nnz = self.col.numel()
+        dev = self.device
+        t_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        t_col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        t_val = torch.empty(max(nnz, 1), dtype=self.dtype, device=dev)
+        ws = workspace if workspace is not None else self.workspace("BA")
+        st = lib.vspmm_transpose_csr(self._h, _ptr(t_ptr), _ptr(t_col), _ptr(t_val), _ptr(ws),
+                                     ws.numel(), _stream(dev))
+        _check(st, "vspmm_transpose_csr")
+        return CsrMatrix.from_arrays((n, m), t_ptr, t_col[:nnz], t_val[:nnz],
+                                     flags=self.flags & ~VALIDATE, force_group=self.force_group)

@@ -1,0 +1,321 @@
+// Building a matrix in the opposite layout on the device: the exact CSR
+// transpose and the VCSR <-> VCSC regrouping. Both are a stable sort of the
+// entries by their new slice (regridding page, section "How it is built":
+// count per row, then place at the rows' cursors keeping each row's entries in
+// source order). On the GPU the placement is an LSD radix sort whose scatter
+// ranks equal digits in input order, so every result is unique and equals a
+// sequential counting sort bit for bit, whatever the timing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vspmm {
+
+constexpr int kSortThreads = 256;
+constexpr int kSortRounds = 16;
+constexpr int kSortTile = kSortThreads * kSortRounds;  // elements per block
+constexpr int kScanTile = 4096;                         // elements per block
+
+// ------------------------------------------------------------------- scan
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+// Exclusive scan of 256 per-thread values across a block; returns the prefix.
+__device__ __forceinline__ int block_exclusive_scan(int x, int *sh_waves /*[4]*/, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int inc = wave_inclusive_scan(x, lane);
+    if (lane == 63) sh_waves[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int s = sh_waves[k];
+        if (k < wave) before += s;
+        total += s;
+    }
+    __syncthreads();
+    return before + inc - x;
+}
+
+// Sum of each tile of kScanTile elements.
+__global__ void __launch_bounds__(256) k_scan_reduce(const int *__restrict__ in, int n,
+                                                     int *__restrict__ bsums) {
+    __shared__ int sh[4];
+    const int base = blockIdx.x * kScanTile;
+    int s = 0;
+    for (int r = 0; r < kScanTile / 256; ++r) {
+        const int i = base + r * 256 + threadIdx.x;
+        if (i < n) s += in[i];
+    }
+    int total;
+    block_exclusive_scan(s, sh, total);
+    if (threadIdx.x == 0) bsums[blockIdx.x] = total;
+}
+
+// Exclusive scan of the tile sums in place (one block); *total = their sum.
+__global__ void __launch_bounds__(256) k_scan_bsums(int *__restrict__ bsums, int nb,
+                                                    int *__restrict__ total) {
+    __shared__ int sh[4];
+    int carry = 0;
+    for (int base = 0; base < nb; base += 256) {
+        const int i = base + threadIdx.x;
+        const int x = i < nb ? bsums[i] : 0;
+        int t;
+        const int ex = block_exclusive_scan(x, sh, t);
+        if (i < nb) bsums[i] = carry + ex;
+        carry += t;
+    }
+    if (threadIdx.x == 0 && total) *total = carry;
+}
+
+// Exclusive scan of each tile plus its offset; out may alias in.
+__global__ void __launch_bounds__(256) k_scan_apply(const int *in, int n,
+                                                    const int *__restrict__ bsums, int *out) {
+    __shared__ int tile[kScanTile];
+    __shared__ int sh[4];
+    const int base = blockIdx.x * kScanTile;
+    for (int r = 0; r < kScanTile / 256; ++r) {
+        const int i = base + r * 256 + threadIdx.x;
+        tile[r * 256 + threadIdx.x] = i < n ? in[i] : 0;
+    }
+    __syncthreads();
+    constexpr int per = kScanTile / 256;
+    int s = 0;
+    for (int k = 0; k < per; ++k) s += tile[threadIdx.x * per + k];
+    int total;
+    int run = block_exclusive_scan(s, sh, total) + bsums[blockIdx.x];
+    for (int k = 0; k < per; ++k) {
+        const int x = tile[threadIdx.x * per + k];
+        tile[threadIdx.x * per + k] = run;
+        run += x;
+    }
+    __syncthreads();
+    for (int r = 0; r < kScanTile / 256; ++r) {
+        const int i = base + r * 256 + threadIdx.x;
+        if (i < n) out[i] = tile[r * 256 + threadIdx.x];
+    }
+}
+
+// ------------------------------------------------------------- radix sort
+
+// Digit histogram of each tile: hist[d * nblocks + b].
+__global__ void __launch_bounds__(kSortThreads)
+k_radix_hist(const uint32_t *__restrict__ keys, int n, int shift, int nblocks,
+             int *__restrict__ hist) {
+    __shared__ int h[256];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kSortTile;
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int i = base + r * kSortThreads + threadIdx.x;
+        if (i < n) atomicAdd(&h[(keys[i] >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    hist[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter: each element goes to offs[d * nblocks + b] plus the number of
+// earlier elements of its tile with the same digit.
+__global__ void __launch_bounds__(kSortThreads)
+k_radix_scatter(const uint32_t *__restrict__ keys, const int *__restrict__ pay, int n, int shift,
+                int nblocks, const int *__restrict__ offs, uint32_t *__restrict__ okeys,
+                int *__restrict__ opay) {
+    __shared__ int run[256];
+    __shared__ int wc[4][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    run[threadIdx.x] = offs[threadIdx.x * nblocks + blockIdx.x];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wc[k][threadIdx.x] = 0;
+    __syncthreads();
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int base = blockIdx.x * kSortTile;
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int i = base + r * kSortThreads + threadIdx.x;
+        const bool valid = i < n;
+        const uint32_t k = valid ? keys[i] : 0u;
+        const int d = (int)((k >> shift) & 255u);
+        uint64_t m = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (d >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        const int wrank = __popcll(m & lt);
+        if (valid && wrank == 0) wc[wave][d] = __popcll(m);
+        __syncthreads();
+        if (valid) {
+            int pos = run[d] + wrank;
+            for (int w2 = 0; w2 < wave; ++w2) pos += wc[w2][d];
+            okeys[pos] = k;
+            opay[pos] = pay[i];
+        }
+        __syncthreads();
+        run[threadIdx.x] += wc[0][threadIdx.x] + wc[1][threadIdx.x] + wc[2][threadIdx.x] +
+                            wc[3][threadIdx.x];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) wc[k2][threadIdx.x] = 0;
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------ entry bookkeeping
+
+// For every entry p: the slice holding it (slice_of) and, for a VCS, its group
+// (group_of). One wave per slice; each lane walks its entries with its own
+// group cursor.
+template <bool VCS>
+__global__ void __launch_bounds__(256)
+k_expand(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
+         int *__restrict__ slice_of, int *__restrict__ group_of) {
+    const int lane = threadIdx.x & 63;
+    const int waves = blockDim.x >> 6;
+    for (int s = blockIdx.x * waves + (threadIdx.x >> 6); s < n_slices; s += gridDim.x * waves) {
+        int e0, e1, kc = 0, kend = 0;
+        if constexpr (VCS) {
+            const int ka = sptr[s], kb = sptr[s + 1];
+            e0 = vptr[ka];
+            e1 = vptr[kb];
+            kc = ka;
+            kend = kb > ka ? vptr[ka + 1] : 0;
+        } else {
+            e0 = sptr[s];
+            e1 = sptr[s + 1];
+        }
+        for (int p = e0 + lane; p < e1; p += 64) {
+            slice_of[p] = s;
+            if constexpr (VCS) {
+                while (p >= kend) {
+                    ++kc;
+                    kend = vptr[kc + 1];
+                }
+                group_of[p] = kc;
+            }
+        }
+    }
+}
+
+// Order key of a float32 bit pattern: ascending value, -0 before +0, NaNs
+// beyond the infinities by payload. Equal keys iff equal bits.
+__device__ __forceinline__ uint32_t value_order(uint32_t bits) {
+    return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
+
+__global__ void __launch_bounds__(256)
+k_value_keys(int nnz, const int *__restrict__ group_of, const float *__restrict__ values,
+             uint32_t *__restrict__ keys, int *__restrict__ pay) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride) {
+        keys[p] = value_order(__float_as_uint(values[group_of[p]]));
+        pay[p] = p;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+k_index_keys(int nnz, const int *__restrict__ idx, uint32_t *__restrict__ keys,
+             int *__restrict__ pay) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride) {
+        keys[p] = (uint32_t)idx[p];
+        pay[p] = p;
+    }
+}
+
+// keys[e] = idx[pay[e]] (the new slice of the e-th entry in current order).
+__global__ void __launch_bounds__(256)
+k_gather_index(int nnz, const int *__restrict__ pay, const int *__restrict__ idx,
+               uint32_t *__restrict__ keys) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride)
+        keys[e] = (uint32_t)idx[pay[e]];
+}
+
+// Entries per new slice (cnt zeroed beforehand).
+__global__ void __launch_bounds__(256)
+k_count(int nnz, const int *__restrict__ idx, int *__restrict__ cnt) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride)
+        atomicAdd(&cnt[idx[p]], 1);
+}
+
+// ------------------------------------------------------------- transpose
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_transpose_emit(int nnz, const int *__restrict__ pay, const int *__restrict__ slice_of,
+                 const T *__restrict__ val, int *__restrict__ t_idx, T *__restrict__ t_val) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
+        const int p = pay[e];
+        t_idx[e] = slice_of[p];
+        t_val[e] = val[p];
+    }
+}
+
+// ------------------------------------------------------------- regrouping
+
+// flag[e] = 1 where a new group starts in the sorted order: a new slice, or a
+// value whose bits differ from the previous entry's.
+__global__ void __launch_bounds__(256)
+k_group_flags(int nnz, const int *__restrict__ pay, const uint32_t *__restrict__ slice_key,
+              const int *__restrict__ group_of, const float *__restrict__ values,
+              int *__restrict__ flag) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
+        int f = 1;
+        if (e > 0) {
+            const uint32_t a = __float_as_uint(values[group_of[pay[e]]]);
+            const uint32_t b = __float_as_uint(values[group_of[pay[e - 1]]]);
+            f = (slice_key[e] != slice_key[e - 1]) || (a != b);
+        }
+        flag[e] = f;
+    }
+}
+
+// Writes the regrouped entries; gid holds the exclusive scan of the flags.
+__global__ void __launch_bounds__(256)
+k_group_emit(int nnz, const int *__restrict__ pay, const int *__restrict__ slice_of,
+             const int *__restrict__ group_of, const float *__restrict__ values,
+             const int *__restrict__ flag, const int *__restrict__ gid,
+             float *__restrict__ t_values, int *__restrict__ t_value_ptr,
+             int *__restrict__ t_indices) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
+        const int p = pay[e];
+        t_indices[e] = slice_of[p];
+        if (flag[e]) {
+            const int g = gid[e];
+            t_values[g] = values[group_of[p]];
+            t_value_ptr[g] = e;
+        }
+    }
+}
+
+// t_major_ptr[j] = first group of new slice j = gid at the slice's first
+// entry (entry offsets tptr), or the group count at the end.
+__global__ void __launch_bounds__(256)
+k_group_major_ptr(int n_minor, int nnz, const int *__restrict__ tptr, const int *__restrict__ gid,
+                  const int *__restrict__ n_groups, int *__restrict__ t_major_ptr,
+                  int *__restrict__ t_value_ptr, int *__restrict__ t_n_groups) {
+    const int stride = gridDim.x * blockDim.x;
+    const int G = *n_groups;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j <= n_minor; j += stride) {
+        const int t = j < n_minor ? tptr[j] : nnz;
+        t_major_ptr[j] = t < nnz ? gid[t] : G;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        t_value_ptr[G] = nnz;
+        if (t_n_groups) *t_n_groups = G;
+    }
+}
+
+}  // namespace vspmm

@@ -1,0 +1,742 @@
+// libvspmm: the C interface declared in include/vspmm.h. Host-side checks,
+// the per-call plan (lane split, grid), kernel launches, and the device
+// builders of the opposite layout for the deterministic misaligned products.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_map>
+
+#include "../../include/vspmm.h"
+#include "schedule.hpp"
+#include "walk.hpp"
+
+using namespace vspmm;
+
+// ------------------------------------------------------------------ handle
+
+struct vspmm_matrix_s {
+    int layout;  // vspmm_layout
+    int64_t n_rows, n_cols, n_groups, nnz;
+    const int32_t *sptr;   // CSR row_ptr or VCS major_ptr
+    const void *vals;      // CSR val or VCS values
+    const int32_t *vptr;   // VCS value_ptr
+    const int32_t *idx;    // minor indices
+    int dtype;             // vspmm_dtype
+    uint32_t flags;
+    int force_group;
+    int device;
+    uint64_t id;
+    int64_t n_major() const { return layout == VSPMM_VCSC ? n_cols : n_rows; }
+    int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
+    size_t elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
+};
+
+namespace {
+
+std::atomic<uint64_t> g_next_id{1};
+
+// Workspaces holding a built opposite layout: ws address -> (handle id, dir).
+std::mutex g_ws_mutex;
+std::unordered_map<const void *, std::pair<uint64_t, int>> g_ws_cache;
+
+struct DeviceInfo {
+    int n_cu = 0;
+    bool ok = false;
+};
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[64];
+
+DeviceInfo device_info(int dev) {
+    std::lock_guard<std::mutex> lk(g_dev_mutex);
+    if (dev < 0 || dev >= 64) return DeviceInfo{};
+    if (!g_dev[dev].ok) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+            g_dev[dev].n_cu = prop.multiProcessorCount;
+            g_dev[dev].ok = true;
+        }
+    }
+    return g_dev[dev];
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool fits_i32(int64_t x) { return x >= 0 && x <= kI32Max; }
+
+int ilog2_floor(int64_t x) {
+    int l = 0;
+    while ((int64_t(1) << (l + 1)) <= x) ++l;
+    return l;
+}
+
+int ilog2_ceil(int64_t x) {
+    int l = 0;
+    while ((int64_t(1) << l) < x) ++l;
+    return l;
+}
+
+int key_bits(int64_t n_keys) {  // bits holding every key in [0, n_keys)
+    return n_keys <= 1 ? 0 : ilog2_ceil(n_keys);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Direction geometry: aligned when the output's rows are the major slices.
+bool is_aligned(const vspmm_matrix_s &h, int dir) {
+    return (h.layout != VSPMM_VCSC) == (dir == VSPMM_AB);
+}
+
+int64_t n_in(const vspmm_matrix_s &h, int dir) { return dir == VSPMM_AB ? h.n_cols : h.n_rows; }
+int64_t n_out(const vspmm_matrix_s &h, int dir) { return dir == VSPMM_AB ? h.n_rows : h.n_cols; }
+
+// ------------------------------------------------------------------- plan
+
+struct Plan {
+    Split sp{0, 0};
+    int vec = 1;
+    int R = 1;
+    bool lds = false;
+    int grid = 0;
+    int block = 256;
+};
+
+// The lane split of one walk over a matrix with n_slices slices and nnz
+// entries, at width w. Entry lanes G and width lanes WW are powers of two with
+// G * WW <= 64; R = 64 / (G * WW) slices share a wave.
+Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_matrix,
+               int force_group, bool scatter, const void *B, const void *out, int n_cu) {
+    Plan pl;
+    int vec = 1;
+    if (!scatter) {
+        const int max_vec = int(16 / elt);
+        for (int v = max_vec; v > 1; v >>= 1) {
+            if (w % v == 0 && aligned(B, v * elt) && aligned(out, v * elt)) {
+                vec = v;
+                break;
+            }
+        }
+    }
+    pl.vec = vec;
+    const int64_t units = (w + vec - 1) / vec;
+    const int log_need = std::min(6, ilog2_ceil(std::max<int64_t>(units, 1)));
+    int log_g, log_ww;
+    if (force_group > 0) {
+        log_g = ilog2_floor(force_group);
+        log_ww = std::min(log_need, 6 - log_g);
+    } else if (split_matrix) {
+        const int64_t mean = n_slices > 0 ? nnz / n_slices : 0;
+        log_g = std::min(6, ilog2_floor(std::max<int64_t>(mean, 1)));
+        log_ww = std::min(log_need, 6 - log_g);
+    } else {
+        log_ww = log_need;
+        log_g = 6 - log_ww;
+    }
+    pl.sp.log_g = log_g;
+    pl.sp.log_ww = log_ww;
+    pl.R = 64 >> (log_g + log_ww);
+    const int64_t per_block = int64_t(pl.block / 64) * pl.R;
+    const int64_t want = (n_slices + per_block - 1) / per_block;
+    const int64_t cap = int64_t(std::max(n_cu, 1)) * 8;
+    pl.grid = int(std::max<int64_t>(1, std::min(want, cap)));
+    return pl;
+}
+
+// --------------------------------------------------------------- launches
+
+vspmm_status hip_status() {
+    return hipGetLastError() == hipSuccess ? VSPMM_OK : VSPMM_ERR_HIP;
+}
+
+void launch_zero(void *p, size_t bytes, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (!words) return;
+    const size_t blocks = std::min<size_t>((words / 4 + 255) / 256 + 1, 4096);
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, words);
+}
+
+template <typename T>
+void launch_aligned(bool vcs, const Plan &pl, int n_slices, const int *sptr, const int *vptr,
+                    const T *vals, const int *idx, const T *B, T *out, int w, hipStream_t s) {
+    const dim3 g(pl.grid), b(pl.block);
+    const bool uni = pl.R == 1;
+#define VSPMM_ALIGNED(VCS, VEC, UNI)                                                         \
+    hipLaunchKernelGGL((k_aligned<VCS, T, VEC, UNI>), g, b, 0, s, n_slices, sptr, vptr, vals, \
+                       idx, B, out, w, pl.sp)
+    if (vcs) {
+        if constexpr (sizeof(T) == 4) {
+            if (uni) {
+                if (pl.vec == 4) VSPMM_ALIGNED(true, 4, true);
+                else if (pl.vec == 2) VSPMM_ALIGNED(true, 2, true);
+                else VSPMM_ALIGNED(true, 1, true);
+            } else {
+                if (pl.vec == 4) VSPMM_ALIGNED(true, 4, false);
+                else if (pl.vec == 2) VSPMM_ALIGNED(true, 2, false);
+                else VSPMM_ALIGNED(true, 1, false);
+            }
+        }
+    } else {
+        if constexpr (sizeof(T) == 4) {
+            if (pl.vec == 4) VSPMM_ALIGNED(false, 4, false);
+            else if (pl.vec == 2) VSPMM_ALIGNED(false, 2, false);
+            else VSPMM_ALIGNED(false, 1, false);
+        } else {
+            if (pl.vec == 2) VSPMM_ALIGNED(false, 2, false);
+            else VSPMM_ALIGNED(false, 1, false);
+        }
+    }
+#undef VSPMM_ALIGNED
+}
+
+template <typename T>
+void launch_scatter(bool vcs, const Plan &pl, int n_slices, const int *sptr, const int *vptr,
+                    const T *vals, const int *idx, const T *B, T *out, int w, hipStream_t s) {
+    const dim3 g(pl.grid), b(pl.block);
+    if (vcs) {
+        if constexpr (sizeof(T) == 4) {
+            if (pl.R == 1)
+                hipLaunchKernelGGL((k_scatter<true, T, true>), g, b, 0, s, n_slices, sptr, vptr,
+                                   vals, idx, B, out, w, pl.sp);
+            else
+                hipLaunchKernelGGL((k_scatter<true, T, false>), g, b, 0, s, n_slices, sptr, vptr,
+                                   vals, idx, B, out, w, pl.sp);
+        }
+    } else {
+        hipLaunchKernelGGL((k_scatter<false, T, false>), g, b, 0, s, n_slices, sptr, vptr, vals,
+                           idx, B, out, w, pl.sp);
+    }
+}
+
+// ------------------------------------------------------------- workspace
+
+// Carves 256-byte aligned arrays out of a workspace (or only counts bytes
+// when base is null).
+struct Bump {
+    char *base;
+    size_t off = 0;
+    template <typename T>
+    T *take(size_t n) {
+        off = align256(off);
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off += std::max<size_t>(n, 1) * sizeof(T);
+        return p;
+    }
+};
+
+// The opposite layout (result, kept across calls) plus the sort's scratch.
+struct OppositeWs {
+    // result
+    int32_t *t_ptr = nullptr;      // n_minor + 1 (CSR row pointers / VCS major_ptr)
+    void *t_vals = nullptr;        // CSR: nnz values; VCS: nnz group values (worst case)
+    int32_t *t_vptr = nullptr;     // VCS: nnz + 1
+    int32_t *t_idx = nullptr;      // nnz
+    int32_t *t_ngroups = nullptr;  // VCS: 1
+    // scratch
+    int32_t *slice_of = nullptr, *group_of = nullptr;
+    uint32_t *keys_a = nullptr, *keys_b = nullptr;
+    int32_t *pay_a = nullptr, *pay_b = nullptr;
+    int32_t *flag = nullptr, *gid = nullptr, *cnt = nullptr;
+    int32_t *hist = nullptr, *bsums = nullptr, *scalars = nullptr;
+    size_t bytes = 0;
+};
+
+OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base) {
+    OppositeWs w;
+    Bump b{static_cast<char *>(base)};
+    const size_t nnz = size_t(h.nnz), nmin = size_t(h.n_minor());
+    const bool vcs = h.layout != VSPMM_CSR;
+    w.t_ptr = b.take<int32_t>(nmin + 1);
+    w.t_vals = b.take<char>(nnz * h.elt());
+    if (vcs) {
+        w.t_vptr = b.take<int32_t>(nnz + 1);
+        w.t_ngroups = b.take<int32_t>(1);
+    }
+    w.t_idx = b.take<int32_t>(nnz);
+    w.slice_of = b.take<int32_t>(nnz);
+    if (vcs) w.group_of = b.take<int32_t>(nnz);
+    w.keys_a = b.take<uint32_t>(nnz);
+    w.keys_b = b.take<uint32_t>(nnz);
+    w.pay_a = b.take<int32_t>(nnz);
+    w.pay_b = b.take<int32_t>(nnz);
+    if (vcs) {
+        w.flag = b.take<int32_t>(nnz);
+        w.gid = b.take<int32_t>(nnz);
+    }
+    w.cnt = b.take<int32_t>(nmin + 1);
+    const size_t nblocks = (nnz + kSortTile - 1) / kSortTile;
+    w.hist = b.take<int32_t>(256 * std::max<size_t>(nblocks, 1));
+    const size_t scan_len = std::max({nnz, nmin + 1, 256 * std::max<size_t>(nblocks, 1)});
+    w.bsums = b.take<int32_t>((scan_len + kScanTile - 1) / kScanTile + 1);
+    w.scalars = b.take<int32_t>(4);
+    w.bytes = align256(b.off);
+    return w;
+}
+
+// Exclusive scan of n ints (out may alias in); *total (device, optional) gets
+// the sum.
+void scan_excl(const int32_t *in, int32_t *out, int64_t n, int32_t *bsums, int32_t *total,
+               hipStream_t s) {
+    if (n <= 0) {
+        if (total) launch_zero(total, 4, s);
+        return;
+    }
+    const int nb = int((n + kScanTile - 1) / kScanTile);
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, s, in, int(n), bsums);
+    hipLaunchKernelGGL(k_scan_bsums, dim3(1), dim3(256), 0, s, bsums, nb, total);
+    hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, s, in, int(n), bsums, out);
+}
+
+// Stable LSD radix sort of (keys, pay) on the low `bits` bits; the result ends
+// in (*ka, *pa).
+void radix_sort(uint32_t **ka, int32_t **pa, uint32_t **kb, int32_t **pb, int64_t n, int bits,
+                int32_t *hist, int32_t *bsums, hipStream_t s) {
+    if (n <= 0) return;
+    const int nblocks = int((n + kSortTile - 1) / kSortTile);
+    for (int shift = 0; shift < bits; shift += 8) {
+        hipLaunchKernelGGL(k_radix_hist, dim3(nblocks), dim3(kSortThreads), 0, s, *ka, int(n),
+                           shift, nblocks, hist);
+        scan_excl(hist, hist, int64_t(256) * nblocks, bsums, nullptr, s);
+        hipLaunchKernelGGL(k_radix_scatter, dim3(nblocks), dim3(kSortThreads), 0, s, *ka, *pa,
+                           int(n), shift, nblocks, hist, *kb, *pb);
+        std::swap(*ka, *kb);
+        std::swap(*pa, *pb);
+    }
+}
+
+int grid_for(int64_t n, int n_cu) {
+    const int64_t want = (n + 255) / 256;
+    return int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(std::max(n_cu, 1)) * 16)));
+}
+
+// Entries per new slice and their exclusive scan (tptr, n_minor + 1 ints).
+void count_and_scan(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *tptr, int n_cu,
+                    hipStream_t s) {
+    const int64_t nmin = h.n_minor();
+    launch_zero(w.cnt, size_t(nmin) * 4, s);
+    if (h.nnz > 0)
+        hipLaunchKernelGGL(k_count, dim3(grid_for(h.nnz, n_cu)), dim3(256), 0, s, int(h.nnz),
+                           h.idx, w.cnt);
+    scan_excl(w.cnt, tptr, nmin, w.bsums, tptr + nmin, s);
+}
+
+void expand_slices(const vspmm_matrix_s &h, const OppositeWs &w, int n_cu, hipStream_t s) {
+    const int64_t nmaj = h.n_major();
+    if (nmaj <= 0 || h.nnz <= 0) return;
+    const int grid = int(std::max<int64_t>(1, std::min<int64_t>((nmaj + 3) / 4, n_cu * 16)));
+    if (h.layout == VSPMM_CSR)
+        hipLaunchKernelGGL(k_expand<false>, dim3(grid), dim3(256), 0, s, int(nmaj), h.sptr,
+                           h.vptr, w.slice_of, w.group_of);
+    else
+        hipLaunchKernelGGL(k_expand<true>, dim3(grid), dim3(256), 0, s, int(nmaj), h.sptr,
+                           h.vptr, w.slice_of, w.group_of);
+}
+
+// The exact CSR transpose into (t_ptr, t_idx, t_val).
+void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_ptr,
+                     int32_t *t_idx, void *t_val, int n_cu, hipStream_t s) {
+    count_and_scan(h, w, t_ptr, n_cu, s);
+    if (h.nnz <= 0) return;
+    expand_slices(h, w, n_cu, s);
+    const int grid = grid_for(h.nnz, n_cu);
+    uint32_t *ka = w.keys_a, *kb = w.keys_b;
+    int32_t *pa = w.pay_a, *pb = w.pay_b;
+    hipLaunchKernelGGL(k_index_keys, dim3(grid), dim3(256), 0, s, int(h.nnz), h.idx, ka, pa);
+    radix_sort(&ka, &pa, &kb, &pb, h.nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
+    if (h.dtype == VSPMM_F64)
+        hipLaunchKernelGGL(k_transpose_emit<double>, dim3(grid), dim3(256), 0, s, int(h.nnz), pa,
+                           w.slice_of, (const double *)h.vals, t_idx, (double *)t_val);
+    else
+        hipLaunchKernelGGL(k_transpose_emit<float>, dim3(grid), dim3(256), 0, s, int(h.nnz), pa,
+                           w.slice_of, (const float *)h.vals, t_idx, (float *)t_val);
+}
+
+// The VCS regrouped by the other axis into (t_major_ptr, t_values,
+// t_value_ptr, t_indices, t_n_groups).
+void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_major_ptr,
+                   float *t_values, int32_t *t_value_ptr, int32_t *t_indices,
+                   int32_t *t_n_groups, int n_cu, hipStream_t s) {
+    int32_t *tptr = w.cnt;  // entry offsets of the new slices (in place over the counts)
+    count_and_scan(h, w, tptr, n_cu, s);
+    const int64_t nnz = h.nnz;
+    const int grid = grid_for(std::max<int64_t>(nnz, 1), n_cu);
+    int32_t *n_groups = w.scalars;
+    if (nnz > 0) {
+        expand_slices(h, w, n_cu, s);
+        uint32_t *ka = w.keys_a, *kb = w.keys_b;
+        int32_t *pa = w.pay_a, *pb = w.pay_b;
+        hipLaunchKernelGGL(k_value_keys, dim3(grid), dim3(256), 0, s, int(nnz), w.group_of,
+                           (const float *)h.vals, ka, pa);
+        radix_sort(&ka, &pa, &kb, &pb, nnz, 32, w.hist, w.bsums, s);
+        hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, h.idx, ka);
+        radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
+        hipLaunchKernelGGL(k_group_flags, dim3(grid), dim3(256), 0, s, int(nnz), pa, ka,
+                           w.group_of, (const float *)h.vals, w.flag);
+        scan_excl(w.flag, w.gid, nnz, w.bsums, n_groups, s);
+        hipLaunchKernelGGL(k_group_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
+                           w.group_of, (const float *)h.vals, w.flag, w.gid, t_values,
+                           t_value_ptr, t_indices);
+    } else {
+        launch_zero(n_groups, 4, s);
+    }
+    const int g2 = grid_for(h.n_minor() + 1, n_cu);
+    hipLaunchKernelGGL(k_group_major_ptr, dim3(g2), dim3(256), 0, s, int(h.n_minor()), int(nnz),
+                       tptr, w.gid, n_groups, t_major_ptr, t_value_ptr, t_n_groups);
+}
+
+// ---------------------------------------------------------------- checks
+
+vspmm_status check_handle(const vspmm_matrix_s *h) { return h ? VSPMM_OK : VSPMM_ERR_NULL; }
+
+vspmm_status check_product(const vspmm_matrix_s &h, const void *B, void *out, int64_t width,
+                           int dir) {
+    if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
+    if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
+    const int64_t ni = n_in(h, dir), no = n_out(h, dir);
+    (void)ni;
+    (void)no;
+    if (width > 0 && ni > 0 && !B) return VSPMM_ERR_NULL;
+    if (width > 0 && no > 0 && !out) return VSPMM_ERR_NULL;
+    if (width > 0 && (!aligned(B, h.elt()) || !aligned(out, h.elt()))) return VSPMM_ERR_DIM;
+    return VSPMM_OK;
+}
+
+vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int64_t width,
+                         int dir, int mode, void *ws, size_t ws_bytes, hipStream_t s) {
+    vspmm_status st = check_product(h, B, out, width, dir);
+    if (st) return st;
+    if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
+    const int64_t no = n_out(h, dir);
+    if (width == 0 || no == 0) return VSPMM_OK;
+    const DeviceInfo di = device_info(h.device);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    const bool vcs = h.layout != VSPMM_CSR;
+    const bool split_matrix = (h.flags & VSPMM_SPLIT_MATRIX) ||
+                              (!vcs && !(h.flags & VSPMM_SPLIT_WIDTH));
+    const int w = int(width);
+    if (h.nnz == 0) {
+        launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
+        return hip_status();
+    }
+    if (is_aligned(h, dir)) {
+        const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
+                                  false, B, out, n_cu);
+        if (h.dtype == VSPMM_F64)
+            launch_aligned<double>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
+                                   (const double *)h.vals, h.idx, (const double *)B,
+                                   (double *)out, w, s);
+        else
+            launch_aligned<float>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
+                                  (const float *)h.vals, h.idx, (const float *)B, (float *)out,
+                                  w, s);
+        return hip_status();
+    }
+    if (mode == VSPMM_ATOMIC) {
+        const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
+                                  true, B, out, n_cu);
+        launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
+        if (h.dtype == VSPMM_F64)
+            launch_scatter<double>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
+                                   (const double *)h.vals, h.idx, (const double *)B,
+                                   (double *)out, w, s);
+        else
+            launch_scatter<float>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
+                                  (const float *)h.vals, h.idx, (const float *)B, (float *)out,
+                                  w, s);
+        return hip_status();
+    }
+    // deterministic: build (or reuse) the opposite layout, then walk it aligned
+    const OppositeWs need = carve_opposite(h, nullptr);
+    if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+    const OppositeWs wl = carve_opposite(h, ws);
+    bool built;
+    {
+        std::lock_guard<std::mutex> lk(g_ws_mutex);
+        auto it = g_ws_cache.find(ws);
+        built = it != g_ws_cache.end() && it->second.first == h.id && it->second.second == dir;
+        if (!built) g_ws_cache[ws] = {h.id, dir};
+    }
+    if (!built) {
+        if (vcs)
+            build_regroup(h, wl, wl.t_ptr, (float *)wl.t_vals, wl.t_vptr, wl.t_idx, wl.t_ngroups,
+                          n_cu, s);
+        else
+            build_transpose(h, wl, wl.t_ptr, wl.t_idx, wl.t_vals, n_cu, s);
+        st = hip_status();
+        if (st) {
+            std::lock_guard<std::mutex> lk(g_ws_mutex);
+            g_ws_cache.erase(ws);
+            return st;
+        }
+    }
+    const int64_t nmin = h.n_minor();
+    const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, false, B, out,
+                              n_cu);
+    if (h.dtype == VSPMM_F64)
+        launch_aligned<double>(false, pl, int(nmin), wl.t_ptr, nullptr,
+                               (const double *)wl.t_vals, wl.t_idx, (const double *)B,
+                               (double *)out, w, s);
+    else
+        launch_aligned<float>(vcs, pl, int(nmin), wl.t_ptr, wl.t_vptr, (const float *)wl.t_vals,
+                              wl.t_idx, (const float *)B, (float *)out, w, s);
+    return hip_status();
+}
+
+vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
+    if (hipGetDevice(&m->device) != hipSuccess) {
+        delete m;
+        return VSPMM_ERR_HIP;
+    }
+    m->id = g_next_id.fetch_add(1);
+    if (m->flags & VSPMM_VALIDATE) {
+        const vspmm_status st = vspmm_validate(m, s);
+        if (st) {
+            delete m;
+            return st;
+        }
+    }
+    *h = m;
+    return VSPMM_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+const char *vspmm_status_string(vspmm_status st) {
+    switch (st) {
+        case VSPMM_OK: return "ok";
+        case VSPMM_ERR_NULL: return "a required pointer is null";
+        case VSPMM_ERR_DIM: return "invalid or inconsistent extent";
+        case VSPMM_ERR_ENUM: return "unknown layout, direction, dtype, mode or flag";
+        case VSPMM_ERR_STRUCTURE: return "malformed sparse structure";
+        case VSPMM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case VSPMM_ERR_UNSUPPORTED: return "unsupported request";
+        case VSPMM_ERR_HIP: return "HIP call or kernel launch failed";
+        case VSPMM_ERR_ALLOC: return "host allocation failed";
+    }
+    return "unknown status";
+}
+
+vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_rows,
+                              int64_t n_cols, int64_t n_groups, int64_t nnz,
+                              const int32_t *major_ptr, const float *values,
+                              const int32_t *value_ptr, const int32_t *indices, uint32_t flags,
+                              int32_t force_group, hipStream_t stream) {
+    if (!h) return VSPMM_ERR_NULL;
+    if (layout != VSPMM_VCSR && layout != VSPMM_VCSC) return VSPMM_ERR_ENUM;
+    if (flags & ~uint32_t(VSPMM_SPLIT_WIDTH | VSPMM_SPLIT_MATRIX | VSPMM_VALIDATE))
+        return VSPMM_ERR_ENUM;
+    if ((flags & VSPMM_SPLIT_WIDTH) && (flags & VSPMM_SPLIT_MATRIX)) return VSPMM_ERR_ENUM;
+    if (!fits_i32(n_rows) || !fits_i32(n_cols) || !fits_i32(n_groups) || !fits_i32(nnz) ||
+        n_rows + 1 > kI32Max || n_cols + 1 > kI32Max || n_groups + 1 > kI32Max)
+        return VSPMM_ERR_DIM;
+    if (force_group < 0 || force_group > 64 || (force_group & (force_group - 1)))
+        return VSPMM_ERR_DIM;
+    if (!major_ptr || !value_ptr) return VSPMM_ERR_NULL;
+    if ((n_groups > 0 && !values) || (nnz > 0 && !indices)) return VSPMM_ERR_NULL;
+    auto *m = new (std::nothrow) vspmm_matrix_s{};
+    if (!m) return VSPMM_ERR_ALLOC;
+    m->layout = layout;
+    m->n_rows = n_rows;
+    m->n_cols = n_cols;
+    m->n_groups = n_groups;
+    m->nnz = nnz;
+    m->sptr = major_ptr;
+    m->vals = values;
+    m->vptr = value_ptr;
+    m->idx = indices;
+    m->dtype = VSPMM_F32;
+    m->flags = flags;
+    m->force_group = force_group;
+    return finish_create(m, h, stream);
+}
+
+vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                              const int32_t *row_ptr, const int32_t *col, const void *val,
+                              vspmm_dtype dtype, uint32_t flags, int32_t force_group,
+                              hipStream_t stream) {
+    if (!h) return VSPMM_ERR_NULL;
+    if (dtype != VSPMM_F32 && dtype != VSPMM_F64) return VSPMM_ERR_ENUM;
+    if (flags & ~uint32_t(VSPMM_SPLIT_WIDTH | VSPMM_SPLIT_MATRIX | VSPMM_VALIDATE))
+        return VSPMM_ERR_ENUM;
+    if ((flags & VSPMM_SPLIT_WIDTH) && (flags & VSPMM_SPLIT_MATRIX)) return VSPMM_ERR_ENUM;
+    if (!fits_i32(n_rows) || !fits_i32(n_cols) || !fits_i32(nnz) || n_rows + 1 > kI32Max ||
+        n_cols + 1 > kI32Max)
+        return VSPMM_ERR_DIM;
+    if (force_group < 0 || force_group > 64 || (force_group & (force_group - 1)))
+        return VSPMM_ERR_DIM;
+    if (!row_ptr) return VSPMM_ERR_NULL;
+    if (nnz > 0 && (!col || !val)) return VSPMM_ERR_NULL;
+    auto *m = new (std::nothrow) vspmm_matrix_s{};
+    if (!m) return VSPMM_ERR_ALLOC;
+    m->layout = VSPMM_CSR;
+    m->n_rows = n_rows;
+    m->n_cols = n_cols;
+    m->n_groups = 0;
+    m->nnz = nnz;
+    m->sptr = row_ptr;
+    m->vals = val;
+    m->vptr = nullptr;
+    m->idx = col;
+    m->dtype = dtype;
+    m->flags = flags;
+    m->force_group = force_group;
+    return finish_create(m, h, stream);
+}
+
+vspmm_status vspmm_destroy(vspmm_matrix h) {
+    if (!h) return VSPMM_ERR_NULL;
+    {
+        std::lock_guard<std::mutex> lk(g_ws_mutex);
+        for (auto it = g_ws_cache.begin(); it != g_ws_cache.end();) {
+            if (it->second.first == h->id) it = g_ws_cache.erase(it);
+            else ++it;
+        }
+    }
+    delete h;
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_spmm(vspmm_matrix h, const void *B, void *out, int64_t width,
+                        vspmm_direction dir, hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    return run_product(*h, B, out, width, dir, VSPMM_ATOMIC, nullptr, 0, stream);
+}
+
+vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
+                                  size_t *bytes) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (!bytes) return VSPMM_ERR_NULL;
+    if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
+    if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
+    *bytes = (mode == VSPMM_DETERMINISTIC && !is_aligned(*h, dir))
+                 ? carve_opposite(*h, nullptr).bytes
+                 : 0;
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t width,
+                           vspmm_direction dir, vspmm_mode mode, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    return run_product(*h, B, out, width, dir, mode, ws, ws_bytes, stream);
+}
+
+vspmm_status vspmm_workspace_invalidate(void *ws) {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    g_ws_cache.erase(ws);
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_validate(vspmm_matrix h, hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    const DeviceInfo di = device_info(h->device);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    int *flag = nullptr;
+    if (hipMalloc(&flag, sizeof(int)) != hipSuccess) return VSPMM_ERR_HIP;
+    launch_zero(flag, 4, stream);
+    const int64_t nmaj = h->n_major();
+    hipLaunchKernelGGL(k_validate_ptr, dim3(grid_for(nmaj + 1, n_cu)), dim3(256), 0, stream,
+                       h->sptr, int(nmaj), int(h->layout == VSPMM_CSR ? h->nnz : h->n_groups),
+                       flag);
+    if (h->layout != VSPMM_CSR)
+        hipLaunchKernelGGL(k_validate_ptr, dim3(grid_for(h->n_groups + 1, n_cu)), dim3(256), 0,
+                           stream, h->vptr, int(h->n_groups), int(h->nnz), flag);
+    if (h->nnz > 0)
+        hipLaunchKernelGGL(k_validate_idx, dim3(grid_for(h->nnz, n_cu)), dim3(256), 0, stream,
+                           h->idx, int(h->nnz), int(h->n_minor()), flag);
+    int host_flag = -1;
+    vspmm_status st = hip_status();
+    if (!st && hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream) !=
+                   hipSuccess)
+        st = VSPMM_ERR_HIP;
+    if (!st && hipStreamSynchronize(stream) != hipSuccess) st = VSPMM_ERR_HIP;
+    (void)hipFree(flag);
+    if (st) return st;
+    return host_flag == 0 ? VSPMM_OK : VSPMM_ERR_STRUCTURE;
+}
+
+vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_col,
+                                 void *t_val, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (h->layout != VSPMM_CSR) return VSPMM_ERR_ENUM;
+    if (!t_row_ptr || (h->nnz > 0 && (!t_col || !t_val))) return VSPMM_ERR_NULL;
+    const OppositeWs need = carve_opposite(*h, nullptr);
+    if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+    {
+        std::lock_guard<std::mutex> lk(g_ws_mutex);
+        g_ws_cache.erase(ws);
+    }
+    const DeviceInfo di = device_info(h->device);
+    build_transpose(*h, carve_opposite(*h, ws), t_row_ptr, t_col, t_val, di.ok ? di.n_cu : 256,
+                    stream);
+    return hip_status();
+}
+
+vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_values,
+                               int32_t *t_value_ptr, int32_t *t_indices, int32_t *t_n_groups,
+                               void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (h->layout == VSPMM_CSR) return VSPMM_ERR_ENUM;
+    if (!t_major_ptr || !t_value_ptr || !t_n_groups) return VSPMM_ERR_NULL;
+    if (h->nnz > 0 && (!t_values || !t_indices)) return VSPMM_ERR_NULL;
+    const OppositeWs need = carve_opposite(*h, nullptr);
+    if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+    {
+        std::lock_guard<std::mutex> lk(g_ws_mutex);
+        g_ws_cache.erase(ws);
+    }
+    const DeviceInfo di = device_info(h->device);
+    build_regroup(*h, carve_opposite(*h, ws), t_major_ptr, t_values, t_value_ptr, t_indices,
+                  t_n_groups, di.ok ? di.n_cu : 256, stream);
+    return hip_status();
+}
+
+vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_bytes) {
+    if (vspmm_status st = check_handle(h)) return st;
+    const size_t nmaj = size_t(h->n_major()), nnz = size_t(h->nnz), e = h->elt();
+    size_t own;
+    if (h->layout == VSPMM_CSR)
+        own = 4 * (nmaj + 1) + (4 + e) * nnz;
+    else
+        own = 4 * (nmaj + 1) + 4 * size_t(h->n_groups) + 4 * (size_t(h->n_groups) + 1) + 4 * nnz;
+    if (bytes) *bytes = own;
+    if (expanded_bytes) *expanded_bytes = 4 * (nmaj + 1) + (4 + e) * nnz;
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
+                             vspmm_mode mode, int32_t *entry_lanes, int32_t *width_lanes,
+                             int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
+    if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
+    if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
+    const bool vcs = h->layout != VSPMM_CSR;
+    const bool split_matrix = (h->flags & VSPMM_SPLIT_MATRIX) ||
+                              (!vcs && !(h->flags & VSPMM_SPLIT_WIDTH));
+    const bool al = is_aligned(*h, dir);
+    const bool scatter = !al && mode == VSPMM_ATOMIC;
+    const int64_t ns = al || scatter ? h->n_major() : h->n_minor();
+    // alignment of the caller's buffers is unknown here: assume 16-byte aligned
+    alignas(16) static const float probe[4] = {0, 0, 0, 0};
+    const Plan pl = make_plan(ns, h->nnz, width, h->elt(), split_matrix, h->force_group, scatter,
+                              probe, probe, 256);
+    if (entry_lanes) *entry_lanes = 1 << pl.sp.log_g;
+    if (width_lanes) *width_lanes = 1 << pl.sp.log_ww;
+    if (vec) *vec = pl.vec;
+    if (slices_per_wave) *slices_per_wave = pl.R;
+    if (lds_staged) *lds_staged = pl.lds ? 1 : 0;
+    return VSPMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+"""CSR products on the GPU against the float64 oracle: the 2,000 x 500
+workload, the regridding-shaped operator in float32 and float64, its exact
+transpose (bit for bit), batch-vs-solo bit identity for every entry split, and
+the deterministic misaligned direction."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import check_close, csr_handle, dims, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cfg1():
+    return W.config1()[1]
+
+
+@pytest.fixture(scope="module")
+def regrid32():
+    return W.config4(np.float32)[1]
+
+
+@pytest.fixture(scope="module")
+def regrid64():
+    return W.config4(np.float64)[1]
+
+
+@pytest.mark.parametrize("width", [1, 2, 3, 8, 16, 33])
+@pytest.mark.parametrize("direction", ["AB", "BA"])
+def test_config1(orc, cfg1, direction, width):
+    dev = need_gpu()
+    A = csr_handle(cfg1, dev)
+    rows, _ = dims(cfg1, direction)
+    B = W.dense_normal(np.random.default_rng(width), rows, width)
+    check_close(orc, cfg1, direction, B, A.spmm(to_dev(B, dev), direction),
+                where=f"csr {direction} w={width}")
+
+
+def test_config1_operators(orc, cfg1):
+    """A @ B with B 500 x 8 and B @ A with B 8 x 2,000, plus SpMV both ways."""
+    dev = need_gpu()
+    A = csr_handle(cfg1, dev)
+    rng = np.random.default_rng(1)
+    B = W.dense_normal(rng, 500, 8)
+    check_close(orc, cfg1, "AB", B, A @ to_dev(B, dev), where="A@B")
+    Bl = W.dense_normal(rng, 8, 2000)  # the 8 x 2,000 left operand
+    got = (to_dev(Bl, dev) @ A).t()
+    check_close(orc, cfg1, "BA", np.ascontiguousarray(Bl.T), got, where="B@A")
+    x = W.dense_normal(rng, 500, 1)[:, 0]
+    check_close(orc, cfg1, "AB", x[:, None], (A @ to_dev(x, dev))[:, None], where="A@x")
+    y = W.dense_normal(rng, 2000, 1)[:, 0]
+    check_close(orc, cfg1, "BA", y[:, None], (to_dev(y, dev) @ A)[:, None], where="y@A")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("direction", ["AB", "BA"])
+def test_regridding_operator(orc, regrid32, regrid64, dtype, direction):
+    dev = need_gpu()
+    C = regrid32 if dtype == "f32" else regrid64
+    A = csr_handle(C, dev)
+    rows, _ = dims(C, direction)
+    np_t = np.float32 if dtype == "f32" else np.float64
+    for width in (1, 32):
+        B = W.dense_normal(np.random.default_rng(width), rows, width, dtype=np_t)
+        out = A.spmm(to_dev(B, dev), direction)
+        tol = 1e-5 if dtype == "f32" else 1e-13
+        check_close(orc, C, direction, B, out, tol=tol, where=f"{dtype} {direction} w={width}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_transpose_equals_oracle_bitwise(orc, regrid32, regrid64, dtype):
+    dev = need_gpu()
+    C = regrid32 if dtype == "f32" else regrid64
+    T = csr_handle(C, dev).transpose()
+    tp, ti, tv = orc.transpose_csr(C.shape[1], C.row_ptr, C.col, C.val)
+    assert np.array_equal(T.row_ptr.cpu().numpy(), tp)
+    assert np.array_equal(T.col.cpu().numpy(), ti)
+    assert np.array_equal(T.val.cpu().numpy().view(np.uint8), tv.view(np.uint8))
+    # and back again
+    TT = T.transpose()
+    assert np.array_equal(TT.row_ptr.cpu().numpy(), C.row_ptr)
+    assert np.array_equal(TT.col.cpu().numpy(), C.col)
+    assert np.array_equal(TT.val.cpu().numpy().view(np.uint8), C.val.view(np.uint8))
+
+
+@pytest.mark.parametrize("group", [0, 1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("which", ["forward", "transpose"])
+def test_batch_equals_solo_bitwise(orc, regrid32, regrid64, which, dtype, group):
+    """With the entry split taken from the matrix, each column of a batch of
+    32 gets exactly the bits it gets alone (regridding page, section "How it is
+    built"), for the forward operator and its exact transpose."""
+    dev = need_gpu()
+    C = regrid32 if dtype == "f32" else regrid64
+    A = csr_handle(C, dev, force_group=group)
+    if which == "transpose":
+        A = A.transpose()
+    np_t = np.float32 if dtype == "f32" else np.float64
+    rows = A.shape[1]
+    Bb = to_dev(W.dense_normal(np.random.default_rng(5), rows, 32, dtype=np_t), dev)
+    batch = A.spmm(Bb, "AB")
+    for c in (0, 1, 7, 16, 31):
+        solo = A.spmm(Bb[:, c:c + 1].contiguous(), "AB")
+        assert torch.equal(batch[:, c], solo[:, 0]), (which, dtype, group, c)
+    if group == 0:
+        info1, info32 = A.plan_info(1), A.plan_info(32)
+        assert info1["entry_lanes"] == info32["entry_lanes"]
+
+
+def test_group_size_follows_matrix(regrid32):
+    """The entry split is the power of two at or below the mean entries per
+    row, at most 64: ~55 -> 32 for the forward operator, ~3 -> 2 for its
+    transpose (regridding page, section "How it is built")."""
+    dev = need_gpu()
+    A = csr_handle(regrid32, dev)
+    assert A.plan_info(1)["entry_lanes"] == 32
+    assert A.transpose().plan_info(1)["entry_lanes"] == 2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_deterministic_misaligned(orc, regrid32, regrid64, dtype):
+    dev = need_gpu()
+    C = regrid32 if dtype == "f32" else regrid64
+    A = csr_handle(C, dev)
+    np_t = np.float32 if dtype == "f32" else np.float64
+    B = W.dense_normal(np.random.default_rng(9), C.shape[0], 32, dtype=np_t)
+    ws = A.workspace("BA")
+    first = A.spmm(to_dev(B, dev), "BA", mode="deterministic", workspace=ws)
+    tol = 1e-5 if dtype == "f32" else 1e-13
+    check_close(orc, C, "BA", B, first, tol=tol, where=f"det BA {dtype}")
+    first = first.clone()
+    for _ in range(5):
+        again = A.spmm(to_dev(B, dev), "BA", mode="deterministic", workspace=ws)
+        assert torch.equal(again, first)
+
+
+def test_integer_exact_atomics(orc, cfg1):
+    dev = need_gpu()
+    C = W.Csr(cfg1.shape, cfg1.row_ptr, cfg1.col, np.rint(cfg1.val * 8).astype(np.float32))
+    A = csr_handle(C, dev)
+    B = W.dense_int(np.random.default_rng(2), 2000, 9)
+    out = A.spmm(to_dev(B, dev), "BA")
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), orc.spmm(C, "BA", B))
+
+
+def test_csr_edge_cases():
+    dev = need_gpu()
+    C = W.Csr((3, 4), np.array([0, 0, 0, 0], np.int32), np.zeros(0, np.int32),
+              np.zeros(0, np.float64))
+    A = csr_handle(C, dev)
+    out = torch.full((3, 2), 5.0, dtype=torch.float64, device=dev)
+    A.spmm(torch.ones((4, 2), dtype=torch.float64, device=dev), out=out)
+    assert not out.any()
+    T = A.transpose()
+    assert T.row_ptr.cpu().tolist() == [0, 0, 0, 0, 0]
