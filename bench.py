@@ -1,16 +1,25 @@
 """Benchmark: VCS SpMM on the 60,000 x 2,000 count matrix (~6M nonzeros) at
 width 16, all four directions, on one MI355X.
 
-A step is one pass of the whole product path over that matrix: VCSR @ B
-(aligned), B @ VCSR (atomic scatter), VCSC @ B (atomic scatter) and B @ VCSC
-(aligned). Inputs are resident in HBM before timing starts. Each product in a
-step reads its own copy of the matrix and dense operands, and the copies rotate
-through more than 1 GB, so no product finds its data in the 256 MB Infinity
-Cache left there by the product before it (cold-HBM numbers).
+A step is one pass of the product path over that matrix in all four
+directions: VCSR @ B and B @ VCSC (aligned walks), B @ VCSR and VCSC @ B
+(misaligned). The headline runs the misaligned directions in the
+deterministic two-pass mode with the opposite layout already built in each
+handle's workspace (pass 2 only; the one-time build is timed and reported
+separately), since hardware float atomics cap the atomic mode at about one
+atomic lane per L2 channel per clock; the atomic-mode times are reported in
+the same line.
 
-value = the four products' minimum algorithmic bytes / the step's GPU time.
-Minimum bytes of one product = the whole compressed structure
-(4(n_major+1) + 4 G + 4(G+1) + 4 nnz) + 4 w (n_in + n_out).
+Inputs are resident in HBM before timing starts. Every product reads its own
+copy of the matrix and dense operands, and the copies rotate through more than
+1 GB, so no product finds its data in the 256 MB Infinity Cache (cold-HBM
+numbers). Each direction's launches run back to back between two HIP events
+on the stream the library launches on; its average launch duration is the
+elapsed time over the launch count.
+
+Minimum algorithmic bytes of one product = the compressed structure the
+product walks (4(n_major+1) + 4 G + 4(G+1) + 4 nnz) + 4 w (n_in + n_out).
+value = the four products' minimum bytes / the sum of their average times.
 
 Prints ONE JSON line. --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -31,20 +40,19 @@ sys.path.insert(0, ROOT)
 METRIC = "HBM GB/s (% of peak) for VCS SpMM 60k×2k, 6M nnz, width 16, 4 directions"
 PEAK_GBPS = 8000.0  # MI355X HBM3E
 
-DIRECTIONS = [  # (name, layout, direction)
-    ("VCSR@B", "vcsr", "AB"),
-    ("B@VCSR", "vcsr", "BA"),
-    ("VCSC@B", "vcsc", "AB"),
-    ("B@VCSC", "vcsc", "BA"),
+# name, layout of the handle, direction, walk used in atomic mode
+DIRECTIONS = [
+    ("VCSR@B", "vcsr", "AB", "aligned"),
+    ("B@VCSR", "vcsr", "BA", "scatter"),
+    ("VCSC@B", "vcsc", "AB", "scatter"),
+    ("B@VCSC", "vcsc", "BA", "aligned"),
 ]
-KERNEL_OF = {"VCSR@B": "k_aligned", "B@VCSR": "k_zero+k_scatter", "VCSC@B": "k_zero+k_scatter",
-             "B@VCSC": "k_aligned"}
 
 
-def min_bytes(L, direction, w):
-    m, n = L.shape
+def dense_bytes(shape, direction, w):
+    m, n = shape
     n_in, n_out = (n, m) if direction == "AB" else (m, n)
-    return L.nbytes() + 4 * w * (n_in + n_out)
+    return 4 * w * (n_in + n_out)
 
 
 def log(msg):
@@ -59,14 +67,14 @@ def cpu_baseline(layouts, width, budget_s):
     rng = np.random.default_rng(1)
     total_bytes, total_s, passes = 0, 0.0, 0
     while total_s < budget_s or passes == 0:
-        for name, layout, direction in DIRECTIONS:
+        for name, layout, direction, _ in DIRECTIONS:
             L = layouts[layout]
             m, n = L.shape
             B = rng.standard_normal((n if direction == "AB" else m, width)).astype(np.float32)
             t0 = time.perf_counter()
             oracle.spmm(L, direction, B)
             total_s += time.perf_counter() - t0
-            total_bytes += min_bytes(L, direction, width)
+            total_bytes += L.nbytes() + dense_bytes(L.shape, direction, width)
         passes += 1
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
@@ -83,10 +91,11 @@ def main():
     ap.add_argument("--copies", type=int, default=20, help="matrix copies rotated for cold HBM")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-mode timings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
-              "build (the product shards by major slices, see the design notes)", file=sys.stderr)
+              "build (the product shards by major slices; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -101,80 +110,109 @@ def main():
     layouts = {"vcsr": W.build_vcs(t, "vcsr"), "vcsc": W.build_vcs(t, "vcsc")}
     m, n = t.shape
     rng = np.random.default_rng(2)
-    B_ab = W.dense_normal(rng, n, w)  # n x w
-    B_ba = W.dense_normal(rng, m, w)  # m x w (B transposed)
+    dense = {"AB": W.dense_normal(rng, n, w), "BA": W.dense_normal(rng, m, w)}
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     base = {lay: [up(a) for a in (L.major_ptr, L.values, L.value_ptr, L.indices)]
             for lay, L in layouts.items()}
-    dense = {"AB": up(B_ab), "BA": up(B_ba)}
-    K = max(args.copies, 4)
+    dense_d = {d: up(x) for d, x in dense.items()}
+    K = max(args.copies, 2)
     log(f"placing {K} copies of each operand set on the device")
     copies = []
     for _ in range(K):
-        c = {}
+        c = {"A": {}, "ws": {}}
         for lay, L in layouts.items():
-            arrs = [a.clone() for a in base[lay]]
-            c[lay] = sdm.VcsMatrix.from_arrays(lay, L.shape, *arrs)
-        c["B"] = {d: x.clone() for d, x in dense.items()}
-        c["out"] = {("vcsr", "AB"): torch.empty((m, w), device=dev),
-                    ("vcsr", "BA"): torch.empty((n, w), device=dev),
-                    ("vcsc", "AB"): torch.empty((m, w), device=dev),
-                    ("vcsc", "BA"): torch.empty((n, w), device=dev)}
+            c["A"][lay] = sdm.VcsMatrix.from_arrays(lay, L.shape, *[a.clone() for a in base[lay]])
+        c["B"] = {d: x.clone() for d, x in dense_d.items()}
+        c["out"] = {(lay, d): torch.empty((m if d == "AB" else n, w), device=dev)
+                    for lay in layouts for d in ("AB", "BA")}
         copies.append(c)
     torch.cuda.synchronize()
 
-    def product(k, d):
-        name, lay, direction = DIRECTIONS[d]
-        c = copies[(4 * k + d) % K]
-        c[lay].spmm(c["B"][direction], direction, out=c["out"][(lay, direction)])
+    def run(k, d, mode):
+        name, lay, direction, _ = DIRECTIONS[d]
+        c = copies[k % K]
+        ws = c["ws"].get((lay, direction)) if mode == "deterministic" else None
+        c["A"][lay].spmm(c["B"][direction], direction, mode=mode, workspace=ws,
+                         out=c["out"][(lay, direction)])
 
-    log(f"warmup {args.warmup} steps")
-    for k in range(args.warmup):
-        for d in range(4):
-            product(k, d)
-    torch.cuda.synchronize()
-
+    # one-time build of the opposite layouts for the deterministic mode
+    build_ms = {}
     stream = torch.cuda.current_stream(dev)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(4)] for _ in range(args.steps)]
-    step0 = torch.cuda.Event(enable_timing=True)
-    step1 = torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    step0.record(stream)
-    for k in range(args.steps):
-        for d in range(4):
-            ev[k][d][0].record(stream)
-            product(args.warmup + k, d)
-            ev[k][d][1].record(stream)
-    step1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = step0.elapsed_time(step1)
-    ms_per_step = total_ms / args.steps
+    for d, (name, lay, direction, walk) in enumerate(DIRECTIONS):
+        if walk != "scatter":
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for k in range(K):
+            c = copies[k]
+            c["ws"][(lay, direction)] = c["A"][lay].workspace(direction, "deterministic")
+            e0.record(stream)
+            run(k, d, "deterministic")  # first call builds, then runs pass 2
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        build_ms[name] = round(float(np.median(times)), 3)
+    log(f"deterministic schedules built: {build_ms} ms (build + first product)")
 
+    def time_direction(d, mode):
+        for k in range(args.warmup):
+            run(k, d, mode)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k in range(args.steps):
+            run(args.warmup + k, d, mode)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / args.steps  # us per launch
+
+    wall0 = time.perf_counter()
     per_dir = {}
-    step_bytes = 0
-    for d, (name, lay, direction) in enumerate(DIRECTIONS):
-        us = 1e3 * float(np.mean([ev[k][d][0].elapsed_time(ev[k][d][1]) for k in range(args.steps)]))
-        b = min_bytes(layouts[lay], direction, w)
-        step_bytes += b
-        gbps = b / (us * 1e-6) / 1e9
-        per_dir[name] = {"us": round(us, 2), "min_bytes": b, "GBps": round(gbps, 1),
-                         "frac": round(gbps / PEAK_GBPS, 4), "kernels": KERNEL_OF[name]}
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    for d, (name, lay, direction, walk) in enumerate(DIRECTIONS):
+        L = layouts[lay]
+        entry = {"walk": walk}
+        if walk == "aligned":
+            us = time_direction(d, "atomic")
+            b = L.nbytes() + dense_bytes(L.shape, direction, w)
+            entry.update(us=round(us, 2), min_bytes=b, mode="aligned",
+                         kernel="k_short" if lay == "vcsr" else "k_long")
+        else:
+            us = time_direction(d, "deterministic")
+            other = layouts["vcsc" if lay == "vcsr" else "vcsr"]  # the regrouped layout walked
+            b = other.nbytes() + dense_bytes(L.shape, direction, w)
+            entry.update(us=round(us, 2), min_bytes=b, mode="deterministic (pass 2)",
+                         kernel="k_long" if lay == "vcsr" else "k_short")
+            if not args.no_atomic:
+                ua = time_direction(d, "atomic")
+                ba = L.nbytes() + dense_bytes(L.shape, direction, w)
+                entry["atomic"] = {"us": round(ua, 2), "min_bytes": ba,
+                                   "GBps": round(ba / (ua * 1e-6) / 1e9, 1),
+                                   "kernels": "k_zero + k_scatter"}
+        entry["GBps"] = round(entry["min_bytes"] / (entry["us"] * 1e-6) / 1e9, 1)
+        entry["frac"] = round(entry["GBps"] / PEAK_GBPS, 4)
+        per_dir[name] = entry
+    wall = time.perf_counter() - wall0
+
+    step_us = sum(e["us"] for e in per_dir.values())
+    step_bytes = sum(e["min_bytes"] for e in per_dir.values())
+    value = step_bytes / (step_us * 1e-6) / 1e9
     dom = max(per_dir, key=lambda k: per_dir[k]["us"])
 
-    # correctness guard on the timed configuration: aligned outputs repeat bit for bit
+    # guard: aligned and deterministic outputs repeat bit for bit
     c0 = copies[0]
-    r1 = c0["vcsr"].spmm(c0["B"]["AB"], "AB").clone()
-    r2 = c0["vcsr"].spmm(c0["B"]["AB"], "AB")
-    repeat_ok = bool(torch.equal(r1, r2))
+    r1 = c0["A"]["vcsr"].spmm(c0["B"]["AB"], "AB").clone()
+    r2 = c0["A"]["vcsr"].spmm(c0["B"]["AB"], "AB")
+    ws = c0["ws"][("vcsc", "AB")]
+    r3 = c0["A"]["vcsc"].spmm(c0["B"]["AB"], "AB", mode="deterministic", workspace=ws).clone()
+    r4 = c0["A"]["vcsc"].spmm(c0["B"]["AB"], "AB", mode="deterministic", workspace=ws)
+    repeat_ok = bool(torch.equal(r1, r2) and torch.equal(r3, r4))
 
+    atomic_us = sum(e["atomic"]["us"] if "atomic" in e else e["us"] for e in per_dir.values())
+    atomic_bytes = sum(e["atomic"]["min_bytes"] if "atomic" in e else e["min_bytes"]
+                       for e in per_dir.values())
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -182,23 +220,27 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(step_us / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"VCS count matrix {m} x {n}, {t.nnz} nnz, width {w}, "
-                               "4 directions (VCSR@B, B@VCSR, VCSC@B, B@VCSC), atomic mode, "
-                               "cold HBM",
-                   "global_batch": w, "seq_len": None, "parallelism": "none (1 GPU)"},
+        "config": {"workload": f"VCS count matrix {m} x {n}, {t.nnz} nnz, width {w}, 4 directions "
+                               "(VCSR@B, B@VCSR, VCSC@B, B@VCSC); misaligned directions in "
+                               "deterministic two-pass mode with the schedule built; cold HBM",
+                   "width": w, "parallelism": "none (1 GPU)"},
         "frac_of_peak": round(value / PEAK_GBPS, 4),
-        "gflops": round(4 * 2 * t.nnz * w / (ms_per_step * 1e-3) / 1e9, 1),
+        "gflops": round(4 * 2 * t.nnz * w / (step_us * 1e-6) / 1e9, 1),
         "directions": per_dir,
-        "roofline": {"bound": "hbm", "kernel": f"{per_dir[dom]['kernels']} ({dom})",
+        "atomic_mode": {"value": round(atomic_bytes / (atomic_us * 1e-6) / 1e9, 2) if not
+                        args.no_atomic else None, "unit": "GB/s",
+                        "ms_per_step": round(atomic_us / 1e3, 5) if not args.no_atomic else None},
+        "det_build_plus_first_product_ms": build_ms,
+        "roofline": {"bound": "hbm", "kernel": f"{per_dir[dom]['kernel']} ({dom})",
                      "achieved": per_dir[dom]["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": per_dir[dom]["frac"], "traffic": None},
-        "aligned_repeat_bitwise": repeat_ok,
+        "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

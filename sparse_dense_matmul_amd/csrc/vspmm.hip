@@ -15,6 +15,7 @@
 #include "../../include/vspmm.h"
 #include "schedule.hpp"
 #include "walk.hpp"
+#include "walk_fast.hpp"
 
 using namespace vspmm;
 
@@ -99,20 +100,28 @@ int64_t n_out(const vspmm_matrix_s &h, int dir) { return dir == VSPMM_AB ? h.n_r
 
 // ------------------------------------------------------------------- plan
 
+enum Kind { kPlain = 0, kShort = 1, kLong = 2 };
+
 struct Plan {
     Split sp{0, 0};
     int vec = 1;
     int R = 1;
+    int kind = kPlain;
     bool lds = false;
+    size_t lds_bytes = 0;
     int grid = 0;
     int block = 256;
 };
+
+constexpr size_t kLdsMax = 160 * 1024;     // LDS per CU on gfx950
+constexpr int64_t kLongMean = 1024;        // mean entries per slice for k_long
 
 // The lane split of one walk over a matrix with n_slices slices and nnz
 // entries, at width w. Entry lanes G and width lanes WW are powers of two with
 // G * WW <= 64; R = 64 / (G * WW) slices share a wave.
 Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_matrix,
-               int force_group, bool scatter, const void *B, const void *out, int n_cu) {
+               int force_group, bool scatter, const void *B, const void *out, int n_cu,
+               int64_t n_in = 0) {
     Plan pl;
     int vec = 1;
     if (!scatter) {
@@ -142,6 +151,31 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
     pl.sp.log_g = log_g;
     pl.sp.log_ww = log_ww;
     pl.R = 64 >> (log_g + log_ww);
+    const int64_t mean = n_slices > 0 ? nnz / n_slices : 0;
+    if (!scatter && pl.R == 1) {
+        const size_t b_bytes = size_t(n_in) * size_t(w) * elt;
+        if (mean >= kLongMean) {
+            pl.kind = kLong;
+            pl.block = 512;
+            pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(n_slices, int64_t(n_cu) * 16)));
+            return pl;
+        }
+        pl.kind = kShort;
+        // dynamic LDS: the staged B (16-byte aligned) and one ring per wave
+        const size_t ring = size_t(kRing) * (elt == 8 ? 16 : 8);
+        const size_t b_al = (b_bytes + 15) & ~size_t(15);
+        if (b_bytes > 0 && b_al + 16 * ring <= kLdsMax && aligned(B, 16)) {
+            pl.lds = true;
+            pl.lds_bytes = b_al + 16 * ring;
+            pl.block = 1024;
+            pl.grid = std::max(n_cu, 1);
+        } else {
+            pl.lds_bytes = 4 * ring;
+            pl.block = 256;
+            pl.grid = std::max(n_cu, 1) * 4;
+        }
+        return pl;
+    }
     const int64_t per_block = int64_t(pl.block / 64) * pl.R;
     const int64_t want = (n_slices + per_block - 1) / per_block;
     const int64_t cap = int64_t(std::max(n_cu, 1)) * 8;
@@ -162,37 +196,60 @@ void launch_zero(void *p, size_t bytes, hipStream_t s) {
     hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, words);
 }
 
+// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory.
+void allow_lds(const void *fn) {
+    static std::mutex mu;
+    static std::unordered_map<const void *, bool> done;
+    std::lock_guard<std::mutex> lk(mu);
+    if (done[fn]) return;
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsMax));
+    done[fn] = true;
+}
+
+template <bool VCS, typename T, int VEC>
+void launch_aligned_v(const Plan &pl, int n_slices, const int *sptr, const int *vptr,
+                      const T *vals, const int *idx, const T *B, T *out, int w, int n_in,
+                      hipStream_t s) {
+    const dim3 g(pl.grid), b(pl.block);
+    if (pl.kind == kLong) {
+        hipLaunchKernelGGL((k_long<VCS, T, VEC>), g, b, 0, s, n_slices, sptr, vptr, vals, idx, B,
+                           out, w, pl.sp);
+    } else if (pl.kind == kShort) {
+        if (pl.lds) {
+            allow_lds(reinterpret_cast<const void *>(&k_short<VCS, T, VEC, true>));
+            hipLaunchKernelGGL((k_short<VCS, T, VEC, true>), g, b, pl.lds_bytes, s, n_slices, sptr,
+                               vptr, vals, idx, B, out, w, n_in, pl.sp);
+        } else {
+            hipLaunchKernelGGL((k_short<VCS, T, VEC, false>), g, b, pl.lds_bytes, s, n_slices, sptr,
+                               vptr, vals, idx, B, out, w, n_in, pl.sp);
+        }
+    } else if (pl.R == 1 && VCS) {
+        hipLaunchKernelGGL((k_aligned<VCS, T, VEC, true>), g, b, 0, s, n_slices, sptr, vptr, vals,
+                           idx, B, out, w, pl.sp);
+    } else {
+        hipLaunchKernelGGL((k_aligned<VCS, T, VEC, false>), g, b, 0, s, n_slices, sptr, vptr, vals,
+                           idx, B, out, w, pl.sp);
+    }
+}
+
 template <typename T>
 void launch_aligned(bool vcs, const Plan &pl, int n_slices, const int *sptr, const int *vptr,
-                    const T *vals, const int *idx, const T *B, T *out, int w, hipStream_t s) {
-    const dim3 g(pl.grid), b(pl.block);
-    const bool uni = pl.R == 1;
-#define VSPMM_ALIGNED(VCS, VEC, UNI)                                                         \
-    hipLaunchKernelGGL((k_aligned<VCS, T, VEC, UNI>), g, b, 0, s, n_slices, sptr, vptr, vals, \
-                       idx, B, out, w, pl.sp)
-    if (vcs) {
-        if constexpr (sizeof(T) == 4) {
-            if (uni) {
-                if (pl.vec == 4) VSPMM_ALIGNED(true, 4, true);
-                else if (pl.vec == 2) VSPMM_ALIGNED(true, 2, true);
-                else VSPMM_ALIGNED(true, 1, true);
-            } else {
-                if (pl.vec == 4) VSPMM_ALIGNED(true, 4, false);
-                else if (pl.vec == 2) VSPMM_ALIGNED(true, 2, false);
-                else VSPMM_ALIGNED(true, 1, false);
-            }
+                    const T *vals, const int *idx, const T *B, T *out, int w, int n_in,
+                    hipStream_t s) {
+    if constexpr (sizeof(T) == 4) {
+        if (vcs) {
+            if (pl.vec == 4) launch_aligned_v<true, T, 4>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
+            else if (pl.vec == 2) launch_aligned_v<true, T, 2>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
+            else launch_aligned_v<true, T, 1>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
+        } else {
+            if (pl.vec == 4) launch_aligned_v<false, T, 4>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
+            else if (pl.vec == 2) launch_aligned_v<false, T, 2>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
+            else launch_aligned_v<false, T, 1>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
         }
     } else {
-        if constexpr (sizeof(T) == 4) {
-            if (pl.vec == 4) VSPMM_ALIGNED(false, 4, false);
-            else if (pl.vec == 2) VSPMM_ALIGNED(false, 2, false);
-            else VSPMM_ALIGNED(false, 1, false);
-        } else {
-            if (pl.vec == 2) VSPMM_ALIGNED(false, 2, false);
-            else VSPMM_ALIGNED(false, 1, false);
-        }
+        if (pl.vec == 2) launch_aligned_v<false, T, 2>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
+        else launch_aligned_v<false, T, 1>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
     }
-#undef VSPMM_ALIGNED
 }
 
 template <typename T>
@@ -425,16 +482,17 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         return hip_status();
     }
     if (is_aligned(h, dir)) {
+        const int64_t ni = h.n_minor();
         const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
-                                  false, B, out, n_cu);
+                                  false, B, out, n_cu, ni);
         if (h.dtype == VSPMM_F64)
             launch_aligned<double>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
                                    (const double *)h.vals, h.idx, (const double *)B,
-                                   (double *)out, w, s);
+                                   (double *)out, w, int(ni), s);
         else
             launch_aligned<float>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
                                   (const float *)h.vals, h.idx, (const float *)B, (float *)out,
-                                  w, s);
+                                  w, int(ni), s);
         return hip_status();
     }
     if (mode == VSPMM_ATOMIC) {
@@ -476,15 +534,16 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         }
     }
     const int64_t nmin = h.n_minor();
+    const int64_t nmaj = h.n_major();
     const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, false, B, out,
-                              n_cu);
+                              n_cu, nmaj);
     if (h.dtype == VSPMM_F64)
         launch_aligned<double>(false, pl, int(nmin), wl.t_ptr, nullptr,
                                (const double *)wl.t_vals, wl.t_idx, (const double *)B,
-                               (double *)out, w, s);
+                               (double *)out, w, int(nmaj), s);
     else
         launch_aligned<float>(vcs, pl, int(nmin), wl.t_ptr, wl.t_vptr, (const float *)wl.t_vals,
-                              wl.t_idx, (const float *)B, (float *)out, w, s);
+                              wl.t_idx, (const float *)B, (float *)out, w, int(nmaj), s);
     return hip_status();
 }
 
@@ -727,10 +786,12 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     const bool al = is_aligned(*h, dir);
     const bool scatter = !al && mode == VSPMM_ATOMIC;
     const int64_t ns = al || scatter ? h->n_major() : h->n_minor();
+    const int64_t ni = al || scatter ? h->n_minor() : h->n_major();
     // alignment of the caller's buffers is unknown here: assume 16-byte aligned
     alignas(16) static const float probe[4] = {0, 0, 0, 0};
+    const DeviceInfo di = device_info(h->device);
     const Plan pl = make_plan(ns, h->nnz, width, h->elt(), split_matrix, h->force_group, scatter,
-                              probe, probe, 256);
+                              probe, probe, di.ok ? di.n_cu : 256, ni);
     if (entry_lanes) *entry_lanes = 1 << pl.sp.log_g;
     if (width_lanes) *width_lanes = 1 << pl.sp.log_ww;
     if (vec) *vec = pl.vec;

@@ -150,7 +150,9 @@ k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
     const int R = 64 >> log_sub;
     const int chunk = VEC << sp.log_ww;
     const int stride = gridDim.x * waves * R;
-    for (int s = (blockIdx.x * waves + (threadIdx.x >> 6)) * R + sub; s < n_slices; s += stride) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int s = (blockIdx.x * waves + wave) * R + (UNIFORM ? 0 : sub); s < n_slices;
+         s += stride) {
         int e0, e1, ka = 0, kb = 0;
         if constexpr (VCS) {
             ka = sptr[s];
@@ -205,7 +207,9 @@ k_scatter(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
     const int R = 64 >> log_sub;
     const int chunk = 1 << sp.log_ww;
     const int stride = gridDim.x * waves * R;
-    for (int s = (blockIdx.x * waves + (threadIdx.x >> 6)) * R + sub; s < n_slices; s += stride) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int s = (blockIdx.x * waves + wave) * R + (UNIFORM ? 0 : sub); s < n_slices;
+         s += stride) {
         int e0, e1, ka = 0, kb = 0;
         if constexpr (VCS) {
             ka = sptr[s];
