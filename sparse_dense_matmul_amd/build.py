@@ -2,7 +2,11 @@
 
 Run as ``python -m sparse_dense_matmul_amd.build`` or through
 ``__graft_entry__.build()``. The library lands next to this file, where the
-binding loads it from.
+binding loads it from. Each translation unit (the host code with the layout
+builders, and one per kernel family; k_vcs_rows once per vector width and
+k_short once per element type) is
+compiled to an object in parallel under ``_build/``, then the objects are
+linked into the library.
 """
 
 from __future__ import annotations
@@ -11,12 +15,21 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvspmm.so")
-SOURCES = [os.path.join(CSRC, "vspmm.hip")]
+OBJDIR = os.path.join(HERE, "_build")
+# (source, extra defines, object name)
+UNITS = [
+    ("vspmm.hip", [], "vspmm"),
+    ("walk_short.hip", ["-DVSPMM_ELT=float"], "walk_short_f32"),
+    ("walk_short.hip", ["-DVSPMM_ELT=double"], "walk_short_f64"),
+    ("walk_long.hip", [], "walk_long"),
+    ("walk_plain.hip", [], "walk_plain"),
+] + [("walk_vcs_rows.hip", [f"-DVSPMM_VEC={v}"], f"walk_vcs_rows_v{v}") for v in (1, 2, 4)]
 ARCH = "gfx950"
 
 
@@ -29,7 +42,7 @@ def hipcc() -> str:
 
 def flags() -> list[str]:
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # keep the compiler from forming packed fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # only explicit fma contracts, so every instance rounds the same way
@@ -41,9 +54,26 @@ def flags() -> list[str]:
     ]
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = True) -> str:
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = True,
+          jobs: int | None = None) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = hipcc()
+    base = flags() + (extra or [])
+
+    def compile_unit(unit):
+        src, defs, name = unit
+        obj = os.path.join(OBJDIR, name + ".o")
+        cmd = [cc] + base + defs + ["-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        return obj
+
+    jobs = jobs or min(len(UNITS), max(1, os.cpu_count() or 1), 16)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        objs = list(pool.map(compile_unit, UNITS))
     tmp = out + ".tmp"
-    cmd = [hipcc()] + flags() + (extra or []) + ["-o", tmp] + SOURCES
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -1,0 +1,69 @@
+// Launch plans and the launchers of each kernel family. Each family lives in
+// a translation unit of its own (walk_*.hip) so the library's kernels compile
+// in parallel; the host code in vspmm.hip sees only these declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vspmm {
+
+struct Split {
+    int log_ww;  // width lanes per entry lane (log2)
+    int log_g;   // entry lanes per slice (log2)
+};
+
+enum Kind { kPlain = 0, kShort = 1, kLong = 2 };
+
+// How one walk is launched: the lane split, the kernel family and its grid.
+struct Plan {
+    Split sp{0, 0};
+    int vec = 1;         // elements per width lane (one 4-, 8- or 16-byte access)
+    int R = 1;           // slices per wave in the plain walk
+    int kind = kPlain;
+    bool lds = false;    // dense operand staged in LDS
+    size_t lds_bytes = 0;
+    int grid = 0;
+    int block = 256;
+};
+
+constexpr size_t kLdsMax = 160 * 1024;  // LDS per CU on gfx950
+constexpr int kRing = 128;              // k_short: ring positions per wave (two windows)
+
+// The operands of one aligned walk (slices of the walked layout = rows of out).
+template <typename T>
+struct WalkArgs {
+    int n_slices;
+    const int *sptr;  // slice pointers: CSR row_ptr or VCS major_ptr
+    const int *vptr;  // VCS value_ptr (null for CSR)
+    const T *vals;    // CSR values or VCS group values
+    const int *idx;   // minor indices
+    const T *B;       // dense input, n_in x w, row-major
+    T *out;           // dense output, n_slices x w, row-major
+    int w;
+    int n_in;
+};
+
+// Raises a kernel's dynamic LDS limit to a whole CU (once per kernel).
+void allow_lds(const void *fn);
+
+// walk_vcs_rows.hip: short VCS slices, float (one object per VEC).
+template <int VEC>
+void launch_vcs_rows(const Plan &pl, const WalkArgs<float> &a, hipStream_t s);
+
+// walk_short.hip: short CSR slices.
+template <typename T>
+void launch_short(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
+
+// walk_long.hip: long slices, a block per slice.
+template <bool VCS, typename T>
+void launch_long(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
+
+// walk_plain.hip: the plain slice-per-lane-group walk and the atomic scatter.
+template <bool VCS, typename T>
+void launch_plain(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
+template <bool VCS, typename T>
+void launch_scatter(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
+
+}  // namespace vspmm

@@ -318,4 +318,51 @@ k_group_major_ptr(int n_minor, int nnz, const int *__restrict__ tptr, const int 
     }
 }
 
+// ----------------------------------------------------------- utilities
+
+// Fill n bytes (a multiple of 4) at p with zeros; p is 4-byte aligned.
+__global__ void __launch_bounds__(256) k_zero(uint32_t *__restrict__ p, size_t n_words) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uintptr_t mis = ((uintptr_t)p >> 2) & 3;  // words before 16-byte alignment
+    const size_t head = mis ? (4 - mis) : 0;
+    if (head >= n_words) {
+        if (t < n_words) p[t] = 0;
+        return;
+    }
+    if (t < head) p[t] = 0;
+    uint4 *q = reinterpret_cast<uint4 *>(p + head);
+    const size_t n4 = (n_words - head) >> 2;
+    for (size_t k = t; k < n4; k += stride) q[k] = make_uint4(0, 0, 0, 0);
+    const size_t tail0 = head + (n4 << 2);
+    if (t < n_words - tail0) p[tail0 + t] = 0;
+}
+
+// Structure checks: flag bit 1 = pointer array does not start at 0, bit 2 =
+// decreasing, bit 4 = last pointer differs from count, bit 8 = index out of
+// range.
+__global__ void __launch_bounds__(256)
+k_validate_ptr(const int *__restrict__ ptr, int n, int count, int *__restrict__ flag) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= n; i += stride) {
+        const int a = ptr[i];
+        int f = 0;
+        if (i == 0 && a != 0) f |= 1;
+        if (i < n && ptr[i + 1] < a) f |= 2;
+        if (i == n && a != count) f |= 4;
+        if (f) atomicOr(flag, f);
+    }
+}
+
+__global__ void __launch_bounds__(256)
+k_validate_idx(const int *__restrict__ idx, int nnz, int n_minor, int *__restrict__ flag) {
+    const int stride = gridDim.x * blockDim.x;
+    int f = 0;
+    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride) {
+        const int i = idx[p];
+        if (i < 0 || i >= n_minor) f = 8;
+    }
+    if (f) atomicOr(flag, f);
+}
+
 }  // namespace vspmm

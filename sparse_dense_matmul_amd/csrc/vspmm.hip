@@ -13,9 +13,8 @@
 #include <unordered_map>
 
 #include "../../include/vspmm.h"
+#include "launch.hpp"
 #include "schedule.hpp"
-#include "walk.hpp"
-#include "walk_fast.hpp"
 
 using namespace vspmm;
 
@@ -37,6 +36,16 @@ struct vspmm_matrix_s {
     int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
     size_t elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
 };
+
+// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory.
+void vspmm::allow_lds(const void *fn) {
+    static std::mutex mu;
+    static std::unordered_map<const void *, bool> done;
+    std::lock_guard<std::mutex> lk(mu);
+    if (done[fn]) return;
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsMax));
+    done[fn] = true;
+}
 
 namespace {
 
@@ -100,20 +109,6 @@ int64_t n_out(const vspmm_matrix_s &h, int dir) { return dir == VSPMM_AB ? h.n_r
 
 // ------------------------------------------------------------------- plan
 
-enum Kind { kPlain = 0, kShort = 1, kLong = 2 };
-
-struct Plan {
-    Split sp{0, 0};
-    int vec = 1;
-    int R = 1;
-    int kind = kPlain;
-    bool lds = false;
-    size_t lds_bytes = 0;
-    int grid = 0;
-    int block = 256;
-};
-
-constexpr size_t kLdsMax = 160 * 1024;     // LDS per CU on gfx950
 constexpr int64_t kLongMean = 1024;        // mean entries per slice for k_long
 
 // The lane split of one walk over a matrix with n_slices slices and nnz
@@ -121,7 +116,7 @@ constexpr int64_t kLongMean = 1024;        // mean entries per slice for k_long
 // G * WW <= 64; R = 64 / (G * WW) slices share a wave.
 Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_matrix,
                int force_group, bool scatter, const void *B, const void *out, int n_cu,
-               int64_t n_in = 0) {
+               int64_t n_in = 0, bool vcs = false) {
     Plan pl;
     int vec = 1;
     if (!scatter) {
@@ -161,8 +156,9 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
             return pl;
         }
         pl.kind = kShort;
-        // dynamic LDS: the staged B (16-byte aligned) and one ring per wave
-        const size_t ring = size_t(kRing) * (elt == 8 ? 16 : 8);
+        // dynamic LDS: the staged B (16-byte aligned) and per wave either a
+        // ring of (index, value) pairs (CSR) or a 64-int row of marks (VCS)
+        const size_t ring = vcs ? 256 : size_t(kRing) * (elt == 8 ? 16 : 8);
         const size_t b_al = (b_bytes + 15) & ~size_t(15);
         if (b_bytes > 0 && b_al + 16 * ring <= kLdsMax && aligned(B, 16)) {
             pl.lds = true;
@@ -196,79 +192,44 @@ void launch_zero(void *p, size_t bytes, hipStream_t s) {
     hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, words);
 }
 
-// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory.
-void allow_lds(const void *fn) {
-    static std::mutex mu;
-    static std::unordered_map<const void *, bool> done;
-    std::lock_guard<std::mutex> lk(mu);
-    if (done[fn]) return;
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsMax));
-    done[fn] = true;
+template <typename T>
+WalkArgs<T> walk_args(int64_t n_slices, const int32_t *sptr, const int32_t *vptr, const void *vals,
+                      const int32_t *idx, const void *B, void *out, int w, int64_t n_in) {
+    return WalkArgs<T>{int(n_slices), sptr, vptr, static_cast<const T *>(vals), idx,
+                       static_cast<const T *>(B), static_cast<T *>(out), w, int(n_in)};
 }
 
-template <bool VCS, typename T, int VEC>
-void launch_aligned_v(const Plan &pl, int n_slices, const int *sptr, const int *vptr,
-                      const T *vals, const int *idx, const T *B, T *out, int w, int n_in,
-                      hipStream_t s) {
-    const dim3 g(pl.grid), b(pl.block);
+// Dispatches one aligned walk to its kernel family.
+template <typename T>
+void launch_aligned(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     if (pl.kind == kLong) {
-        hipLaunchKernelGGL((k_long<VCS, T, VEC>), g, b, 0, s, n_slices, sptr, vptr, vals, idx, B,
-                           out, w, pl.sp);
-    } else if (pl.kind == kShort) {
-        if (pl.lds) {
-            allow_lds(reinterpret_cast<const void *>(&k_short<VCS, T, VEC, true>));
-            hipLaunchKernelGGL((k_short<VCS, T, VEC, true>), g, b, pl.lds_bytes, s, n_slices, sptr,
-                               vptr, vals, idx, B, out, w, n_in, pl.sp);
-        } else {
-            hipLaunchKernelGGL((k_short<VCS, T, VEC, false>), g, b, pl.lds_bytes, s, n_slices, sptr,
-                               vptr, vals, idx, B, out, w, n_in, pl.sp);
-        }
-    } else if (pl.R == 1 && VCS) {
-        hipLaunchKernelGGL((k_aligned<VCS, T, VEC, true>), g, b, 0, s, n_slices, sptr, vptr, vals,
-                           idx, B, out, w, pl.sp);
-    } else {
-        hipLaunchKernelGGL((k_aligned<VCS, T, VEC, false>), g, b, 0, s, n_slices, sptr, vptr, vals,
-                           idx, B, out, w, pl.sp);
-    }
-}
-
-template <typename T>
-void launch_aligned(bool vcs, const Plan &pl, int n_slices, const int *sptr, const int *vptr,
-                    const T *vals, const int *idx, const T *B, T *out, int w, int n_in,
-                    hipStream_t s) {
-    if constexpr (sizeof(T) == 4) {
-        if (vcs) {
-            if (pl.vec == 4) launch_aligned_v<true, T, 4>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-            else if (pl.vec == 2) launch_aligned_v<true, T, 2>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-            else launch_aligned_v<true, T, 1>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-        } else {
-            if (pl.vec == 4) launch_aligned_v<false, T, 4>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-            else if (pl.vec == 2) launch_aligned_v<false, T, 2>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-            else launch_aligned_v<false, T, 1>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-        }
-    } else {
-        if (pl.vec == 2) launch_aligned_v<false, T, 2>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-        else launch_aligned_v<false, T, 1>(pl, n_slices, sptr, vptr, vals, idx, B, out, w, n_in, s);
-    }
-}
-
-template <typename T>
-void launch_scatter(bool vcs, const Plan &pl, int n_slices, const int *sptr, const int *vptr,
-                    const T *vals, const int *idx, const T *B, T *out, int w, hipStream_t s) {
-    const dim3 g(pl.grid), b(pl.block);
-    if (vcs) {
         if constexpr (sizeof(T) == 4) {
-            if (pl.R == 1)
-                hipLaunchKernelGGL((k_scatter<true, T, true>), g, b, 0, s, n_slices, sptr, vptr,
-                                   vals, idx, B, out, w, pl.sp);
-            else
-                hipLaunchKernelGGL((k_scatter<true, T, false>), g, b, 0, s, n_slices, sptr, vptr,
-                                   vals, idx, B, out, w, pl.sp);
+            if (vcs) return launch_long<true, T>(pl, a, s);
         }
-    } else {
-        hipLaunchKernelGGL((k_scatter<false, T, false>), g, b, 0, s, n_slices, sptr, vptr, vals,
-                           idx, B, out, w, pl.sp);
+        return launch_long<false, T>(pl, a, s);
     }
+    if (pl.kind == kShort) {
+        if constexpr (sizeof(T) == 4) {
+            if (vcs) {
+                if (pl.vec == 4) return launch_vcs_rows<4>(pl, a, s);
+                if (pl.vec == 2) return launch_vcs_rows<2>(pl, a, s);
+                return launch_vcs_rows<1>(pl, a, s);
+            }
+        }
+        return launch_short<T>(pl, a, s);
+    }
+    if constexpr (sizeof(T) == 4) {
+        if (vcs) return launch_plain<true, T>(pl, a, s);
+    }
+    launch_plain<false, T>(pl, a, s);
+}
+
+template <typename T>
+void launch_scatter_any(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
+    if constexpr (sizeof(T) == 4) {
+        if (vcs) return launch_scatter<true, T>(pl, a, s);
+    }
+    launch_scatter<false, T>(pl, a, s);
 }
 
 // ------------------------------------------------------------- workspace
@@ -484,15 +445,13 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     if (is_aligned(h, dir)) {
         const int64_t ni = h.n_minor();
         const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
-                                  false, B, out, n_cu, ni);
+                                  false, B, out, n_cu, ni, vcs);
         if (h.dtype == VSPMM_F64)
-            launch_aligned<double>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
-                                   (const double *)h.vals, h.idx, (const double *)B,
-                                   (double *)out, w, int(ni), s);
+            launch_aligned<double>(vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr, h.vals,
+                                                              h.idx, B, out, w, ni), s);
         else
-            launch_aligned<float>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
-                                  (const float *)h.vals, h.idx, (const float *)B, (float *)out,
-                                  w, int(ni), s);
+            launch_aligned<float>(vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr, h.vals,
+                                                            h.idx, B, out, w, ni), s);
         return hip_status();
     }
     if (mode == VSPMM_ATOMIC) {
@@ -500,13 +459,11 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
                                   true, B, out, n_cu);
         launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
         if (h.dtype == VSPMM_F64)
-            launch_scatter<double>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
-                                   (const double *)h.vals, h.idx, (const double *)B,
-                                   (double *)out, w, s);
+            launch_scatter_any<double>(vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr,
+                                                                  h.vals, h.idx, B, out, w, 0), s);
         else
-            launch_scatter<float>(vcs, pl, int(h.n_major()), h.sptr, h.vptr,
-                                  (const float *)h.vals, h.idx, (const float *)B, (float *)out,
-                                  w, s);
+            launch_scatter_any<float>(vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr,
+                                                                h.vals, h.idx, B, out, w, 0), s);
         return hip_status();
     }
     // deterministic: build (or reuse) the opposite layout, then walk it aligned
@@ -536,14 +493,13 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     const int64_t nmin = h.n_minor();
     const int64_t nmaj = h.n_major();
     const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, false, B, out,
-                              n_cu, nmaj);
+                              n_cu, nmaj, vcs);
     if (h.dtype == VSPMM_F64)
-        launch_aligned<double>(false, pl, int(nmin), wl.t_ptr, nullptr,
-                               (const double *)wl.t_vals, wl.t_idx, (const double *)B,
-                               (double *)out, w, int(nmaj), s);
+        launch_aligned<double>(false, pl, walk_args<double>(nmin, wl.t_ptr, nullptr, wl.t_vals,
+                                                            wl.t_idx, B, out, w, nmaj), s);
     else
-        launch_aligned<float>(vcs, pl, int(nmin), wl.t_ptr, wl.t_vptr, (const float *)wl.t_vals,
-                              wl.t_idx, (const float *)B, (float *)out, w, int(nmaj), s);
+        launch_aligned<float>(vcs, pl, walk_args<float>(nmin, wl.t_ptr, wl.t_vptr, wl.t_vals,
+                                                        wl.t_idx, B, out, w, nmaj), s);
     return hip_status();
 }
 
@@ -791,7 +747,7 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     alignas(16) static const float probe[4] = {0, 0, 0, 0};
     const DeviceInfo di = device_info(h->device);
     const Plan pl = make_plan(ns, h->nnz, width, h->elt(), split_matrix, h->force_group, scatter,
-                              probe, probe, di.ok ? di.n_cu : 256, ni);
+                              probe, probe, di.ok ? di.n_cu : 256, ni, vcs);
     if (entry_lanes) *entry_lanes = 1 << pl.sp.log_g;
     if (width_lanes) *width_lanes = 1 << pl.sp.log_ww;
     if (vec) *vec = pl.vec;

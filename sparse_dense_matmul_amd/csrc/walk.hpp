@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace vspmm {
 
 template <typename T, int N>
@@ -56,11 +58,99 @@ __device__ __forceinline__ float readlane(float x, int l) {
 __device__ __forceinline__ void atomic_add_t(float *p, float v) { unsafeAtomicAdd(p, v); }
 __device__ __forceinline__ void atomic_add_t(double *p, double v) { unsafeAtomicAdd(p, v); }
 
-// Lane geometry of one product.
-struct Split {
-    int log_ww;  // width lanes per entry lane (log2)
-    int log_g;   // entry lanes per slice (log2)
-};
+// The G entry lanes of a slice are summed by a fixed butterfly over the slot
+// bits of the lane id (bits log_ww .. log_ww + log_g - 1), highest bit first:
+// at each level a lane adds the partial of the lane whose id differs in that
+// bit. The pairing and order depend only on G, never on the width lanes, so
+// a column gets the same bits in any batch. slot_reduce_xor does it with
+// lane shuffles (any sub-wave size); slot_reduce_dpp does the same pairing
+// with cross-lane VALU ops for a full wave (G * WW == 64).
+template <typename T, int VEC>
+__device__ __forceinline__ void slot_reduce_xor(T (&acc)[VEC], int log_ww, int log_sub) {
+    for (int off = (1 << log_sub) >> 1; off >= (1 << log_ww); off >>= 1) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+    }
+}
+
+// One butterfly level on a 32-bit value: partner differs in lane bit `bit`.
+__device__ __forceinline__ float level_f(float v, int bit) {
+    const uint32_t u = __float_as_uint(v);
+    switch (bit) {
+        case 5: {
+            const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+        case 4: {
+            const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+        // within a row of 16 the rotations pair lanes like xor because the
+        // higher in-row bit was already summed (partials are equal there)
+        case 3: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xf, 0xf, false));
+        case 2: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x124, 0xf, 0xf, false));
+        case 1: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xf, 0xf, false));
+        default: return v + __int_as_float(__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xf, 0xf, false));
+    }
+}
+
+__device__ __forceinline__ double partner_d(double v, int bit) {
+    const unsigned long long u = __double_as_longlong(v);
+    uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    uint32_t plo, phi;
+    switch (bit) {
+        case 5: {
+            const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+            const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+            // lanes in the low half get the partner from the second result
+            const bool low = (__lane_id() & 32) == 0;
+            plo = low ? a[1] : a[0];
+            phi = low ? b[1] : b[0];
+            break;
+        }
+        case 4: {
+            const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+            const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+            const bool even = (__lane_id() & 16) == 0;
+            plo = even ? a[1] : a[0];
+            phi = even ? b[1] : b[0];
+            break;
+        }
+        default: {
+            const int ctrl = bit == 3 ? 0x128 : bit == 2 ? 0x124 : bit == 1 ? 0x4E : 0xB1;
+            switch (ctrl) {
+                case 0x128:
+                    plo = __builtin_amdgcn_update_dpp(0, (int)lo, 0x128, 0xf, 0xf, false);
+                    phi = __builtin_amdgcn_update_dpp(0, (int)hi, 0x128, 0xf, 0xf, false);
+                    break;
+                case 0x124:
+                    plo = __builtin_amdgcn_update_dpp(0, (int)lo, 0x124, 0xf, 0xf, false);
+                    phi = __builtin_amdgcn_update_dpp(0, (int)hi, 0x124, 0xf, 0xf, false);
+                    break;
+                case 0x4E:
+                    plo = __builtin_amdgcn_update_dpp(0, (int)lo, 0x4E, 0xf, 0xf, false);
+                    phi = __builtin_amdgcn_update_dpp(0, (int)hi, 0x4E, 0xf, 0xf, false);
+                    break;
+                default:
+                    plo = __builtin_amdgcn_update_dpp(0, (int)lo, 0xB1, 0xf, 0xf, false);
+                    phi = __builtin_amdgcn_update_dpp(0, (int)hi, 0xB1, 0xf, 0xf, false);
+                    break;
+            }
+        }
+    }
+    return __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void slot_reduce_dpp(T (&acc)[VEC], int log_ww) {
+    for (int bit = 5; bit >= log_ww; --bit) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (sizeof(T) == 4) acc[e] = level_f(acc[e], bit);
+            else acc[e] = acc[e] + partner_d(acc[e], bit);
+        }
+    }
+}
 
 // Walks the entries [e0, e1) of one slice in steps of G. For a VCS slice the
 // value of each entry is its group's: with UNIFORM (one slice per wave) the
@@ -179,10 +269,7 @@ k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                                                     acc[e] = fma_t(v, b[e], acc[e]);
                                             }
                                         });
-            for (int off = 1 << sp.log_ww; off < (1 << log_sub); off <<= 1) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-            }
+            slot_reduce_xor<T, VEC>(acc, sp.log_ww, log_sub);
             if (slot == 0 && act) store_vec<T, VEC>(out + (size_t)s * w + col, acc);
         }
     }
@@ -231,51 +318,6 @@ k_scatter(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                                         });
         }
     }
-}
-
-// Fill n bytes (a multiple of 4) at p with zeros; p is 4-byte aligned.
-__global__ void __launch_bounds__(256) k_zero(uint32_t *__restrict__ p, size_t n_words) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uintptr_t mis = ((uintptr_t)p >> 2) & 3;  // words before 16-byte alignment
-    const size_t head = mis ? (4 - mis) : 0;
-    if (head >= n_words) {
-        if (t < n_words) p[t] = 0;
-        return;
-    }
-    if (t < head) p[t] = 0;
-    uint4 *q = reinterpret_cast<uint4 *>(p + head);
-    const size_t n4 = (n_words - head) >> 2;
-    for (size_t k = t; k < n4; k += stride) q[k] = make_uint4(0, 0, 0, 0);
-    const size_t tail0 = head + (n4 << 2);
-    if (t < n_words - tail0) p[tail0 + t] = 0;
-}
-
-// Structure checks: flag bit 1 = pointer array does not start at 0, bit 2 =
-// decreasing, bit 4 = last pointer differs from count, bit 8 = index out of
-// range.
-__global__ void __launch_bounds__(256)
-k_validate_ptr(const int *__restrict__ ptr, int n, int count, int *__restrict__ flag) {
-    const int stride = gridDim.x * blockDim.x;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= n; i += stride) {
-        const int a = ptr[i];
-        int f = 0;
-        if (i == 0 && a != 0) f |= 1;
-        if (i < n && ptr[i + 1] < a) f |= 2;
-        if (i == n && a != count) f |= 4;
-        if (f) atomicOr(flag, f);
-    }
-}
-
-__global__ void __launch_bounds__(256)
-k_validate_idx(const int *__restrict__ idx, int nnz, int n_minor, int *__restrict__ flag) {
-    const int stride = gridDim.x * blockDim.x;
-    int f = 0;
-    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride) {
-        const int i = idx[p];
-        if (i < 0 || i >= n_minor) f = 8;
-    }
-    if (f) atomicOr(flag, f);
 }
 
 }  // namespace vspmm

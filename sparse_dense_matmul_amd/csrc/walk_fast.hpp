@@ -206,12 +206,11 @@ __device__ __forceinline__ void batch_consume(const Pending<T, VEC, NS> &pd, T (
     }
 }
 
+// Sum of the slice's G entry lanes for a full-wave split (G * WW == 64).
 template <typename T, int VEC>
 __device__ __forceinline__ void xor_reduce(T (&acc)[VEC], int from, int to) {
-    for (int off = from; off < to; off <<= 1) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-    }
+    (void)to;
+    slot_reduce_dpp<T, VEC>(acc, __builtin_ctz(from));
 }
 
 // Accumulates the batches starting at c, c + stride, ... below e1 into acc,
@@ -338,7 +337,6 @@ __device__ __forceinline__ T lanes_at(const T (&X)[N], int g) {
 // Per-wave LDS ring of (index, value) pairs: positions of the round are
 // written 64 at a time (one window) and read back by the entry lanes, so each
 // step costs two LDS reads instead of shuffles and scalar loops.
-constexpr int kRing = 128;  // positions per wave (two windows)
 
 template <typename T>
 struct RingEntry {
@@ -349,7 +347,7 @@ struct RingEntry {
 // out[s] for each slice of a loaded round (width chunk c0). Windows are
 // turned into (index, value) pairs one at a time; every step whose entries
 // are already in the ring is then walked, finishing slices as they end.
-template <bool VCS, typename T, int VEC, int NWR, int GWR>
+template <bool VCS, typename T, int VEC, int NWR, int GWR, int SB>
 __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR],
                                               const T (&V)[NWR], const int (&GS)[GWR],
                                               const T (&GV)[GWR], int c0, int lane, int slot,
@@ -397,16 +395,37 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
                 if (i >= r.nsl) break;
                 e1 = readlane(r.he, i + 1);
             }
-            if (i >= r.nsl || min(q + G, e1) > ready) break;
-            const int p = q + slot;
-            const RingEntry<T> re = ring[(p - r.E0) & (kRing - 1)];
-            if (p < e1 && act) {
-                T x[VEC];
-                load_vec<T, VEC>(Bs + (size_t)re.ix * w + col, x);
+            if (i >= r.nsl) break;
+            // steps of slice i whose entries are all in the ring: every step
+            // up to the slice's end if it ends before `ready`, else whole steps
+            const int avail = min(e1, ready);
+            if (avail <= q) break;
+            int nb = avail == e1 ? (avail - q + G - 1) >> sp.log_g : (avail - q) >> sp.log_g;
+            if (nb == 0) break;
+            nb = min(nb, SB);
+            RingEntry<T> re[SB];
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] = fma_t(re.v, x[e], acc[e]);
+            for (int t = 0; t < SB; ++t)
+                if (t < nb) re[t] = ring[(q + t * G + slot - r.E0) & (kRing - 1)];
+            T bv[SB][VEC];
+#pragma unroll
+            for (int t = 0; t < SB; ++t) {
+                if (t < nb && act && q + t * G + slot < e1) {
+                    load_vec<T, VEC>(Bs + (size_t)re[t].ix * w + col, bv[t]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) bv[t][e] = T(0);
+                }
             }
-            q += G;
+#pragma unroll
+            for (int t = 0; t < SB; ++t) {
+                if (t < nb) {
+                    const T v = q + t * G + slot < e1 ? re[t].v : T(0);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[e] = fma_t(v, bv[t][e], acc[e]);
+                }
+            }
+            q += nb * G;
         }
     }
     // slices left after the last window are empty (no entries): zeros
@@ -553,11 +572,11 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
             big_slice<VCS, T, VEC, SB>(sa, lane, slot, cl, sp, sptr, vptr, vals, idx, Bs, out, w);
             sa += 1;
         } else {
-            round_compute<VCS, T, VEC, NWR, GWR>(r, W, V, GS, GV, 0, lane, slot, cl, sp, Bs, ring,
-                                                 out, w);
-            for (int c0 = chunk; c0 < w; c0 += chunk)
-                round_compute<VCS, T, VEC, NWR, GWR>(r, W, V, GS, GV, c0, lane, slot, cl, sp, Bs,
+            round_compute<VCS, T, VEC, NWR, GWR, SB>(r, W, V, GS, GV, 0, lane, slot, cl, sp, Bs,
                                                      ring, out, w);
+            for (int c0 = chunk; c0 < w; c0 += chunk)
+                round_compute<VCS, T, VEC, NWR, GWR, SB>(r, W, V, GS, GV, c0, lane, slot, cl, sp,
+                                                         Bs, ring, out, w);
             sa += r.nsl;
         }
         if (sa < s_end) {

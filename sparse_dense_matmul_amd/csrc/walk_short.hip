@@ -1,0 +1,40 @@
+// Launcher of k_short (short CSR slices). Built once per element type
+// (-DVSPMM_ELT=float or double), each object holding that type's instances.
+#include "launch.hpp"
+#include "walk_fast.hpp"
+
+#ifndef VSPMM_ELT
+#error "build with -DVSPMM_ELT=float or double"
+#endif
+
+namespace vspmm {
+
+namespace {
+
+template <typename T, int VEC>
+void launch_short_v(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
+    const dim3 g(pl.grid), b(pl.block);
+    if (pl.lds) {
+        allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true>));
+        hipLaunchKernelGGL((k_short<false, T, VEC, true>), g, b, pl.lds_bytes, s, a.n_slices,
+                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp);
+    } else {
+        hipLaunchKernelGGL((k_short<false, T, VEC, false>), g, b, pl.lds_bytes, s, a.n_slices,
+                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp);
+    }
+}
+
+}  // namespace
+
+template <typename T>
+void launch_short(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
+    if constexpr (sizeof(T) == 4) {
+        if (pl.vec == 4) return launch_short_v<T, 4>(pl, a, s);
+    }
+    if (pl.vec == 2) return launch_short_v<T, 2>(pl, a, s);
+    launch_short_v<T, 1>(pl, a, s);
+}
+
+template void launch_short<VSPMM_ELT>(const Plan &, const WalkArgs<VSPMM_ELT> &, hipStream_t);
+
+}  // namespace vspmm
