@@ -21,14 +21,24 @@ Minimum algorithmic bytes of one product = the compressed structure the
 product walks (4(n_major+1) + 4 G + 4(G+1) + 4 nnz) + 4 w (n_in + n_out).
 value = the four products' minimum bytes / the sum of their average times.
 
+roofline.traffic is the HBM bytes per launch of the dominant kernel, from two
+rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this script, each scaled
+by what the same counter reads for a plain device copy of known size
+(--copy-calibration). The figures sit in a record under profiles/ keyed by a
+hash of the kernel sources; when the sources have changed since, traffic is
+null.
+
 Prints ONE JSON line. --gpus above 1 is refused: this build runs on one GPU.
 """
 
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,6 +49,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "HBM GB/s (% of peak) for VCS SpMM 60k×2k, 6M nnz, width 16, 4 directions"
 PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+CSRC = os.path.join(ROOT, "sparse_dense_matmul_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 # name, layout of the handle, direction, walk used in atomic mode
 DIRECTIONS = [
@@ -57,6 +70,45 @@ def dense_bytes(shape, direction, w):
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources (every file under csrc/, by name)."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_record(kernel, direction, width):
+    """HBM bytes per launch from the counter record in profiles/, when its
+    source hash matches the sources built now; else None."""
+    want = kernel_source_hash()
+    pat = re.compile(r"^traffic-record:\s*(.*)$")
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(f):
+            m = pat.match(line.strip())
+            if not m:
+                continue
+            kv = dict(tok.split("=", 1) for tok in m.group(1).split())
+            if (kv.get("kernel") == kernel and kv.get("direction") == direction and
+                    int(kv.get("width", -1)) == width and kv.get("source_sha256") == want):
+                return int(kv["hbm_bytes"]), os.path.relpath(f, ROOT)
+    return None, None
+
+
+def copy_calibration(mib):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
 def cpu_baseline(layouts, width, budget_s):
@@ -92,11 +144,16 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-mode timings")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
               "build (the product shards by major slices; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
 
@@ -178,13 +235,14 @@ def main():
             us = time_direction(d, "atomic")
             b = L.nbytes() + dense_bytes(L.shape, direction, w)
             entry.update(us=round(us, 2), min_bytes=b, mode="aligned",
-                         kernel="k_short" if lay == "vcsr" else "k_long")
+                         kernel=copies[0]["A"][lay].plan_info(w, direction)["kernel_name"])
         else:
             us = time_direction(d, "deterministic")
             other = layouts["vcsc" if lay == "vcsr" else "vcsr"]  # the regrouped layout walked
             b = other.nbytes() + dense_bytes(L.shape, direction, w)
             entry.update(us=round(us, 2), min_bytes=b, mode="deterministic (pass 2)",
-                         kernel="k_long" if lay == "vcsr" else "k_short")
+                         kernel=copies[0]["A"][lay].plan_info(w, direction,
+                                                              "deterministic")["kernel_name"])
             if not args.no_atomic:
                 ua = time_direction(d, "atomic")
                 ba = L.nbytes() + dense_bytes(L.shape, direction, w)
@@ -210,6 +268,7 @@ def main():
     r4 = c0["A"]["vcsc"].spmm(c0["B"]["AB"], "AB", mode="deterministic", workspace=ws)
     repeat_ok = bool(torch.equal(r1, r2) and torch.equal(r3, r4))
 
+    traffic, traffic_src = traffic_record(per_dir[dom]["kernel"], dom, w)
     atomic_us = sum(e["atomic"]["us"] if "atomic" in e else e["us"] for e in per_dir.values())
     atomic_bytes = sum(e["atomic"]["min_bytes"] if "atomic" in e else e["min_bytes"]
                        for e in per_dir.values())
@@ -239,7 +298,10 @@ def main():
         "det_build_plus_first_product_ms": build_ms,
         "roofline": {"bound": "hbm", "kernel": f"{per_dir[dom]['kernel']} ({dom})",
                      "achieved": per_dir[dom]["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": per_dir[dom]["frac"], "traffic": None},
+                     "frac": per_dir[dom]["frac"], "traffic": traffic,
+                     "traffic_source": traffic_src,
+                     "algorithmic_bytes": per_dir[dom]["min_bytes"],
+                     "launch_us": per_dir[dom]["us"]},
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }

@@ -187,12 +187,24 @@ vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_va
  * indices). Both host. */
 vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_bytes);
 
+/* Kernel family a product's walk runs in (reported by vspmm_plan_info). */
+typedef enum {
+    VSPMM_KERNEL_PLAIN = 0,   /* slices side by side, one lane group each */
+    VSPMM_KERNEL_SHORT = 1,   /* a wave walks a block of short slices in register rounds */
+    VSPMM_KERNEL_LONG = 2,    /* a block of waves walks one long slice */
+    VSPMM_KERNEL_SCATTER = 3  /* misaligned walk with float atomics */
+} vspmm_kernel;
+
 /* The lane split a product would use (host outputs, any may be NULL):
- * entry lanes per slice, width lanes, elements per lane, slices per wave and
- * whether the gathered operand is staged in LDS. */
+ * entry lanes per slice, width lanes, elements per lane, slices per wave,
+ * whether the gathered operand is staged in LDS, and the kernel family
+ * (vspmm_kernel). In deterministic mode a misaligned product reports its
+ * second pass, the aligned walk over the opposite layout. The caller's buffer
+ * alignment is not known here, so 16-byte aligned operands are assumed. */
 vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
                              vspmm_mode mode, int32_t *entry_lanes, int32_t *width_lanes,
-                             int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged);
+                             int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged,
+                             int32_t *kernel);
 
 /* A static string naming the status. */
 const char *vspmm_status_string(vspmm_status st);

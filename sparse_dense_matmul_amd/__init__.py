@@ -50,7 +50,7 @@ EXPORTS = {
     "vspmm_regroup_vcs": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_footprint": ([_vp, _P(_sz), _P(_sz)], ctypes.c_int),
     "vspmm_plan_info": ([_vp, _i64, ctypes.c_int, ctypes.c_int, _P(_i32), _P(_i32), _P(_i32),
-                         _P(_i32), _P(_i32)], ctypes.c_int),
+                         _P(_i32), _P(_i32), _P(_i32)], ctypes.c_int),
     "vspmm_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -196,11 +196,18 @@ class SparseMatrix:
         return int(a.value), int(b.value)
 
     def plan_info(self, width: int, direction: str = "AB", mode: str = "atomic") -> dict:
-        vals = [_i32(0) for _ in range(5)]
+        vals = [_i32(0) for _ in range(6)]
         _check(lib.vspmm_plan_info(self._h, width, DIRECTIONS[direction], MODES[mode],
                                    *[ctypes.byref(v) for v in vals]), "vspmm_plan_info")
-        keys = ("entry_lanes", "width_lanes", "vec", "slices_per_wave", "lds_staged")
-        return {k: int(v.value) for k, v in zip(keys, vals)}
+        keys = ("entry_lanes", "width_lanes", "vec", "slices_per_wave", "lds_staged", "kernel")
+        info = {k: int(v.value) for k, v in zip(keys, vals)}
+        # the walked layout: the handle's own, or the opposite one in deterministic mode
+        aligned = (self.layout != "vcsc") == (direction == "AB")
+        walked = self.layout if aligned or mode == "atomic" else \
+            {"vcsr": "vcsc", "vcsc": "vcsr", "csr": "csr"}[self.layout]
+        short = "k_vcs_rows" if walked != "csr" else "k_short"
+        info["kernel_name"] = {0: "k_aligned", 1: short, 2: "k_long", 3: "k_scatter"}[info["kernel"]]
+        return info
 
 
 class VcsMatrix(SparseMatrix):

@@ -30,6 +30,11 @@ struct Plan {
 
 constexpr size_t kLdsMax = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kRing = 128;              // k_short: ring positions per wave (two windows)
+// k_vcs_rows: entry windows and group windows per round, and the per-wave LDS
+// they need (a mark byte per round position, a float per round group)
+constexpr int kRowsNWR = 16;
+constexpr int kRowsGWR = 4;
+constexpr int kRowsWaveLds = 64 * kRowsNWR + 256 * kRowsGWR;
 
 // The operands of one aligned walk (slices of the walked layout = rows of out).
 template <typename T>

@@ -157,8 +157,9 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
         }
         pl.kind = kShort;
         // dynamic LDS: the staged B (16-byte aligned) and per wave either a
-        // ring of (index, value) pairs (CSR) or a 64-int row of marks (VCS)
-        const size_t ring = vcs ? 256 : size_t(kRing) * (elt == 8 ? 16 : 8);
+        // ring of (index, value) pairs (CSR) or the round's group marks and
+        // values (VCS)
+        const size_t ring = vcs ? size_t(kRowsWaveLds) : size_t(kRing) * (elt == 8 ? 16 : 8);
         const size_t b_al = (b_bytes + 15) & ~size_t(15);
         if (b_bytes > 0 && b_al + 16 * ring <= kLdsMax && aligned(B, 16)) {
             pl.lds = true;
@@ -731,7 +732,8 @@ vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_byt
 
 vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
                              vspmm_mode mode, int32_t *entry_lanes, int32_t *width_lanes,
-                             int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged) {
+                             int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged,
+                             int32_t *kernel) {
     if (vspmm_status st = check_handle(h)) return st;
     if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
     if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
@@ -753,6 +755,11 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     if (vec) *vec = pl.vec;
     if (slices_per_wave) *slices_per_wave = pl.R;
     if (lds_staged) *lds_staged = pl.lds ? 1 : 0;
+    if (kernel)
+        *kernel = scatter ? VSPMM_KERNEL_SCATTER
+                          : pl.kind == kLong ? VSPMM_KERNEL_LONG
+                                             : pl.kind == kShort ? VSPMM_KERNEL_SHORT
+                                                                 : VSPMM_KERNEL_PLAIN;
     return VSPMM_OK;
 }
 
