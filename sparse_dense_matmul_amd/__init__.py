@@ -205,8 +205,10 @@ class SparseMatrix:
         aligned = (self.layout != "vcsc") == (direction == "AB")
         walked = self.layout if aligned or mode == "atomic" else \
             {"vcsr": "vcsc", "vcsc": "vcsr", "csr": "csr"}[self.layout]
-        short = "k_vcs_rows" if walked != "csr" else "k_short"
-        info["kernel_name"] = {0: "k_aligned", 1: short, 2: "k_long", 3: "k_scatter"}[info["kernel"]]
+        vcs = walked != "csr"
+        info["kernel_name"] = {0: "k_aligned", 1: "k_vcs_rows" if vcs else "k_short",
+                               2: "k_vcs_long" if vcs else "k_long",
+                               3: "k_scatter"}[info["kernel"]]
         return info
 
 

@@ -3,7 +3,7 @@
 Run as ``python -m sparse_dense_matmul_amd.build`` or through
 ``__graft_entry__.build()``. The library lands next to this file, where the
 binding loads it from. Each translation unit (the host code with the layout
-builders, and one per kernel family; k_vcs_rows once per vector width and
+builders, and one per kernel family; the VCS walks once per vector width and
 k_short once per element type) is
 compiled to an object in parallel under ``_build/``, then the objects are
 linked into the library.
@@ -29,7 +29,8 @@ UNITS = [
     ("walk_short.hip", ["-DVSPMM_ELT=double"], "walk_short_f64"),
     ("walk_long.hip", [], "walk_long"),
     ("walk_plain.hip", [], "walk_plain"),
-] + [("walk_vcs_rows.hip", [f"-DVSPMM_VEC={v}"], f"walk_vcs_rows_v{v}") for v in (1, 2, 4)]
+] + [(f"walk_vcs_{kind}.hip", [f"-DVSPMM_VEC={v}"], f"walk_vcs_{kind}_v{v}")
+     for kind in ("rows", "long") for v in (1, 2, 4)]
 ARCH = "gfx950"
 
 

@@ -57,11 +57,15 @@ void allow_lds(const void *fn);
 template <int VEC>
 void launch_vcs_rows(const Plan &pl, const WalkArgs<float> &a, hipStream_t s);
 
+// walk_vcs_long.hip: long VCS slices, float (one object per VEC).
+template <int VEC>
+void launch_vcs_long(const Plan &pl, const WalkArgs<float> &a, hipStream_t s);
+
 // walk_short.hip: short CSR slices.
 template <typename T>
 void launch_short(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
 
-// walk_long.hip: long slices, a block per slice.
+// walk_long.hip: long CSR slices, a block per slice.
 template <bool VCS, typename T>
 void launch_long(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
 

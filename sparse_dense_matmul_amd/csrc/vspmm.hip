@@ -147,8 +147,10 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
     pl.sp.log_ww = log_ww;
     pl.R = 64 >> (log_g + log_ww);
     const int64_t mean = n_slices > 0 ? nnz / n_slices : 0;
-    if (!scatter && pl.R == 1) {
-        const size_t b_bytes = size_t(n_in) * size_t(w) * elt;
+    const size_t b_bytes = size_t(n_in) * size_t(w) * elt;
+    // the VCS walks address B with 32-bit byte offsets and 24-bit row numbers
+    const bool small_b = b_bytes < (size_t(1) << 32) && n_in < (int64_t(1) << 24);
+    if (!scatter && pl.R == 1 && (!vcs || small_b)) {
         if (mean >= kLongMean) {
             pl.kind = kLong;
             pl.block = 512;
@@ -205,7 +207,11 @@ template <typename T>
 void launch_aligned(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     if (pl.kind == kLong) {
         if constexpr (sizeof(T) == 4) {
-            if (vcs) return launch_long<true, T>(pl, a, s);
+            if (vcs) {
+                if (pl.vec == 4) return launch_vcs_long<4>(pl, a, s);
+                if (pl.vec == 2) return launch_vcs_long<2>(pl, a, s);
+                return launch_vcs_long<1>(pl, a, s);
+            }
         }
         return launch_long<false, T>(pl, a, s);
     }

@@ -1,4 +1,4 @@
-// Launcher of k_long (long slices, a block per slice).
+// Launcher of k_long (long CSR slices, a block per slice).
 #include "launch.hpp"
 #include "walk_fast.hpp"
 
@@ -21,7 +21,6 @@ void launch_long(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
 #undef VSPMM_LONG
 }
 
-template void launch_long<true, float>(const Plan &, const WalkArgs<float> &, hipStream_t);
 template void launch_long<false, float>(const Plan &, const WalkArgs<float> &, hipStream_t);
 template void launch_long<false, double>(const Plan &, const WalkArgs<double> &, hipStream_t);
 

@@ -103,6 +103,276 @@ struct SlotSum {
     }
 };
 
+// Lane geometry of the VCS walks: G entry lanes per step, NSTEP steps per
+// 64-entry window, taken in stages of SBV steps whose gathers are in flight
+// together (NSB stages per window).
+template <int LOG_WW, int VEC>
+struct Geo {
+    static constexpr int G = 64 >> LOG_WW;
+    static constexpr int NSTEP = 64 / G;
+    static constexpr int SBV = NSTEP < (VEC >= 4 ? 4 : 8) ? NSTEP : (VEC >= 4 ? 4 : 8);
+    static constexpr int NSB = NSTEP / SBV;
+};
+
+// The gathered operands of one stage: the entry values and B's row pieces.
+template <int SBV, int VEC>
+struct Stage {
+    float vj[SBV];
+    float bv[SBV][VEC];
+};
+
+// The window walk shared by both VCS walks. Positions base + 64k + lane of
+// windows k < nwin hold W[k] (indices); `mark` holds the round's group-start
+// bytes at the same offsets and `gvt` the group values. Stages run as a
+// two-deep pipeline: the next stage's gathers are issued before the current
+// stage is consumed, so their latency overlaps the current stage's work.
+// consume(k, j0, stage) does the arithmetic of stage (k, j0). Returns the
+// group number (round-relative plus one) of the last window's last lane.
+// B rows are read at byte offset ix * w4 + coff4 from Bb (32-bit offsets:
+// every row index is below 2^24 and B is under 4 GiB).
+template <int LOG_WW, int VEC, int NWR, typename Consume>
+__device__ __forceinline__ int window_stream(const int (&W)[NWR], int nwin, int lane, int slot,
+                                              const unsigned char *mark, const float *gvt,
+                                              const char *Bb, uint32_t w4, uint32_t coff4,
+                                              Consume &&consume) {
+    using Gm = Geo<LOG_WW, VEC>;
+    using St = Stage<Gm::SBV, VEC>;
+    const int ns = nwin * Gm::NSB;
+    int carry = 0;  // group number reaching the next window's start
+    int wi = 0;     // the current window's indices
+    float vk = 0;   // and values
+    auto issue = [&](int q, St &st) {
+        const int k = q / Gm::NSB;
+        const int j0 = (q - k * Gm::NSB) * Gm::SBV;
+        if (j0 == 0) {
+            wi = W[k];
+            const int g = max(wave_max_scan((int)mark[64 * k + lane]), carry);
+            carry = readlane(g, 63);
+            vk = gvt[g - 1];
+        }
+#pragma unroll
+        for (int t = 0; t < Gm::SBV; ++t) {
+            const int src = (j0 + t) * Gm::G + slot;
+            const int ix = __shfl(wi, src);
+            st.vj[t] = __shfl(vk, src);
+            const uint32_t off = __umul24((uint32_t)ix, w4) + coff4;
+            load_vec<float, VEC>(reinterpret_cast<const float *>(Bb + off), st.bv[t]);
+        }
+    };
+    auto eat = [&](int q, const St &st) {
+        const int k = q / Gm::NSB;
+        consume(k, (q - k * Gm::NSB) * Gm::SBV, st);
+    };
+    if (ns <= 0) return carry;
+    St a, b;
+    issue(0, a);
+    for (int q = 0;;) {
+        if (q + 1 < ns) issue(q + 1, b);
+        eat(q, a);
+        if (++q >= ns) break;
+        if (q + 1 < ns) issue(q + 1, a);
+        eat(q, b);
+        if (++q >= ns) break;
+    }
+    return carry;
+}
+
+// Writes the round's (or pass's) group marks and value table: group numbers
+// are round-relative plus one. Non-empty groups starting in [base, pe) mark
+// their first position (relative to base); with mark_first, group 0 holds
+// position base (it may start before it) and marks position 0.
+template <int GWR>
+__device__ __forceinline__ void write_marks(const int (&GS)[GWR], const float (&GV)[GWR],
+                                            int n_grp, int base, int pe, bool mark_first,
+                                            int lane, unsigned char *mark, float *gvt) {
+    reinterpret_cast<uint4 *>(mark)[lane] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < GWR; ++j) {
+        gvt[64 * j + lane] = GV[j];
+        int nxt = __shfl_down(GS[j], 1);
+        if (j + 1 < GWR) {
+            const int first_next = readlane(GS[j + 1 < GWR ? j + 1 : j], 0);
+            nxt = lane == 63 ? first_next : nxt;
+        }
+        const int li = 64 * j + lane;
+        // group 0 may start before base; an empty group 0 (base at its
+        // slice's end) holds nothing, and the group starting at base marks it
+        if (mark_first && li == 0) {
+            if (nxt > GS[j]) mark[0] = 1;
+        } else if (li < n_grp && nxt > GS[j] && GS[j] < pe) {
+            mark[GS[j] - base] = (unsigned char)(li + 1);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Accumulates entries [P0, P1) of one VCS slice, whose groups are [ka, kb),
+// into acc: entry lane `slot` takes positions P0 + 64k + jG + slot in order.
+// The entries are walked in passes of up to 64 * kRowsNWR positions and
+// 64 * kRowsGWR - 1 groups with the per-wave LDS marks and value table of
+// k_vcs_rows. The group holding a pass's first position is found 64 group
+// starts at a time with a ballot. Indices are read non-temporally so the
+// stream does not push B's rows out of L2.
+template <int LOG_WW, int VEC>
+__device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int lane, int slot,
+                                          uint32_t coff4, const int *__restrict__ vptr,
+                                          const float *__restrict__ vals,
+                                          const int *__restrict__ idx, const char *Bb,
+                                          uint32_t w4, unsigned char *mark, float *gvt,
+                                          float (&acc)[VEC]) {
+    using Gm = Geo<LOG_WW, VEC>;
+    constexpr int NWR = kRowsNWR;
+    constexpr int GWR = kRowsGWR;
+    int kf = ka;  // the group holding position P0
+    while (P0 < P1) {
+        for (;;) {  // count the groups after kf that start at or before P0
+            const int k = kf + 1 + lane;
+            const int gs = vptr[min(k, kb)];
+            const int n = __popcll(__ballot(k < kb && gs <= P0));
+            kf += n;
+            if (n < 64) break;
+        }
+        int PE = min(P1, P0 + 64 * NWR);
+        if (kb - kf > 64 * GWR - 1) PE = min(PE, vptr[kf + 64 * GWR - 1]);
+        int W[NWR], GS[GWR];
+        float GV[GWR];
+#pragma unroll
+        for (int k = 0; k < NWR; ++k) {
+            if (P0 + 64 * k < PE) W[k] = __builtin_nontemporal_load(idx + min(P0 + 64 * k + lane, PE - 1));
+        }
+#pragma unroll
+        for (int j = 0; j < GWR; ++j) {
+            GS[j] = vptr[min(kf + 64 * j + lane, kb)];
+            GV[j] = vals[min(kf + 64 * j + lane, kb - 1)];
+        }
+        write_marks<GWR>(GS, GV, min(kb - kf, 64 * GWR - 1), P0, PE, true, lane, mark, gvt);
+        const int nwin = (PE - P0 + 63) >> 6;
+        const int last_g = window_stream<LOG_WW, VEC, NWR>(
+            W, nwin, lane, slot, mark, gvt, Bb, w4, coff4,
+            [&](int k, int j0, const Stage<Gm::SBV, VEC> &st) {
+                const int step0 = P0 + 64 * k + j0 * Gm::G;
+                if (step0 + Gm::SBV * Gm::G <= PE) {
+#pragma unroll
+                    for (int t = 0; t < Gm::SBV; ++t) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < Gm::SBV; ++t) {
+                        if (step0 + t * Gm::G + slot < PE) {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e)
+                                acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
+                        }
+                    }
+                }
+            });
+        kf += last_g - 1;  // the group of the pass's last position
+        P0 = PE;
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Where a wave's walk stands: the next slice, and (mid) whether the walk is
+// inside that slice at entry p, whose group is kf.
+struct RowCursor {
+    int sa, p, kf;
+    bool mid;
+};
+
+// A round of k_vcs_rows: entries [E0, E1) and groups [K0, K1). nsl slices end
+// inside it; with open_end the slice after them continues past E1 (a slice
+// too large for one round is walked as a run of such rounds, its sum carried
+// over). With mid, the round starts inside slice sa at E0, and group K0 holds
+// E0. hp / he: lanes hold the first group / first entry of slice sa + lane.
+struct RowRound {
+    int sa, nsl, E0, E1, K0, K1, hp, he;
+    bool open_end, mid;
+};
+
+template <int NWR, int GWR>
+__device__ __forceinline__ void rows_plan(RowRound &r, const RowCursor &c, int s_end,
+                                          int n_slices, int lane, const int *__restrict__ sptr,
+                                          const int *__restrict__ vptr) {
+    r.sa = c.sa;
+    r.mid = c.mid;
+    r.hp = sptr[min(c.sa + lane, n_slices)];
+    r.he = vptr[r.hp];
+    // the last group of slice sa starting at or before P0 (past empty groups)
+    auto seek = [&](int K0, int P0) {
+        const int kb = readlane(r.hp, 1);
+        for (;;) {
+            const int k = K0 + 1 + lane;
+            const int n = __popcll(__ballot(k < kb && vptr[min(k, kb)] <= P0));
+            K0 += n;
+            if (n < 64) return K0;
+        }
+    };
+    int P0, K0;
+    if (c.mid) {
+        P0 = c.p;
+        K0 = seek(c.kf, P0);
+    } else {
+        P0 = readlane(r.he, 0);
+        K0 = readlane(r.hp, 0);
+    }
+    const bool fits = (c.sa + lane <= s_end) && (r.he - P0 <= 64 * NWR) &&
+                      (r.hp - K0 <= 64 * GWR - 1);
+    const int last = __popcll(__ballot(fits)) - 1;  // fits is a prefix; lane 0 always fits
+    r.E0 = P0;
+    r.K0 = K0;
+    if (last >= 1) {
+        r.nsl = last;
+        r.open_end = false;
+        r.E1 = readlane(r.he, last);
+        r.K1 = readlane(r.hp, last);
+    } else {  // the next slice alone does not fit: take the part that does
+        if (!c.mid) r.K0 = K0 = seek(K0, P0);  // so that group K0 + 255 starts after P0
+        r.nsl = 0;
+        r.open_end = true;
+        const int kb = readlane(r.hp, 1);
+        int e1 = min(readlane(r.he, 1), P0 + 64 * NWR);
+        if (kb - K0 > 64 * GWR - 1) e1 = min(e1, vptr[K0 + 64 * GWR - 1]);
+        r.E1 = e1;
+        r.K1 = min(kb, K0 + 64 * GWR - 1);
+        if (e1 == readlane(r.he, 1)) {  // the rest of the slice fits after all
+            r.nsl = 1;                   // (groups past K1 are empty)
+            r.open_end = false;
+        }
+    }
+}
+
+// Loads a round's entry windows W[k] = idx[E0 + 64k + lane] (clamped to the
+// last entry) and group windows GS[j] = vptr[K0 + 64j + lane] (clamped to
+// K1), GV[j] = values[...] (clamped to K1 - 1).
+template <int NWR, int GWR>
+__device__ __forceinline__ void rows_load(const RowRound &r, int (&W)[NWR], int (&GS)[GWR],
+                                          float (&GV)[GWR], int lane,
+                                          const int *__restrict__ vptr,
+                                          const float *__restrict__ vals,
+                                          const int *__restrict__ idx) {
+#pragma unroll
+    for (int k = 0; k < NWR; ++k) {
+        if (r.E0 + 64 * k < r.E1) W[k] = idx[min(r.E0 + 64 * k + lane, r.E1 - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < GWR; ++j) {
+        if (r.K0 + 64 * j <= r.K1) {
+            GS[j] = vptr[min(r.K0 + 64 * j + lane, r.K1)];
+            GV[j] = vals[max(min(r.K0 + 64 * j + lane, r.K1 - 1), 0)];
+        }
+    }
+}
+
+// Short VCS slices: each wave walks a contiguous block of slices in rounds of
+// up to 64 * kRowsNWR entries and 64 * kRowsGWR - 1 groups (a longer slice
+// takes several rounds). With LDS_B the dense operand B (n_in x w) is first
+// copied into the CU's LDS (one 1024-thread block per CU) and gathered from
+// there. Dynamic LDS: [B, 16-byte aligned][per wave: kRowsWaveLds bytes of
+// marks and group values]. Width chunks wider than the wave's width lanes are
+// walked one after the other, each over the whole block of slices.
 template <int LOG_WW, bool LDS_B, int VEC>
 __global__ void __launch_bounds__(1024)
 k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
@@ -110,14 +380,11 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
            const float *__restrict__ B, float *__restrict__ out, int w, int n_in) {
     using T = float;
     using Sum = SlotSum<LOG_WW, VEC>;
+    using Gm = Geo<LOG_WW, VEC>;
     constexpr int NWR = kRowsNWR;
     constexpr int GWR = kRowsGWR;
     static_assert(NWR == 16, "one 16-byte mark word per lane");
     static_assert(64 * NWR + 256 * GWR == kRowsWaveLds, "per-wave LDS layout");
-    constexpr int G = 64 >> LOG_WW;
-    constexpr int NSTEP = 64 / G;  // steps per window
-    // steps per sub-batch: the gathers of one sub-batch are in flight together
-    constexpr int SBV = NSTEP < (VEC >= 4 ? 4 : 8) ? NSTEP : (VEC >= 4 ? 4 : 8);
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int waves = blockDim.x >> 6;
@@ -126,23 +393,24 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     const int chunk = VEC << LOG_WW;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const size_t b_bytes = LDS_B ? (((size_t)n_in * w * sizeof(T) + 15) & ~size_t(15)) : 0;
-    // per wave: [64*NWR mark bytes][64*GWR group values]
     unsigned char *mark = smem + b_bytes + (size_t)wave * kRowsWaveLds;
     T *gvt = reinterpret_cast<T *>(mark + 64 * NWR);
     const long long tw = (long long)gridDim.x * waves;
     const long long gw = (long long)blockIdx.x * waves + wave;
     const int s_beg = (int)(gw * n_slices / tw);
     const int s_end = (int)((gw + 1) * n_slices / tw);
+    const uint32_t w4 = (uint32_t)w * 4u;
 
-    Round r;
+    RowRound r;
     int W[NWR], GS[GWR];
-    T V[NWR], GV[GWR];
+    T GV[GWR];
+    const RowCursor start{s_beg, 0, 0, false};
     if (s_beg < s_end) {
-        round_plan<true, NWR, GWR>(r, s_beg, s_end, n_slices, lane, sptr, vptr);
-        if (r.nsl > 0) round_load<true, T, NWR, GWR>(r, W, V, GS, GV, lane, vptr, vals, idx);
+        rows_plan<NWR, GWR>(r, start, s_end, n_slices, lane, sptr, vptr);
+        rows_load<NWR, GWR>(r, W, GS, GV, lane, vptr, vals, idx);
     }
 
-    const T *Bs = B;
+    const char *Bb = reinterpret_cast<const char *>(B);
     if constexpr (LDS_B) {
         T *lb = reinterpret_cast<T *>(smem);
         const size_t n_el = (size_t)n_in * w;
@@ -155,117 +423,145 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
             for (size_t k = threadIdx.x; k < n_el; k += blockDim.x) lb[k] = B[k];
         }
         __syncthreads();
-        Bs = lb;
+        Bb = reinterpret_cast<const char *>(lb);
     }
+    if (s_beg >= s_end) return;
 
-    int sa = s_beg;
-    while (sa < s_end) {
-        if (r.nsl < 0) {  // one slice larger than a round
-            big_slice<true, T, VEC, 4>(sa, lane, slot, cl, Split{LOG_WW, 6 - LOG_WW}, sptr, vptr,
-                                       vals, idx, Bs, out, w);
-            sa += 1;
-        } else {
-            // the round's group starts (bytes) and values (table)
-            reinterpret_cast<uint4 *>(mark)[lane] = make_uint4(0, 0, 0, 0);
-            const int n_grp = r.K1 - r.K0;
+    for (int c0 = 0; c0 < w; c0 += chunk) {
+        const int col = c0 + cl * VEC;
+        const bool act = col < w;
+        const uint32_t coff4 = act ? 4u * col : 0u;  // gathers stay inside B's rows
+        T acc[VEC];  // carried over the rounds of a slice
 #pragma unroll
-            for (int j = 0; j < GWR; ++j) {
-                gvt[64 * j + lane] = GV[j];
-                int nxt = __shfl_down(GS[j], 1);
-                if (j + 1 < GWR) {
-                    const int first_next = readlane(GS[j + 1 < GWR ? j + 1 : j], 0);
-                    nxt = lane == 63 ? first_next : nxt;
-                }
-                const int gidx = 64 * j + lane;
-                if (gidx < n_grp && nxt > GS[j]) mark[GS[j] - r.E0] = (unsigned char)(gidx + 1);
-            }
-            __builtin_amdgcn_wave_barrier();
+        for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+        if (c0 > 0) {
+            rows_plan<NWR, GWR>(r, start, s_end, n_slices, lane, sptr, vptr);
+            rows_load<NWR, GWR>(r, W, GS, GV, lane, vptr, vals, idx);
+        }
+        for (;;) {
+            write_marks<GWR>(GS, GV, r.K1 - r.K0, r.E0, r.E1, r.mid || r.open_end, lane, mark,
+                             gvt);
             const int nwin = (r.E1 - r.E0 + 63) >> 6;
-            for (int c0 = 0; c0 < w; c0 += chunk) {
-                const int col = c0 + cl * VEC;
-                const bool act = col < w;
-                const int coff = act ? col : 0;  // gathers stay inside B's rows
-                int i = 0;                       // slice of the round being accumulated
-                int e0 = r.E0;                   // its first entry
-                int e1 = readlane(r.he, 1);      // its end
-                int carry = 0;                   // group number reaching the window start
-                T acc[VEC];
+            int i = 0;        // slice of the round being accumulated
+            int e0 = r.E0;    // its first entry in the round
+            int e1 = r.nsl > 0 ? readlane(r.he, 1) : r.E1;  // its end (round end if open)
+
+            // sums slice i over the entry lanes, writes its row, moves on
+            auto close = [&]() {
+                T res[Sum::VO];
+                Sum::run(acc, res);
+                if (Sum::writer(lane) && act) {
+                    T *o = out + (size_t)(r.sa + i) * w + col + Sum::base(lane);
+                    store_vec<T, Sum::VO>(o, res);
+                }
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+                ++i;
+                e0 = e1;
+                e1 = i < r.nsl ? readlane(r.he, i + 1) : (r.open_end ? r.E1 : e1);
+            };
 
-                // sums slice i over the entry lanes, writes its row, moves on
-                auto close = [&]() {
-                    T res[Sum::VO];
-                    Sum::run(acc, res);
-                    if (Sum::writer(lane) && act) {
-                        T *o = out + (size_t)(r.sa + i) * w + col + Sum::base(lane);
-                        store_vec<T, Sum::VO>(o, res);
+            // empty slices before the first entry
+            while (i < r.nsl && e1 <= r.E0) close();
+            const int g_last = window_stream<LOG_WW, VEC, NWR>(
+                W, nwin, lane, slot, mark, gvt, Bb, w4, coff4,
+                [&](int k, int j0, const Stage<Gm::SBV, VEC> &st) {
+                    const int step0 = r.E0 + 64 * k + j0 * Gm::G;
+                    if (e1 >= step0 + Gm::SBV * Gm::G) {
+                        // every lane of the stage is in the current slice
+#pragma unroll
+                        for (int t = 0; t < Gm::SBV; ++t) {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e)
+                                acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
+                        }
+                        return;
                     }
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[e] = T(0);
-                    ++i;
-                    e0 = e1;
-                    if (i < r.nsl) e1 = readlane(r.he, i + 1);
-                };
-
-                // empty slices before the first entry
-                while (i < r.nsl && e1 <= r.E0) close();
-                for (int k = 0; k < nwin; ++k) {
-                    const int wbase = r.E0 + 64 * k;
-                    const int wi = W[k];
-                    const int g = max(wave_max_scan((int)mark[64 * k + lane]), carry);
-                    carry = readlane(g, 63);
-                    const T vk = gvt[g - 1];
-#pragma unroll 1
-                    for (int j0 = 0; j0 < NSTEP; j0 += SBV) {
-                        T vj[SBV];
-                        T bv[SBV][VEC];
-#pragma unroll
-                        for (int t = 0; t < SBV; ++t) {
-                            const int src = (j0 + t) * G + slot;
-                            const int ix = __shfl(wi, src);
-                            vj[t] = __shfl(vk, src);
-                            // LDS rows: n_in * w < 2^24 (a 24-bit multiply is full rate)
-                            const size_t at = LDS_B ? size_t(__umul24(ix, w) + coff)
-                                                    : size_t(ix) * size_t(w) + size_t(coff);
-                            load_vec<T, VEC>(Bs + at, bv[t]);
-                        }
-#pragma unroll
-                        for (int t = 0; t < SBV; ++t) {
-                            const int step_end = wbase + (j0 + t + 1) * G;
-                            if (i < r.nsl && e1 >= step_end) {
-                                // every lane of the step is in slice i
+                    for (int t = 0; t < Gm::SBV; ++t) {
+                        const int step_end = step0 + (t + 1) * Gm::G;
+                        const int pj = step_end - Gm::G + slot;
+                        // close every slice that ends inside this step
+                        while (i < r.nsl && e1 < step_end) {
+                            if (pj >= e0 && pj < e1) {
 #pragma unroll
                                 for (int e = 0; e < VEC; ++e)
-                                    acc[e] = fma_t(vj[t], bv[t][e], acc[e]);
-                            } else {
-                                const int pj = wbase + (j0 + t) * G + slot;
-                                while (i < r.nsl && e1 < step_end) {
-                                    if (pj >= e0 && pj < e1) {
-#pragma unroll
-                                        for (int e = 0; e < VEC; ++e)
-                                            acc[e] = fma_t(vj[t], bv[t][e], acc[e]);
-                                    }
-                                    close();
-                                }
-                                if (i < r.nsl && pj >= e0) {
-#pragma unroll
-                                    for (int e = 0; e < VEC; ++e)
-                                        acc[e] = fma_t(vj[t], bv[t][e], acc[e]);
-                                }
+                                    acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
                             }
+                            close();
+                        }
+                        if (pj >= e0 && pj < e1) {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e)
+                                acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
                         }
                     }
-                }
-                // slices ending at the round's last entry, and empty ones after
-                while (i < r.nsl) close();
-            }
-            sa += r.nsl;
+                });
+            // slices ending at the round's last entry, and empty ones after
+            while (i < r.nsl) close();
+            RowCursor nxt;
+            if (r.open_end) nxt = RowCursor{r.sa, r.E1, r.K0 + g_last - 1, true};
+            else nxt = RowCursor{r.sa + r.nsl, 0, 0, false};
             __builtin_amdgcn_wave_barrier();
+            if (nxt.sa >= s_end) break;
+            rows_plan<NWR, GWR>(r, nxt, s_end, n_slices, lane, sptr, vptr);
+            rows_load<NWR, GWR>(r, W, GS, GV, lane, vptr, vals, idx);
         }
-        if (sa < s_end) {
-            round_plan<true, NWR, GWR>(r, sa, s_end, n_slices, lane, sptr, vptr);
-            if (r.nsl > 0) round_load<true, T, NWR, GWR>(r, W, V, GS, GV, lane, vptr, vals, idx);
+    }
+}
+
+// Long VCS slices: a block of up to 8 waves walks one slice at a time
+// (grid-stride over slices). Wave k takes the k-th of `waves` contiguous pieces
+// of the slice's entries (vcs_piece); the waves' sums are added in wave order.
+// B stays in global memory (it is gathered through L2).
+template <int LOG_WW, int VEC>
+__global__ void __launch_bounds__(512)
+k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
+           const float *__restrict__ vals, const int *__restrict__ idx,
+           const float *__restrict__ B, float *__restrict__ out, int w) {
+    using T = float;
+    using Sum = SlotSum<LOG_WW, VEC>;
+    __shared__ T part[8][64 * VEC];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[8][kRowsWaveLds];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int waves = blockDim.x >> 6;
+    const int slot = lane >> LOG_WW;
+    const int cl = lane & ((1 << LOG_WW) - 1);
+    const int chunk = VEC << LOG_WW;
+    unsigned char *mark = lds[wave];
+    T *gvt = reinterpret_cast<T *>(lds[wave] + 64 * kRowsNWR);
+    const uint32_t w4 = (uint32_t)w * 4u;
+    const char *Bb = reinterpret_cast<const char *>(B);
+    for (int s = blockIdx.x; s < n_slices; s += gridDim.x) {
+        const int ka = sptr[s], kb = sptr[s + 1];
+        const int e0 = vptr[ka], e1 = vptr[kb];
+        const long long len = e1 - e0;
+        const int ps = e0 + (int)(len * wave / waves);
+        const int pe = e0 + (int)(len * (wave + 1) / waves);
+        for (int c0 = 0; c0 < w; c0 += chunk) {
+            const int col = c0 + cl * VEC;
+            const bool act = col < w;
+            T acc[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+            vcs_piece<LOG_WW, VEC>(ka, kb, ps, pe, lane, slot, act ? 4u * col : 0u, vptr, vals,
+                                   idx, Bb, w4, mark, gvt, acc);
+            T res[Sum::VO];
+            Sum::run(acc, res);
+            if (Sum::writer(lane)) {
+#pragma unroll
+                for (int e = 0; e < Sum::VO; ++e) part[wave][cl * VEC + Sum::base(lane) + e] = res[e];
+            }
+            __syncthreads();
+            for (int t = threadIdx.x; t < chunk; t += blockDim.x) {
+                if (c0 + t < w) {
+                    T tot = part[0][t];
+                    for (int k = 1; k < waves; ++k) tot += part[k][t];
+                    out[(size_t)s * w + c0 + t] = tot;
+                }
+            }
+            __syncthreads();
         }
     }
 }

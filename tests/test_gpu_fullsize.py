@@ -48,6 +48,40 @@ def stress_matrices():
     yield "tiny_rows", W.count_matrix(120_000, 300, 3.0, 64, rng)        # many slices per wave, empty rows
     yield "long_rows", W.count_matrix(400, 30_000, 3000.0, 255, rng)     # rows beyond one round, ~250 groups
     yield "many_groups", W.count_matrix(6_000, 4_000, 700.0, 255, rng)   # ~200 groups per row
+    yield "mixed_rows", mixed_rows(rng)
+
+
+def mixed_rows(rng):
+    """Short rows with a few planted long ones: rows of 1,500-2,900 entries
+    (several register rounds each), rows whose entries take ~600 distinct
+    values (more groups than one round holds), among Poisson(30) rows."""
+    t = W.count_matrix(20_000, 3_000, 30.0, 64, rng)
+    planted = rng.choice(20_000, size=12, replace=False)
+    keep = ~np.isin(t.rows, planted)
+    rows, cols, vals = [t.rows[keep]], [t.cols[keep]], [t.vals[keep]]
+    for k, r in enumerate(planted):
+        n = int(rng.integers(1_500, 2_900))
+        c = rng.choice(3_000, size=n, replace=False)
+        v = (rng.integers(1, 600, size=n) if k % 2 else W.count_values(rng, n, 64))
+        rows.append(np.full(n, r, dtype=t.rows.dtype))
+        cols.append(c.astype(t.cols.dtype))
+        vals.append(np.asarray(v, dtype=np.float32))
+    return W.Triplets(t.shape, np.concatenate(rows), np.concatenate(cols), np.concatenate(vals))
+
+
+def with_empty_groups(L, rng, n_rows=6, per_row=300):
+    """The same matrix with runs of empty groups (value_ptr[k] == value_ptr[k+1])
+    inserted at the start, middle and end of some slices: the product must not
+    change."""
+    mp, vals, vp = L.major_ptr.astype(np.int64), L.values.copy(), L.value_ptr.astype(np.int64)
+    for r in sorted(rng.choice(L.n_major, size=n_rows, replace=False), reverse=True):
+        g0, g1 = int(mp[r]), int(mp[r + 1])
+        at = [g0, (g0 + g1) // 2, g1][r % 3]
+        vals = np.insert(vals, at, np.float32(7.0) * np.ones(per_row, np.float32))
+        vp = np.insert(vp, at, np.full(per_row, vp[at]))
+        mp[r + 1:] += per_row
+    return W.Vcs(L.layout, L.shape, mp.astype(np.int32), vals.astype(np.float32),
+                 vp.astype(np.int32), L.indices)
 
 
 @pytest.fixture(scope="module")
@@ -55,13 +89,19 @@ def stress():
     out = {}
     for name, t in stress_matrices():
         out[name] = {"vcsr": W.build_vcs(t, "vcsr"), "vcsc": W.build_vcs(t, "vcsc")}
+    rng = W.rng_for(32)
+    out["empty_groups"] = {lay: with_empty_groups(out["mixed_rows"][lay], rng)
+                           for lay in ("vcsr", "vcsc")}
     return out
+
+
+STRESS = ["tiny_rows", "long_rows", "many_groups", "mixed_rows", "empty_groups"]
 
 
 @pytest.mark.parametrize("width", [1, 5, 16])
 @pytest.mark.parametrize("direction", ["AB", "BA"])
 @pytest.mark.parametrize("layout", ["vcsr", "vcsc"])
-@pytest.mark.parametrize("name", ["tiny_rows", "long_rows", "many_groups"])
+@pytest.mark.parametrize("name", STRESS)
 def test_stress_parity(orc, stress, name, layout, direction, width):
     dev = need_gpu()
     L = stress[name][layout]
@@ -74,7 +114,7 @@ def test_stress_parity(orc, stress, name, layout, direction, width):
     check_close(orc, L, direction, B, out, where=f"{name} {layout} {direction} w={width}")
 
 
-@pytest.mark.parametrize("name", ["tiny_rows", "long_rows", "many_groups"])
+@pytest.mark.parametrize("name", STRESS)
 def test_stress_integer_exact(orc, stress, name):
     dev = need_gpu()
     for layout in ("vcsr", "vcsc"):
