@@ -26,6 +26,7 @@ struct Plan {
     size_t lds_bytes = 0;
     int grid = 0;
     int block = 256;
+    int wps = 8;         // k_vcs_long: waves per slice
 };
 
 constexpr size_t kLdsMax = 160 * 1024;  // LDS per CU on gfx950

@@ -12,7 +12,7 @@
 #include <new>
 #include <unordered_map>
 
-#include "../../include/vspmm.h"
+#include "vspmm.h"
 #include "launch.hpp"
 #include "schedule.hpp"
 
@@ -154,7 +154,19 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
         if (mean >= kLongMean) {
             pl.kind = kLong;
             pl.block = 512;
-            pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(n_slices, int64_t(n_cu) * 16)));
+            if (vcs) {
+                // k_vcs_long: waves per slice so that the grid's waves fill the
+                // chip (16 per CU) about once
+                const int64_t target = int64_t(std::max(n_cu, 1)) * 16;
+                int wps = 1;
+                while (wps < 8 && n_slices * wps * 2 <= target) wps *= 2;
+                pl.wps = wps;
+                const int64_t spb = 8 / wps;
+                const int64_t blocks = (n_slices + spb - 1) / spb;
+                pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(blocks, int64_t(n_cu) * 8)));
+            } else {
+                pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(n_slices, int64_t(n_cu) * 16)));
+            }
             return pl;
         }
         pl.kind = kShort;

@@ -226,6 +226,14 @@ __device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int la
     constexpr int GWR = kRowsGWR;
     int kf = ka;  // the group holding position P0
     while (P0 < P1) {
+        // the pass's indices do not depend on its groups: issue them first
+        int PE = min(P1, P0 + 64 * NWR);
+        int W[NWR], GS[GWR];
+        float GV[GWR];
+#pragma unroll
+        for (int k = 0; k < NWR; ++k) {
+            if (P0 + 64 * k < PE) W[k] = __builtin_nontemporal_load(idx + min(P0 + 64 * k + lane, PE - 1));
+        }
         for (;;) {  // count the groups after kf that start at or before P0
             const int k = kf + 1 + lane;
             const int gs = vptr[min(k, kb)];
@@ -233,14 +241,8 @@ __device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int la
             kf += n;
             if (n < 64) break;
         }
-        int PE = min(P1, P0 + 64 * NWR);
+        // at most 64 * GWR - 1 groups per pass (the windows loaded past PE are not used)
         if (kb - kf > 64 * GWR - 1) PE = min(PE, vptr[kf + 64 * GWR - 1]);
-        int W[NWR], GS[GWR];
-        float GV[GWR];
-#pragma unroll
-        for (int k = 0; k < NWR; ++k) {
-            if (P0 + 64 * k < PE) W[k] = __builtin_nontemporal_load(idx + min(P0 + 64 * k + lane, PE - 1));
-        }
 #pragma unroll
         for (int j = 0; j < GWR; ++j) {
             GS[j] = vptr[min(kf + 64 * j + lane, kb)];
@@ -510,15 +512,18 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     }
 }
 
-// Long VCS slices: a block of up to 8 waves walks one slice at a time
-// (grid-stride over slices). Wave k takes the k-th of `waves` contiguous pieces
-// of the slice's entries (vcs_piece); the waves' sums are added in wave order.
-// B stays in global memory (it is gathered through L2).
+// Long VCS slices: each slice is walked by `wps` waves (1, 2, 4 or 8) of a
+// block of 8 waves, so a block takes 8 / wps slices at a time (grid-stride
+// over slice groups). Wave k of a slice takes the k-th of wps contiguous
+// pieces of its entries (vcs_piece); the pieces' sums are added in wave order.
+// The host picks wps so the grid's waves fill the chip about once: each wave
+// then pays its chain of dependent header loads once. B stays in global
+// memory (it is gathered through L2).
 template <int LOG_WW, int VEC>
 __global__ void __launch_bounds__(512)
 k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
            const float *__restrict__ vals, const int *__restrict__ idx,
-           const float *__restrict__ B, float *__restrict__ out, int w) {
+           const float *__restrict__ B, float *__restrict__ out, int w, int wps) {
     using T = float;
     using Sum = SlotSum<LOG_WW, VEC>;
     __shared__ T part[8][64 * VEC];
@@ -526,6 +531,9 @@ k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
+    const int spb = waves / wps;     // slices per block
+    const int sub = wave / wps;      // this wave's slice within the block
+    const int piece = wave - sub * wps;
     const int slot = lane >> LOG_WW;
     const int cl = lane & ((1 << LOG_WW) - 1);
     const int chunk = VEC << LOG_WW;
@@ -533,20 +541,27 @@ k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     T *gvt = reinterpret_cast<T *>(lds[wave] + 64 * kRowsNWR);
     const uint32_t w4 = (uint32_t)w * 4u;
     const char *Bb = reinterpret_cast<const char *>(B);
-    for (int s = blockIdx.x; s < n_slices; s += gridDim.x) {
-        const int ka = sptr[s], kb = sptr[s + 1];
-        const int e0 = vptr[ka], e1 = vptr[kb];
-        const long long len = e1 - e0;
-        const int ps = e0 + (int)(len * wave / waves);
-        const int pe = e0 + (int)(len * (wave + 1) / waves);
+    for (int s0 = blockIdx.x * spb; s0 < n_slices; s0 += gridDim.x * spb) {
+        const int s = s0 + sub;  // wave-uniform
+        const bool live = s < n_slices;
+        int ka = 0, kb = 0, ps = 0, pe = 0;
+        if (live) {
+            ka = sptr[s];
+            kb = sptr[s + 1];
+            const int e0 = vptr[ka], e1 = vptr[kb];
+            const long long len = e1 - e0;
+            ps = e0 + (int)(len * piece / wps);
+            pe = e0 + (int)(len * (piece + 1) / wps);
+        }
         for (int c0 = 0; c0 < w; c0 += chunk) {
             const int col = c0 + cl * VEC;
             const bool act = col < w;
             T acc[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = T(0);
-            vcs_piece<LOG_WW, VEC>(ka, kb, ps, pe, lane, slot, act ? 4u * col : 0u, vptr, vals,
-                                   idx, Bb, w4, mark, gvt, acc);
+            if (live)
+                vcs_piece<LOG_WW, VEC>(ka, kb, ps, pe, lane, slot, act ? 4u * col : 0u, vptr,
+                                       vals, idx, Bb, w4, mark, gvt, acc);
             T res[Sum::VO];
             Sum::run(acc, res);
             if (Sum::writer(lane)) {
@@ -554,11 +569,12 @@ k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
                 for (int e = 0; e < Sum::VO; ++e) part[wave][cl * VEC + Sum::base(lane) + e] = res[e];
             }
             __syncthreads();
-            for (int t = threadIdx.x; t < chunk; t += blockDim.x) {
-                if (c0 + t < w) {
-                    T tot = part[0][t];
-                    for (int k = 1; k < waves; ++k) tot += part[k][t];
-                    out[(size_t)s * w + c0 + t] = tot;
+            for (int t = threadIdx.x; t < spb * chunk; t += blockDim.x) {
+                const int ss = t / chunk, c = t - ss * chunk;
+                if (s0 + ss < n_slices && c0 + c < w) {
+                    T tot = part[ss * wps][c];
+                    for (int k = 1; k < wps; ++k) tot += part[ss * wps + k][c];
+                    out[(size_t)(s0 + ss) * w + c0 + c] = tot;
                 }
             }
             __syncthreads();

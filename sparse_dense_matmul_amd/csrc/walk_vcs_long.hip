@@ -14,7 +14,7 @@ void launch_vcs_long(const Plan &pl, const WalkArgs<float> &a, hipStream_t s) {
     const dim3 g(pl.grid), b(pl.block);
 #define VSPMM_VLONG(LW)                                                                          \
     hipLaunchKernelGGL((k_vcs_long<LW, VEC>), g, b, 0, s, a.n_slices, a.sptr, a.vptr, a.vals,    \
-                       a.idx, a.B, a.out, a.w)
+                       a.idx, a.B, a.out, a.w, pl.wps)
     switch (pl.sp.log_ww) {
         case 0: VSPMM_VLONG(0); break;
         case 1: VSPMM_VLONG(1); break;
