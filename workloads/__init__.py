@@ -293,6 +293,65 @@ def config5(seed_salt: int = 0) -> Triplets:
     return count_matrix(1_000_000, 20_000, 200.0, 255, rng_for(5, seed_salt))
 
 
+def _vcsr_chunk(job):
+    """One chunk of count_vcsr_chunked (a process-pool task)."""
+    seed, rows_n, n, lam, cap = job
+    rng = np.random.Generator(np.random.PCG64(seed))
+    counts = rng.poisson(lam, size=rows_n)
+    rows, cols = sample_columns(rng, counts, n)
+    vals = count_values(rng, rows.size, cap)
+    # canonical order inside the chunk: row, value, column (one int64 key)
+    key = (rows * (cap + 1) + vals.astype(np.int64)) * n + cols
+    order = np.argsort(key, kind="stable")
+    rows, cols, vals = rows[order], cols[order], vals[order]
+    start = np.ones(rows.size, dtype=bool)
+    start[1:] = (rows[1:] != rows[:-1]) | (vals[1:] != vals[:-1])
+    gstart = np.flatnonzero(start)
+    groups_per_row = np.bincount(rows[gstart], minlength=rows_n)
+    return (vals[gstart].astype(np.float32), gstart.astype(np.int64), cols.astype(np.int32),
+            groups_per_row)
+
+
+def count_vcsr_chunked(m: int, n: int, lam: float, cap: int, seed: list, chunk: int = 50_000,
+                       workers: int = 1, log=None) -> Vcs:
+    """Canonical VCSR of a count matrix built ``chunk`` rows at a time: per row
+    Poisson(lam) distinct uniform columns (``sample_columns``) and
+    ``min(1 + Geometric(0.3), cap)`` values, grouped by value (ascending value,
+    then ascending column). Chunk c draws from its own stream
+    PCG64(seed + [c]), so chunks can be built in parallel (``workers``
+    processes) with the same result."""
+    jobs = [(list(seed) + [c], min(chunk, m - r0), n, lam, cap)
+            for c, r0 in enumerate(range(0, m, chunk))]
+    if workers > 1:
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        with cf.ProcessPoolExecutor(max_workers=workers,
+                                    mp_context=mp.get_context("fork")) as pool:
+            parts = list(pool.map(_vcsr_chunk, jobs))
+    else:
+        parts = [_vcsr_chunk(j) for j in jobs]
+    major_ptr = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(np.concatenate([p[3] for p in parts]), out=major_ptr[1:])
+    e_off, value_ptr = 0, []
+    for vals, gstart, cols, _ in parts:
+        value_ptr.append(gstart + e_off)
+        e_off += cols.size
+    value_ptr.append(np.array([e_off], dtype=np.int64))
+    if log:
+        log(f"{m} rows, {e_off} entries")
+    return Vcs("vcsr", (m, n), major_ptr.astype(np.int32),
+               np.concatenate([p[0] for p in parts]),
+               np.concatenate(value_ptr).astype(np.int32),
+               np.concatenate([p[2] for p in parts]))
+
+
+def config5_vcsr(seed_salt: int = 0, workers: int = 1, log=None) -> Vcs:
+    """The 1,000,000 x 20,000 count matrix (~200M entries, values capped at
+    255) as a canonical VCSR, built in chunks of 50,000 rows."""
+    return count_vcsr_chunked(1_000_000, 20_000, 200.0, 255, [SEED_BASE + 5, seed_salt],
+                              workers=workers, log=log)
+
+
 def tiny_count(m: int, n: int, density: float, cap: int, rng: np.random.Generator) -> Triplets:
     """Small count matrix for brute-force checks (Bernoulli(density) pattern)."""
     mask = rng.random((m, n)) < density
