@@ -31,11 +31,22 @@ struct Plan {
 
 constexpr size_t kLdsMax = 160 * 1024;  // LDS per CU on gfx950
 constexpr int kRing = 128;              // k_short: ring positions per wave (two windows)
-// k_vcs_rows: entry windows and group windows per round, and the per-wave LDS
-// they need (a mark byte per round position, a float per round group)
-constexpr int kRowsNWR = 16;
-constexpr int kRowsGWR = 4;
+// k_vcs_rows: entry windows and group windows per round (two rounds are held
+// in registers at once), and the per-wave LDS they need (a mark byte per round
+// position, a float per round group)
+constexpr int kRowsNWR = 8;
+constexpr int kRowsGWR = 2;
 constexpr int kRowsWaveLds = 64 * kRowsNWR + 256 * kRowsGWR;
+// k_vcs_rows: slices per unit of work, and the block's slice-header table
+// (entries per array: the block's slice count plus the end pointer, rounded)
+constexpr int kRowsChunk = 4;
+__host__ __device__ inline int rows_header_cap(int n_slices, int n_blocks) {
+    return ((n_slices + n_blocks - 1) / n_blocks + 2 + 3) & ~3;
+}
+// k_vcs_long: the same per pass of a slice piece
+constexpr int kPieceNWR = 16;
+constexpr int kPieceGWR = 4;
+constexpr int kPieceWaveLds = 64 * kPieceNWR + 256 * kPieceGWR;
 
 // The operands of one aligned walk (slices of the walked layout = rows of out).
 template <typename T>

@@ -175,15 +175,23 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
         // values (VCS)
         const size_t ring = vcs ? size_t(kRowsWaveLds) : size_t(kRing) * (elt == 8 ? 16 : 8);
         const size_t b_al = (b_bytes + 15) & ~size_t(15);
-        if (b_bytes > 0 && b_al + 16 * ring <= kLdsMax && aligned(B, 16)) {
+        // VCS: the block's slice-header table (two int arrays) and a counter
+        auto extra = [&](int64_t grid) -> size_t {
+            if (!vcs) return 0;
+            return size_t(8) * size_t(rows_header_cap(int(n_slices), int(grid))) + 16;
+        };
+        const int64_t g1 = std::max(n_cu, 1);
+        if (b_bytes > 0 && b_al + 16 * ring + extra(g1) <= kLdsMax && aligned(B, 16)) {
             pl.lds = true;
-            pl.lds_bytes = b_al + 16 * ring;
+            pl.lds_bytes = b_al + 16 * ring + extra(g1);
             pl.block = 1024;
-            pl.grid = std::max(n_cu, 1);
+            pl.grid = int(g1);
         } else {
-            pl.lds_bytes = 4 * ring;
+            // enough blocks that a block's header table stays small
+            const int64_t g4 = std::max<int64_t>(g1 * 4, vcs ? (n_slices + 2047) / 2048 : 0);
+            pl.lds_bytes = 4 * ring + extra(g4);
             pl.block = 256;
-            pl.grid = std::max(n_cu, 1) * 4;
+            pl.grid = int(g4);
         }
         return pl;
     }

@@ -130,7 +130,7 @@ struct Stage {
 // group number (round-relative plus one) of the last window's last lane.
 // B rows are read at byte offset ix * w4 + coff4 from Bb (32-bit offsets:
 // every row index is below 2^24 and B is under 4 GiB).
-template <int LOG_WW, int VEC, int NWR, typename Consume>
+template <int LOG_WW, int VEC, int NWR, bool ROTATE, typename Consume>
 __device__ __forceinline__ int window_stream(const int (&W)[NWR], int nwin, int lane, int slot,
                                               const unsigned char *mark, const float *gvt,
                                               const char *Bb, uint32_t w4, uint32_t coff4,
@@ -141,11 +141,24 @@ __device__ __forceinline__ int window_stream(const int (&W)[NWR], int nwin, int 
     int carry = 0;  // group number reaching the next window's start
     int wi = 0;     // the current window's indices
     float vk = 0;   // and values
+    // ROTATE: the windows still to come move down one register per window
+    // (short arrays are otherwise indexed through a select chain per window)
+    int Wq[ROTATE ? NWR : 1];
+    if constexpr (ROTATE) {
+#pragma unroll
+        for (int k = 0; k < NWR; ++k) Wq[k] = W[k];
+    }
     auto issue = [&](int q, St &st) {
         const int k = q / Gm::NSB;
         const int j0 = (q - k * Gm::NSB) * Gm::SBV;
         if (j0 == 0) {
-            wi = W[k];
+            if constexpr (ROTATE) {
+                wi = Wq[0];
+#pragma unroll
+                for (int m = 0; m + 1 < NWR; ++m) Wq[m] = Wq[m + 1];
+            } else {
+                wi = W[k];
+            }
             const int g = max(wave_max_scan((int)mark[64 * k + lane]), carry);
             carry = readlane(g, 63);
             vk = gvt[g - 1];
@@ -181,11 +194,13 @@ __device__ __forceinline__ int window_stream(const int (&W)[NWR], int nwin, int 
 // are round-relative plus one. Non-empty groups starting in [base, pe) mark
 // their first position (relative to base); with mark_first, group 0 holds
 // position base (it may start before it) and marks position 0.
-template <int GWR>
+template <int NWR, int GWR>
 __device__ __forceinline__ void write_marks(const int (&GS)[GWR], const float (&GV)[GWR],
                                             int n_grp, int base, int pe, bool mark_first,
                                             int lane, unsigned char *mark, float *gvt) {
-    reinterpret_cast<uint4 *>(mark)[lane] = make_uint4(0, 0, 0, 0);
+    static_assert(NWR == 8 || NWR == 16, "a mark row of 512 or 1024 bytes");
+    if constexpr (NWR == 16) reinterpret_cast<uint4 *>(mark)[lane] = make_uint4(0, 0, 0, 0);
+    else reinterpret_cast<uint2 *>(mark)[lane] = make_uint2(0, 0);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < GWR; ++j) {
@@ -209,11 +224,11 @@ __device__ __forceinline__ void write_marks(const int (&GS)[GWR], const float (&
 
 // Accumulates entries [P0, P1) of one VCS slice, whose groups are [ka, kb),
 // into acc: entry lane `slot` takes positions P0 + 64k + jG + slot in order.
-// The entries are walked in passes of up to 64 * kRowsNWR positions and
-// 64 * kRowsGWR - 1 groups with the per-wave LDS marks and value table of
-// k_vcs_rows. The group holding a pass's first position is found 64 group
-// starts at a time with a ballot. Indices are read non-temporally so the
-// stream does not push B's rows out of L2.
+// The entries are walked in passes of up to 64 * kPieceNWR positions and
+// 64 * kPieceGWR - 1 groups with per-wave LDS marks and a value table. The
+// group holding a pass's first position is found 64 group starts at a time
+// with a ballot. Indices are read non-temporally so the stream does not push
+// B's rows out of L2.
 template <int LOG_WW, int VEC>
 __device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int lane, int slot,
                                           uint32_t coff4, const int *__restrict__ vptr,
@@ -222,8 +237,8 @@ __device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int la
                                           uint32_t w4, unsigned char *mark, float *gvt,
                                           float (&acc)[VEC]) {
     using Gm = Geo<LOG_WW, VEC>;
-    constexpr int NWR = kRowsNWR;
-    constexpr int GWR = kRowsGWR;
+    constexpr int NWR = kPieceNWR;
+    constexpr int GWR = kPieceGWR;
     int kf = ka;  // the group holding position P0
     while (P0 < P1) {
         // the pass's indices do not depend on its groups: issue them first
@@ -248,9 +263,9 @@ __device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int la
             GS[j] = vptr[min(kf + 64 * j + lane, kb)];
             GV[j] = vals[min(kf + 64 * j + lane, kb - 1)];
         }
-        write_marks<GWR>(GS, GV, min(kb - kf, 64 * GWR - 1), P0, PE, true, lane, mark, gvt);
+        write_marks<NWR, GWR>(GS, GV, min(kb - kf, 64 * GWR - 1), P0, PE, true, lane, mark, gvt);
         const int nwin = (PE - P0 + 63) >> 6;
-        const int last_g = window_stream<LOG_WW, VEC, NWR>(
+        const int last_g = window_stream<LOG_WW, VEC, NWR, false>(
             W, nwin, lane, slot, mark, gvt, Bb, w4, coff4,
             [&](int k, int j0, const Stage<Gm::SBV, VEC> &st) {
                 const int step0 = P0 + 64 * k + j0 * Gm::G;
@@ -278,7 +293,7 @@ __device__ __forceinline__ void vcs_piece(int ka, int kb, int P0, int P1, int la
 }
 
 // Where a wave's walk stands: the next slice, and (mid) whether the walk is
-// inside that slice at entry p, whose group is kf.
+// inside that slice at entry p, whose group is at or after kf.
 struct RowCursor {
     int sa, p, kf;
     bool mid;
@@ -288,20 +303,40 @@ struct RowCursor {
 // inside it; with open_end the slice after them continues past E1 (a slice
 // too large for one round is walked as a run of such rounds, its sum carried
 // over). With mid, the round starts inside slice sa at E0, and group K0 holds
-// E0. hp / he: lanes hold the first group / first entry of slice sa + lane.
+// E0. hp / he: lanes hold the first group / first entry of slice sa + lane
+// (lanes below nhl hold headers).
 struct RowRound {
-    int sa, nsl, E0, E1, K0, K1, hp, he;
+    int sa, nsl, E0, E1, K0, K1, hp, he, nhl;
     bool open_end, mid;
 };
 
+// Loads the headers of slices sa .. sa + 63 into the lanes.
+__device__ __forceinline__ void rows_headers(RowRound &r, int sa, int n_slices, int lane,
+                                             const int *__restrict__ sptr,
+                                             const int *__restrict__ vptr) {
+    r.hp = sptr[min(sa + lane, n_slices)];
+    r.he = vptr[r.hp];
+    r.nhl = 64;
+}
+
+// The same from the block's header table in LDS (slice bb + t in entry t,
+// entries up to be - bb).
+__device__ __forceinline__ void rows_headers_lds(RowRound &r, int sa, int bb, int be, int lane,
+                                                 const int *hp_l, const int *he_l) {
+    const int t = min(sa - bb + lane, be - bb);
+    r.hp = hp_l[t];
+    r.he = he_l[t];
+    r.nhl = 64;
+}
+
+// Plans the round that starts at cursor c from the headers in r (slice c.sa in
+// lane 0): the longest run of whole slices that fits (at least one), or, when
+// the first slice alone does not fit, the part of it that does.
 template <int NWR, int GWR>
-__device__ __forceinline__ void rows_plan(RowRound &r, const RowCursor &c, int s_end,
-                                          int n_slices, int lane, const int *__restrict__ sptr,
-                                          const int *__restrict__ vptr) {
+__device__ __forceinline__ void rows_fit(RowRound &r, const RowCursor &c, int s_end, int lane,
+                                         const int *__restrict__ vptr) {
     r.sa = c.sa;
     r.mid = c.mid;
-    r.hp = sptr[min(c.sa + lane, n_slices)];
-    r.he = vptr[r.hp];
     // the last group of slice sa starting at or before P0 (past empty groups)
     auto seek = [&](int K0, int P0) {
         const int kb = readlane(r.hp, 1);
@@ -320,7 +355,7 @@ __device__ __forceinline__ void rows_plan(RowRound &r, const RowCursor &c, int s
         P0 = readlane(r.he, 0);
         K0 = readlane(r.hp, 0);
     }
-    const bool fits = (c.sa + lane <= s_end) && (r.he - P0 <= 64 * NWR) &&
+    const bool fits = lane < r.nhl && (c.sa + lane <= s_end) && (r.he - P0 <= 64 * NWR) &&
                       (r.hp - K0 <= 64 * GWR - 1);
     const int last = __popcll(__ballot(fits)) - 1;  // fits is a prefix; lane 0 always fits
     r.E0 = P0;
@@ -331,7 +366,7 @@ __device__ __forceinline__ void rows_plan(RowRound &r, const RowCursor &c, int s
         r.E1 = readlane(r.he, last);
         r.K1 = readlane(r.hp, last);
     } else {  // the next slice alone does not fit: take the part that does
-        if (!c.mid) r.K0 = K0 = seek(K0, P0);  // so that group K0 + 255 starts after P0
+        if (!c.mid) r.K0 = K0 = seek(K0, P0);  // so that group K0 + 64 GWR - 1 starts after P0
         r.nsl = 0;
         r.open_end = true;
         const int kb = readlane(r.hp, 1);
@@ -346,9 +381,9 @@ __device__ __forceinline__ void rows_plan(RowRound &r, const RowCursor &c, int s
     }
 }
 
-// Loads a round's entry windows W[k] = idx[E0 + 64k + lane] (clamped to the
-// last entry) and group windows GS[j] = vptr[K0 + 64j + lane] (clamped to
-// K1), GV[j] = values[...] (clamped to K1 - 1).
+// Loads a round's entry windows W[k] = idx[E0 + 64k + lane] and group windows
+// GS[j] = vptr[K0 + 64j + lane], GV[j] = values[K0 + 64j + lane], every one
+// of them (clamped to the round), so the number of loads in flight is fixed.
 template <int NWR, int GWR>
 __device__ __forceinline__ void rows_load(const RowRound &r, int (&W)[NWR], int (&GS)[GWR],
                                           float (&GV)[GWR], int lane,
@@ -356,25 +391,27 @@ __device__ __forceinline__ void rows_load(const RowRound &r, int (&W)[NWR], int 
                                           const float *__restrict__ vals,
                                           const int *__restrict__ idx) {
 #pragma unroll
-    for (int k = 0; k < NWR; ++k) {
-        if (r.E0 + 64 * k < r.E1) W[k] = idx[min(r.E0 + 64 * k + lane, r.E1 - 1)];
-    }
+    for (int k = 0; k < NWR; ++k) W[k] = idx[max(min(r.E0 + 64 * k + lane, r.E1 - 1), 0)];
 #pragma unroll
     for (int j = 0; j < GWR; ++j) {
-        if (r.K0 + 64 * j <= r.K1) {
-            GS[j] = vptr[min(r.K0 + 64 * j + lane, r.K1)];
-            GV[j] = vals[max(min(r.K0 + 64 * j + lane, r.K1 - 1), 0)];
-        }
+        GS[j] = vptr[min(r.K0 + 64 * j + lane, r.K1)];
+        GV[j] = vals[max(min(r.K0 + 64 * j + lane, r.K1 - 1), 0)];
     }
 }
 
-// Short VCS slices: each wave walks a contiguous block of slices in rounds of
-// up to 64 * kRowsNWR entries and 64 * kRowsGWR - 1 groups (a longer slice
-// takes several rounds). With LDS_B the dense operand B (n_in x w) is first
-// copied into the CU's LDS (one 1024-thread block per CU) and gathered from
-// there. Dynamic LDS: [B, 16-byte aligned][per wave: kRowsWaveLds bytes of
-// marks and group values]. Width chunks wider than the wave's width lanes are
-// walked one after the other, each over the whole block of slices.
+// Short VCS slices. A block (one per CU with LDS_B) takes a contiguous range
+// of slices, cut into chunks of kRowsChunk slices; a (width pass, chunk) pair
+// is a unit of work. Each wave starts with unit `wave` and then claims the
+// next free unit from a counter in LDS, so waves that the CU serves faster
+// take more units. A unit is walked in rounds of up to 64 * kRowsNWR entries
+// and 64 * kRowsGWR - 1 groups that start at the chunk's first slice (a
+// longer slice takes several rounds), so a slice's arithmetic does not depend
+// on which wave walks it. Two rounds are held in registers: while one is
+// walked, the next one's windows are in flight, planned from the block's
+// slice headers in LDS. With LDS_B the dense operand B (n_in x w) is copied
+// into the CU's LDS first and gathered from there. Dynamic LDS: [B, 16-byte
+// aligned][per wave: kRowsWaveLds bytes of marks and group values][header
+// table: 2 x hcap ints][unit counter].
 template <int LOG_WW, bool LDS_B, int VEC>
 __global__ void __launch_bounds__(1024)
 k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
@@ -385,129 +422,212 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     using Gm = Geo<LOG_WW, VEC>;
     constexpr int NWR = kRowsNWR;
     constexpr int GWR = kRowsGWR;
-    static_assert(NWR == 16, "one 16-byte mark word per lane");
+    constexpr int CH = kRowsChunk;
     static_assert(64 * NWR + 256 * GWR == kRowsWaveLds, "per-wave LDS layout");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int waves = blockDim.x >> 6;
     const int slot = lane >> LOG_WW;
     const int cl = lane & ((1 << LOG_WW) - 1);
-    const int chunk = VEC << LOG_WW;
+    const int chunk_w = VEC << LOG_WW;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const size_t b_bytes = LDS_B ? (((size_t)n_in * w * sizeof(T) + 15) & ~size_t(15)) : 0;
     unsigned char *mark = smem + b_bytes + (size_t)wave * kRowsWaveLds;
     T *gvt = reinterpret_cast<T *>(mark + 64 * NWR);
-    const long long tw = (long long)gridDim.x * waves;
-    const long long gw = (long long)blockIdx.x * waves + wave;
-    const int s_beg = (int)(gw * n_slices / tw);
-    const int s_end = (int)((gw + 1) * n_slices / tw);
+    const int hcap = rows_header_cap(n_slices, gridDim.x);
+    int *hp_l = reinterpret_cast<int *>(smem + b_bytes + (size_t)waves * kRowsWaveLds);
+    int *he_l = hp_l + hcap;
+    int *unit_ctr = he_l + hcap;
+    const int bb = (int)((long long)blockIdx.x * n_slices / gridDim.x);
+    const int be = (int)((long long)(blockIdx.x + 1) * n_slices / gridDim.x);
+    const int nch = (be - bb + CH - 1) / CH;
+    const int npass = (w + chunk_w - 1) / chunk_w;
+    const int nunits = nch * npass;
     const uint32_t w4 = (uint32_t)w * 4u;
 
+    // B into LDS first, as direct global->LDS copies (16 bytes per lane, 1 KB
+    // per wave instruction; no registers).
+    const size_t b_el = (size_t)n_in * w;
+    const bool b_dma = LDS_B && (b_el * sizeof(T)) % 16 == 0 && ((uintptr_t)B % 16) == 0;
+    if constexpr (LDS_B) {
+        if (b_dma) {
+            const int nq = (int)(b_el * sizeof(T) / 16);
+            const uint4 *src = reinterpret_cast<const uint4 *>(B);
+            for (int c = wave; c * 64 < nq; c += waves) {
+                if (c * 64 + lane < nq)
+                    __builtin_amdgcn_global_load_lds(
+                        src + c * 64 + lane,
+                        (__attribute__((address_space(3))) void *)(smem + (size_t)c * 1024), 16, 0, 0);
+            }
+        }
+    }
+    // the block's slice headers into LDS
+    for (int t = threadIdx.x; t <= be - bb; t += blockDim.x) {
+        const int hp = sptr[bb + t];
+        hp_l[t] = hp;
+        he_l[t] = vptr[hp];
+    }
+    if (threadIdx.x == 0) *unit_ctr = waves;  // units 0 .. waves-1 are taken below
+
+    // the first unit's first round, planned from global headers meanwhile
+    int u = wave;
+    int cs = 0, ce = 0, c0 = 0;
+    auto unit_bounds = [&](int unit) {
+        const int c = unit % nch;
+        c0 = (unit / nch) * chunk_w;
+        cs = bb + c * CH;
+        ce = min(cs + CH, be);
+    };
     RowRound r;
     int W[NWR], GS[GWR];
     T GV[GWR];
-    const RowCursor start{s_beg, 0, 0, false};
-    if (s_beg < s_end) {
-        rows_plan<NWR, GWR>(r, start, s_end, n_slices, lane, sptr, vptr);
+    if (u < nunits) {
+        unit_bounds(u);
+        rows_headers(r, cs, n_slices, lane, sptr, vptr);
+        rows_fit<NWR, GWR>(r, RowCursor{cs, 0, 0, false}, ce, lane, vptr);
         rows_load<NWR, GWR>(r, W, GS, GV, lane, vptr, vals, idx);
     }
 
     const char *Bb = reinterpret_cast<const char *>(B);
     if constexpr (LDS_B) {
         T *lb = reinterpret_cast<T *>(smem);
-        const size_t n_el = (size_t)n_in * w;
-        if ((n_el * sizeof(T)) % 16 == 0 && ((uintptr_t)B % 16) == 0) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(B);
-            uint4 *dst = reinterpret_cast<uint4 *>(lb);
-            for (size_t k = threadIdx.x; k < n_el * sizeof(T) / 16; k += blockDim.x)
-                dst[k] = src[k];
-        } else {
-            for (size_t k = threadIdx.x; k < n_el; k += blockDim.x) lb[k] = B[k];
+        if (!b_dma) {
+            for (size_t k = threadIdx.x; k < b_el; k += blockDim.x) lb[k] = B[k];
         }
-        __syncthreads();
         Bb = reinterpret_cast<const char *>(lb);
     }
-    if (s_beg >= s_end) return;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+    __syncthreads();                     // and every other wave's, and the headers
+    if (u >= nunits) return;
 
-    for (int c0 = 0; c0 < w; c0 += chunk) {
+    int u_next = -1;  // the unit claimed for after this one
+    T acc[VEC];       // carried over the rounds of a slice
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+    for (;;) {
+        // this round's windows have landed (they were in flight during the
+        // previous round); after this wait only the next round's loads are
+        // pending, and nothing in this round's walk waits for them
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        if (u_next < 0) {
+            int t = 0;
+            if (lane == 0) t = atomicAdd(unit_ctr, 1);
+            u_next = readlane(t, 0);
+        }
         const int col = c0 + cl * VEC;
         const bool act = col < w;
         const uint32_t coff4 = act ? 4u * col : 0u;  // gathers stay inside B's rows
-        T acc[VEC];  // carried over the rounds of a slice
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = T(0);
-        if (c0 > 0) {
-            rows_plan<NWR, GWR>(r, start, s_end, n_slices, lane, sptr, vptr);
-            rows_load<NWR, GWR>(r, W, GS, GV, lane, vptr, vals, idx);
+
+        // plan the next round and put its windows in flight (not after a
+        // partial round: where it stops is known only once it is walked)
+        RowRound rn;
+        int W2[NWR], GS2[GWR];
+        T GV2[GWR];
+        bool pre = false, switch_unit = false;
+        if (!r.open_end) {
+            const int s_next = r.sa + r.nsl;
+            if (s_next < ce) {
+                rows_headers_lds(rn, s_next, bb, be, lane, hp_l, he_l);
+                rows_fit<NWR, GWR>(rn, RowCursor{s_next, 0, 0, false}, ce, lane, vptr);
+                pre = true;
+            } else if (u_next < nunits) {
+                const int c = u_next % nch;
+                const int ncs = bb + c * CH, nce = min(ncs + CH, be);
+                rows_headers_lds(rn, ncs, bb, be, lane, hp_l, he_l);
+                rows_fit<NWR, GWR>(rn, RowCursor{ncs, 0, 0, false}, nce, lane, vptr);
+                pre = switch_unit = true;
+            }
+            if (pre) rows_load<NWR, GWR>(rn, W2, GS2, GV2, lane, vptr, vals, idx);
         }
-        for (;;) {
-            write_marks<GWR>(GS, GV, r.K1 - r.K0, r.E0, r.E1, r.mid || r.open_end, lane, mark,
-                             gvt);
-            const int nwin = (r.E1 - r.E0 + 63) >> 6;
-            int i = 0;        // slice of the round being accumulated
-            int e0 = r.E0;    // its first entry in the round
-            int e1 = r.nsl > 0 ? readlane(r.he, 1) : r.E1;  // its end (round end if open)
 
-            // sums slice i over the entry lanes, writes its row, moves on
-            auto close = [&]() {
-                T res[Sum::VO];
-                Sum::run(acc, res);
-                if (Sum::writer(lane) && act) {
-                    T *o = out + (size_t)(r.sa + i) * w + col + Sum::base(lane);
-                    store_vec<T, Sum::VO>(o, res);
-                }
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] = T(0);
-                ++i;
-                e0 = e1;
-                e1 = i < r.nsl ? readlane(r.he, i + 1) : (r.open_end ? r.E1 : e1);
-            };
+        write_marks<NWR, GWR>(GS, GV, r.K1 - r.K0, r.E0, r.E1, r.mid || r.open_end, lane,
+                              mark, gvt);
+        const int nwin = (r.E1 - r.E0 + 63) >> 6;
+        int i = 0;        // slice of the round being accumulated
+        int e0 = r.E0;    // its first entry in the round
+        int e1 = r.nsl > 0 ? readlane(r.he, 1) : r.E1;  // its end (round end if open)
 
-            // empty slices before the first entry
-            while (i < r.nsl && e1 <= r.E0) close();
-            const int g_last = window_stream<LOG_WW, VEC, NWR>(
-                W, nwin, lane, slot, mark, gvt, Bb, w4, coff4,
-                [&](int k, int j0, const Stage<Gm::SBV, VEC> &st) {
-                    const int step0 = r.E0 + 64 * k + j0 * Gm::G;
-                    if (e1 >= step0 + Gm::SBV * Gm::G) {
-                        // every lane of the stage is in the current slice
+        // sums slice i over the entry lanes, writes its row, moves on
+        auto close = [&]() {
+            T res[Sum::VO];
+            Sum::run(acc, res);
+            if (Sum::writer(lane) && act) {
+                T *o = out + (size_t)(r.sa + i) * w + col + Sum::base(lane);
+                store_vec<T, Sum::VO>(o, res);
+            }
 #pragma unroll
-                        for (int t = 0; t < Gm::SBV; ++t) {
-#pragma unroll
-                            for (int e = 0; e < VEC; ++e)
-                                acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
-                        }
-                        return;
-                    }
+            for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+            ++i;
+            e0 = e1;
+            e1 = i < r.nsl ? readlane(r.he, i + 1) : (r.open_end ? r.E1 : e1);
+        };
+
+        // empty slices before the first entry
+        while (i < r.nsl && e1 <= r.E0) close();
+        const int g_last = window_stream<LOG_WW, VEC, NWR, true>(
+            W, nwin, lane, slot, mark, gvt, Bb, w4, coff4,
+            [&](int k, int j0, const Stage<Gm::SBV, VEC> &st) {
+                const int step0 = r.E0 + 64 * k + j0 * Gm::G;
+                if (e1 >= step0 + Gm::SBV * Gm::G) {
+                    // every lane of the stage is in the current slice
 #pragma unroll
                     for (int t = 0; t < Gm::SBV; ++t) {
-                        const int step_end = step0 + (t + 1) * Gm::G;
-                        const int pj = step_end - Gm::G + slot;
-                        // close every slice that ends inside this step
-                        while (i < r.nsl && e1 < step_end) {
-                            if (pj >= e0 && pj < e1) {
 #pragma unroll
-                                for (int e = 0; e < VEC; ++e)
-                                    acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
-                            }
-                            close();
-                        }
+                        for (int e = 0; e < VEC; ++e)
+                            acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
+                    }
+                    return;
+                }
+#pragma unroll
+                for (int t = 0; t < Gm::SBV; ++t) {
+                    const int step_end = step0 + (t + 1) * Gm::G;
+                    if (e0 <= step_end - Gm::G && e1 >= step_end) {
+                        // this step lies inside the current slice
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
+                        continue;
+                    }
+                    const int pj = step_end - Gm::G + slot;
+                    // close every slice that ends inside this step
+                    while (i < r.nsl && e1 < step_end) {
                         if (pj >= e0 && pj < e1) {
 #pragma unroll
                             for (int e = 0; e < VEC; ++e)
                                 acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
                         }
+                        close();
                     }
-                });
-            // slices ending at the round's last entry, and empty ones after
-            while (i < r.nsl) close();
-            RowCursor nxt;
-            if (r.open_end) nxt = RowCursor{r.sa, r.E1, r.K0 + g_last - 1, true};
-            else nxt = RowCursor{r.sa + r.nsl, 0, 0, false};
-            __builtin_amdgcn_wave_barrier();
-            if (nxt.sa >= s_end) break;
-            rows_plan<NWR, GWR>(r, nxt, s_end, n_slices, lane, sptr, vptr);
+                    if (pj >= e0 && pj < e1) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            acc[e] = fma_t(st.vj[t], st.bv[t][e], acc[e]);
+                    }
+                }
+            });
+        // slices ending at the round's last entry, and empty ones after
+        while (i < r.nsl) close();
+        __builtin_amdgcn_wave_barrier();
+        if (r.open_end) {  // the open slice goes on from E1
+            const RowCursor c{r.sa, r.E1, r.K0 + g_last - 1, true};
+            rows_headers_lds(r, c.sa, bb, be, lane, hp_l, he_l);
+            rows_fit<NWR, GWR>(r, c, ce, lane, vptr);
             rows_load<NWR, GWR>(r, W, GS, GV, lane, vptr, vals, idx);
+            continue;
+        }
+        if (!pre) break;
+        if (switch_unit) {
+            u = u_next;
+            u_next = -1;
+            unit_bounds(u);
+        }
+        r = rn;
+#pragma unroll
+        for (int k = 0; k < NWR; ++k) W[k] = W2[k];
+#pragma unroll
+        for (int j = 0; j < GWR; ++j) {
+            GS[j] = GS2[j];
+            GV[j] = GV2[j];
         }
     }
 }
@@ -527,7 +647,7 @@ k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     using T = float;
     using Sum = SlotSum<LOG_WW, VEC>;
     __shared__ T part[8][64 * VEC];
-    __shared__ __attribute__((aligned(16))) unsigned char lds[8][kRowsWaveLds];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[8][kPieceWaveLds];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
@@ -538,7 +658,7 @@ k_vcs_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     const int cl = lane & ((1 << LOG_WW) - 1);
     const int chunk = VEC << LOG_WW;
     unsigned char *mark = lds[wave];
-    T *gvt = reinterpret_cast<T *>(lds[wave] + 64 * kRowsNWR);
+    T *gvt = reinterpret_cast<T *>(lds[wave] + 64 * kPieceNWR);
     const uint32_t w4 = (uint32_t)w * 4u;
     const char *Bb = reinterpret_cast<const char *>(B);
     for (int s0 = blockIdx.x * spb; s0 < n_slices; s0 += gridDim.x * spb) {
