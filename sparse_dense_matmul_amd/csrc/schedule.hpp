@@ -247,6 +247,24 @@ k_count(int nnz, const int *__restrict__ idx, int *__restrict__ cnt) {
         atomicAdd(&cnt[idx[p]], 1);
 }
 
+// The same with a per-block histogram in LDS (n_bins ints of dynamic LDS),
+// for few bins hit many times per block: each block counts a contiguous range
+// of entries locally and adds its non-zero bins to cnt once.
+__global__ void __launch_bounds__(1024)
+k_count_lds(int nnz, const int *__restrict__ idx, int *__restrict__ cnt, int n_bins) {
+    extern __shared__ int hist[];
+    for (int b = threadIdx.x; b < n_bins; b += blockDim.x) hist[b] = 0;
+    __syncthreads();
+    const int p0 = (int)((long long)blockIdx.x * nnz / gridDim.x);
+    const int p1 = (int)((long long)(blockIdx.x + 1) * nnz / gridDim.x);
+    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&hist[idx[p]], 1);
+    __syncthreads();
+    for (int b = threadIdx.x; b < n_bins; b += blockDim.x) {
+        const int c = hist[b];
+        if (c) atomicAdd(&cnt[b], c);
+    }
+}
+
 // ------------------------------------------------------------- transpose
 
 template <typename T>

@@ -365,9 +365,16 @@ void count_and_scan(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *tptr,
                     hipStream_t s) {
     const int64_t nmin = h.n_minor();
     launch_zero(w.cnt, size_t(nmin) * 4, s);
-    if (h.nnz > 0)
+    const int64_t blocks = std::max(n_cu, 1);
+    if (h.nnz > 0 && nmin <= 32768 && nmin * 4 <= h.nnz / blocks) {
+        // few bins, each hit many times per block: count in LDS first
+        allow_lds(reinterpret_cast<const void *>(&k_count_lds));
+        hipLaunchKernelGGL(k_count_lds, dim3(unsigned(blocks)), dim3(1024), size_t(nmin) * 4, s,
+                           int(h.nnz), h.idx, w.cnt, int(nmin));
+    } else if (h.nnz > 0) {
         hipLaunchKernelGGL(k_count, dim3(grid_for(h.nnz, n_cu)), dim3(256), 0, s, int(h.nnz),
                            h.idx, w.cnt);
+    }
     scan_excl(w.cnt, tptr, nmin, w.bsums, tptr + nmin, s);
 }
 
