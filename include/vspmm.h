@@ -198,7 +198,10 @@ typedef enum {
 /* The lane split a product would use (host outputs, any may be NULL):
  * entry lanes per slice, width lanes, elements per lane, slices per wave,
  * whether the gathered operand is staged in LDS, and the kernel family
- * (vspmm_kernel). In deterministic mode a misaligned product reports its
+ * (vspmm_kernel). The scatter walk balances entries rather than slices over
+ * its waves (slices per wave 0), takes its entry lanes as entries added side
+ * by side, and reports as LDS-staged the copy of the output each block adds
+ * into when the output fits in LDS. In deterministic mode a misaligned product reports its
  * second pass, the aligned walk over the opposite layout. The caller's buffer
  * alignment is not known here, so 16-byte aligned operands are assumed. */
 vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,

@@ -29,6 +29,7 @@ UNITS = [
     ("walk_short.hip", ["-DVSPMM_ELT=double"], "walk_short_f64"),
     ("walk_long.hip", [], "walk_long"),
     ("walk_plain.hip", [], "walk_plain"),
+    ("walk_scatter.hip", [], "walk_scatter"),
 ] + [(f"walk_vcs_{kind}.hip", [f"-DVSPMM_VEC={v}"], f"walk_vcs_{kind}_v{v}")
      for kind in ("rows", "long") for v in (1, 2, 4)]
 ARCH = "gfx950"

@@ -62,6 +62,22 @@ struct WalkArgs {
     int n_in;
 };
 
+// The operands of one scatter walk (slices of the walked layout = rows of B).
+template <typename T>
+struct ScatterArgs {
+    int n_slices;
+    int n_groups;     // VCS groups (unused for CSR)
+    int nnz;
+    const int *sptr;  // slice pointers: CSR row_ptr or VCS major_ptr
+    const int *vptr;  // VCS value_ptr (null for CSR)
+    const T *vals;    // CSR values or VCS group values
+    const int *idx;   // minor indices (rows of out)
+    const T *B;       // dense input, n_slices x w, row-major
+    T *out;           // dense output, n_out x w, row-major, zeroed by the caller
+    int w;
+    int n_out;
+};
+
 // Raises a kernel's dynamic LDS limit to a whole CU (once per kernel).
 void allow_lds(const void *fn);
 
@@ -81,10 +97,13 @@ void launch_short(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
 template <bool VCS, typename T>
 void launch_long(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
 
-// walk_plain.hip: the plain slice-per-lane-group walk and the atomic scatter.
+// walk_plain.hip: the plain slice-per-lane-group walk.
 template <bool VCS, typename T>
 void launch_plain(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
+
+// walk_scatter.hip: the atomic scatter walk (pl.vec, pl.sp.log_ww, grid,
+// block; pl.lds adds through an LDS copy of out of pl.lds_bytes).
 template <bool VCS, typename T>
-void launch_scatter(const Plan &pl, const WalkArgs<T> &a, hipStream_t s);
+void launch_scatter(const Plan &pl, const ScatterArgs<T> &a, hipStream_t s);
 
 }  // namespace vspmm

@@ -115,17 +115,14 @@ constexpr int64_t kLongMean = 1024;        // mean entries per slice for k_long
 // entries, at width w. Entry lanes G and width lanes WW are powers of two with
 // G * WW <= 64; R = 64 / (G * WW) slices share a wave.
 Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_matrix,
-               int force_group, bool scatter, const void *B, const void *out, int n_cu,
+               int force_group, const void *B, const void *out, int n_cu,
                int64_t n_in = 0, bool vcs = false) {
     Plan pl;
     int vec = 1;
-    if (!scatter) {
-        const int max_vec = int(16 / elt);
-        for (int v = max_vec; v > 1; v >>= 1) {
-            if (w % v == 0 && aligned(B, v * elt) && aligned(out, v * elt)) {
-                vec = v;
-                break;
-            }
+    for (int v = int(16 / elt); v > 1; v >>= 1) {
+        if (w % v == 0 && aligned(B, v * elt) && aligned(out, v * elt)) {
+            vec = v;
+            break;
         }
     }
     pl.vec = vec;
@@ -150,7 +147,7 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
     const size_t b_bytes = size_t(n_in) * size_t(w) * elt;
     // the VCS walks address B with 32-bit byte offsets and 24-bit row numbers
     const bool small_b = b_bytes < (size_t(1) << 32) && n_in < (int64_t(1) << 24);
-    if (!scatter && pl.R == 1 && (!vcs || small_b)) {
+    if (pl.R == 1 && (!vcs || small_b)) {
         if (mean >= kLongMean) {
             pl.kind = kLong;
             pl.block = 512;
@@ -251,8 +248,48 @@ void launch_aligned(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t 
     launch_plain<false, T>(pl, a, s);
 }
 
+// The scatter walk's plan: one column per lane, WW = w lanes per entry
+// rounded up to a power of two (at most 64), a wave per balanced entry range.
+// The adds' cost is set by the hardware's atomic rates: an L2 float atomic
+// instruction costs about the same per 64-byte run it touches whether one
+// lane or sixteen add into that run, while LDS float atomics go about one
+// lane per two to three clocks per CU. So a block adds into a private LDS copy
+// of out (then once per element into out) only when out fits in LDS, its
+// rows are narrow (at most 32 bytes, where most of an L2 request would be
+// idle) and enough blocks share the entries (32 per 4 bytes of row: with
+// fewer CUs adding, the LDS adds fall behind the L2's). The copy's flush is
+// coalesced, so a full grid costs it little.
+Plan scatter_plan(int64_t nnz, int64_t w, int64_t no, size_t elt, int n_cu, int force_group) {
+    Plan pl;
+    pl.vec = 1;
+    pl.sp.log_ww = std::min(6, ilog2_ceil(std::max<int64_t>(w, 1)));
+    if (force_group > 0) pl.sp.log_ww = 6 - std::min(6, ilog2_floor(force_group));
+    pl.sp.log_g = 6 - pl.sp.log_ww;
+    pl.R = 0;  // entries, not slices, are balanced over the waves
+    n_cu = std::max(n_cu, 1);
+    const size_t out_bytes = size_t(no) * size_t(w) * elt;
+    const int64_t priv_grid = std::min<int64_t>(n_cu, nnz / (2 * std::max<int64_t>(no, 1)));
+    if (out_bytes > 0 && out_bytes <= kLdsMax && size_t(w) * elt <= 32 &&
+        priv_grid >= int64_t(w) * int64_t(elt) * 8) {
+        pl.lds = true;
+        pl.lds_bytes = out_bytes;
+        pl.block = 1024;
+        pl.grid = int(priv_grid);
+        return pl;
+    }
+    // waves of at least 8 windows, 16 waves per CU at most
+    const int64_t waves = std::max<int64_t>(1, std::min<int64_t>((nnz + 511) / 512, int64_t(n_cu) * 16));
+    pl.block = 256;
+    pl.grid = int((waves + 3) / 4);
+    return pl;
+}
+
 template <typename T>
-void launch_scatter_any(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
+void launch_scatter_any(bool vcs, const Plan &pl, const vspmm_matrix_s &h, const void *B,
+                        void *out, int w, int64_t no, hipStream_t s) {
+    const ScatterArgs<T> a{int(h.n_major()), int(h.n_groups), int(h.nnz), h.sptr, h.vptr,
+                           static_cast<const T *>(h.vals), h.idx, static_cast<const T *>(B),
+                           static_cast<T *>(out), w, int(no)};
     if constexpr (sizeof(T) == 4) {
         if (vcs) return launch_scatter<true, T>(pl, a, s);
     }
@@ -479,7 +516,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     if (is_aligned(h, dir)) {
         const int64_t ni = h.n_minor();
         const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
-                                  false, B, out, n_cu, ni, vcs);
+                                  B, out, n_cu, ni, vcs);
         if (h.dtype == VSPMM_F64)
             launch_aligned<double>(vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr, h.vals,
                                                               h.idx, B, out, w, ni), s);
@@ -489,15 +526,10 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         return hip_status();
     }
     if (mode == VSPMM_ATOMIC) {
-        const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
-                                  true, B, out, n_cu);
+        const Plan pl = scatter_plan(h.nnz, w, no, h.elt(), n_cu, h.force_group);
         launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
-        if (h.dtype == VSPMM_F64)
-            launch_scatter_any<double>(vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr,
-                                                                  h.vals, h.idx, B, out, w, 0), s);
-        else
-            launch_scatter_any<float>(vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr,
-                                                                h.vals, h.idx, B, out, w, 0), s);
+        if (h.dtype == VSPMM_F64) launch_scatter_any<double>(vcs, pl, h, B, out, w, no, s);
+        else launch_scatter_any<float>(vcs, pl, h, B, out, w, no, s);
         return hip_status();
     }
     // deterministic: build (or reuse) the opposite layout, then walk it aligned
@@ -526,7 +558,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     }
     const int64_t nmin = h.n_minor();
     const int64_t nmaj = h.n_major();
-    const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, false, B, out,
+    const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, B, out,
                               n_cu, nmaj, vcs);
     if (h.dtype == VSPMM_F64)
         launch_aligned<double>(false, pl, walk_args<double>(nmin, wl.t_ptr, nullptr, wl.t_vals,
@@ -781,8 +813,11 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     // alignment of the caller's buffers is unknown here: assume 16-byte aligned
     alignas(16) static const float probe[4] = {0, 0, 0, 0};
     const DeviceInfo di = device_info(h->device);
-    const Plan pl = make_plan(ns, h->nnz, width, h->elt(), split_matrix, h->force_group, scatter,
-                              probe, probe, di.ok ? di.n_cu : 256, ni, vcs);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    const Plan pl = scatter ? scatter_plan(h->nnz, width, n_out(*h, dir), h->elt(), n_cu,
+                                           h->force_group)
+                            : make_plan(ns, h->nnz, width, h->elt(), split_matrix,
+                                        h->force_group, probe, probe, n_cu, ni, vcs);
     if (entry_lanes) *entry_lanes = 1 << pl.sp.log_g;
     if (width_lanes) *width_lanes = 1 << pl.sp.log_ww;
     if (vec) *vec = pl.vec;

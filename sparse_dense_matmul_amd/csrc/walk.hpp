@@ -1,6 +1,6 @@
-// Slice walks for gfx950 (wave64): the aligned walk (output rows are the
-// layout's major slices) and the scatter walk (output rows are the minor
-// indices). Both follow the lane split of the vsparse page, section "The
+// Slice walks for gfx950 (wave64): the plain aligned walk (output rows are
+// the layout's major slices) and the helpers the walk families share. It
+// follows the lane split of the vsparse page, section "The
 // kernels", widened to a 64-lane wave: a slice is walked by G "entry lanes"
 // that take its entries in stride, and each entry lane is WW "width lanes"
 // wide, each covering VEC consecutive elements of the dense width. With
@@ -271,51 +271,6 @@ k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                                         });
             slot_reduce_xor<T, VEC>(acc, sp.log_ww, log_sub);
             if (slot == 0 && act) store_vec<T, VEC>(out + (size_t)s * w + col, acc);
-        }
-    }
-}
-
-// Scatter walk: for every entry (s, i, v) of slice s, out[i][:] += v * B[s][:]
-// with hardware float atomics (out must be zeroed first). B: n_slices x w,
-// out: n_minor x w. One element per width lane, so the lanes of an entry hit
-// one contiguous run of out.
-template <bool VCS, typename T, bool UNIFORM>
-__global__ void __launch_bounds__(256)
-k_scatter(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
-          const T *__restrict__ vals, const int *__restrict__ idx,
-          const T *__restrict__ B, T *__restrict__ out, int w, Split sp) {
-    const int lane = threadIdx.x & 63;
-    const int waves = blockDim.x >> 6;
-    const int log_sub = sp.log_ww + sp.log_g;
-    const int G = 1 << sp.log_g;
-    const int sub = lane >> log_sub;
-    const int slot = (lane >> sp.log_ww) & (G - 1);
-    const int cl = lane & ((1 << sp.log_ww) - 1);
-    const int R = 64 >> log_sub;
-    const int chunk = 1 << sp.log_ww;
-    const int stride = gridDim.x * waves * R;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int s = (blockIdx.x * waves + wave) * R + (UNIFORM ? 0 : sub); s < n_slices;
-         s += stride) {
-        int e0, e1, ka = 0, kb = 0;
-        if constexpr (VCS) {
-            ka = sptr[s];
-            kb = sptr[s + 1];
-            e0 = vptr[ka];
-            e1 = vptr[kb];
-        } else {
-            e0 = sptr[s];
-            e1 = sptr[s + 1];
-        }
-        for (int c0 = 0; c0 < w; c0 += chunk) {
-            const int col = c0 + cl;
-            const bool act = col < w;
-            const T b = act ? B[(size_t)s * w + col] : T(0);
-            walk_slice<VCS, UNIFORM, T>(lane, slot, G, ka, kb, e0, e1, vptr, vals, idx,
-                                        [&](bool valid, int i, T v) {
-                                            if (valid && act)
-                                                atomic_add_t(out + (size_t)i * w + col, v * b);
-                                        });
         }
     }
 }

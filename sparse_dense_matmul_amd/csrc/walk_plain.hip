@@ -1,5 +1,4 @@
-// Launchers of the plain aligned walk (k_aligned) and the atomic scatter walk
-// (k_scatter).
+// Launcher of the plain aligned walk (k_aligned).
 #include "launch.hpp"
 #include "walk.hpp"
 
@@ -29,22 +28,8 @@ void launch_plain(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
 #undef VSPMM_PLAIN
 }
 
-template <bool VCS, typename T>
-void launch_scatter(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
-    const dim3 g(pl.grid), b(pl.block);
-    if (VCS && pl.R == 1)
-        hipLaunchKernelGGL((k_scatter<VCS, T, VCS>), g, b, 0, s, a.n_slices, a.sptr, a.vptr,
-                           a.vals, a.idx, a.B, a.out, a.w, pl.sp);
-    else
-        hipLaunchKernelGGL((k_scatter<VCS, T, false>), g, b, 0, s, a.n_slices, a.sptr, a.vptr,
-                           a.vals, a.idx, a.B, a.out, a.w, pl.sp);
-}
-
 template void launch_plain<true, float>(const Plan &, const WalkArgs<float> &, hipStream_t);
 template void launch_plain<false, float>(const Plan &, const WalkArgs<float> &, hipStream_t);
 template void launch_plain<false, double>(const Plan &, const WalkArgs<double> &, hipStream_t);
-template void launch_scatter<true, float>(const Plan &, const WalkArgs<float> &, hipStream_t);
-template void launch_scatter<false, float>(const Plan &, const WalkArgs<float> &, hipStream_t);
-template void launch_scatter<false, double>(const Plan &, const WalkArgs<double> &, hipStream_t);
 
 }  // namespace vspmm

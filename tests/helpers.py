@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import workloads as W
 from conftest import gpu_required
 
 TOL = 1e-5  # max |gpu - oracle| / (|A| |B|) on float32 results
@@ -57,3 +58,18 @@ def check_close(orc, L, direction, B, got, want=None, tol=TOL, where=""):
     assert zeros_ok, f"{where}: outputs with |A||B| = 0 are not exactly zero"
     assert rel <= tol, f"{where}: max relative error {rel:.3e} > {tol:g}"
     return rel
+
+
+def with_empty_groups(L, rng, n_rows=6, per_row=300):
+    """The same matrix with runs of empty groups (value_ptr[k] == value_ptr[k+1])
+    inserted at the start, middle and end of some slices: the product must not
+    change."""
+    mp, vals, vp = L.major_ptr.astype(np.int64), L.values.copy(), L.value_ptr.astype(np.int64)
+    for r in sorted(rng.choice(L.n_major, size=n_rows, replace=False), reverse=True):
+        g0, g1 = int(mp[r]), int(mp[r + 1])
+        at = [g0, (g0 + g1) // 2, g1][r % 3]
+        vals = np.insert(vals, at, np.float32(7.0) * np.ones(per_row, np.float32))
+        vp = np.insert(vp, at, np.full(per_row, vp[at]))
+        mp[r + 1:] += per_row
+    return W.Vcs(L.layout, L.shape, mp.astype(np.int32), vals.astype(np.float32),
+                 vp.astype(np.int32), L.indices)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from helpers import check_close, dims, need_gpu, to_dev, vcs_handle
+from helpers import check_close, dims, need_gpu, to_dev, vcs_handle, with_empty_groups
 
 pytestmark = pytest.mark.gpu
 
@@ -67,21 +67,6 @@ def mixed_rows(rng):
         cols.append(c.astype(t.cols.dtype))
         vals.append(np.asarray(v, dtype=np.float32))
     return W.Triplets(t.shape, np.concatenate(rows), np.concatenate(cols), np.concatenate(vals))
-
-
-def with_empty_groups(L, rng, n_rows=6, per_row=300):
-    """The same matrix with runs of empty groups (value_ptr[k] == value_ptr[k+1])
-    inserted at the start, middle and end of some slices: the product must not
-    change."""
-    mp, vals, vp = L.major_ptr.astype(np.int64), L.values.copy(), L.value_ptr.astype(np.int64)
-    for r in sorted(rng.choice(L.n_major, size=n_rows, replace=False), reverse=True):
-        g0, g1 = int(mp[r]), int(mp[r + 1])
-        at = [g0, (g0 + g1) // 2, g1][r % 3]
-        vals = np.insert(vals, at, np.float32(7.0) * np.ones(per_row, np.float32))
-        vp = np.insert(vp, at, np.full(per_row, vp[at]))
-        mp[r + 1:] += per_row
-    return W.Vcs(L.layout, L.shape, mp.astype(np.int32), vals.astype(np.float32),
-                 vp.astype(np.int32), L.indices)
 
 
 @pytest.fixture(scope="module")
