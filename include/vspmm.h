@@ -143,12 +143,32 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * the other axis) inside ws, and runs the aligned walk over it. Later calls
  * with the same handle, direction and ws reuse what is there: the caller must
  * not write into ws between them, or must call vspmm_workspace_invalidate.
+ *
+ * Tiled schedule (VCSR/VCSC, float, either direction): when B's rows do not
+ * fit in a CU's LDS and ws holds at least vspmm_workspace_size_width bytes
+ * for this width, deterministic mode instead builds a tiled copy of the
+ * matrix: B's rows are cut into tiles that fit in LDS and each output row's
+ * entries are split by tile, every (tile, output row) part grouped by value
+ * as in the pages' value-grouped layouts. The product walks it with each
+ * block's tile of B in LDS, writes one partial row per (tile, output row) into
+ * ws and adds them in tile order; it repeats bit for bit. The copy is reused
+ * like the opposite layout (it also depends on the tile size, which follows
+ * the width). A smaller ws falls back to the path above (aligned: the plain
+ * walk, ws unused).
+ *
  * ws: device, 256-byte aligned, at least vspmm_workspace_size bytes; unused
  * (may be NULL) when the size is 0. Errors: as vspmm_spmm, plus
  * _WORKSPACE. */
 vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t width,
                            vspmm_direction dir, vspmm_mode mode, void *ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/* Bytes of workspace for a product of the given width: in deterministic
+ * mode, what the tiled schedule needs when it applies (see vspmm_spmm_ex),
+ * else the same as vspmm_workspace_size. bytes: host. Errors: as
+ * vspmm_workspace_size, plus _DIM (negative width). */
+vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
+                                        int64_t width, size_t *bytes);
 
 /* Forget any schedule cached in the workspace at ws (call before reusing
  * that memory for anything else). */
@@ -201,13 +221,15 @@ typedef enum {
  * (vspmm_kernel). The scatter walk balances entries rather than slices over
  * its waves (slices per wave 0), takes its entry lanes as entries added side
  * by side, and reports as LDS-staged the copy of the output each block adds
- * into when the output fits in LDS. In deterministic mode a misaligned product reports its
+ * into when the output fits in LDS. tiles: in deterministic mode, the tiles of
+ * B a tiled schedule would use (0 when none applies); the other outputs then
+ * describe the walk over the tiled copy. In deterministic mode a misaligned product reports its
  * second pass, the aligned walk over the opposite layout. The caller's buffer
  * alignment is not known here, so 16-byte aligned operands are assumed. */
 vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
                              vspmm_mode mode, int32_t *entry_lanes, int32_t *width_lanes,
                              int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged,
-                             int32_t *kernel);
+                             int32_t *kernel, int32_t *tiles);
 
 /* A static string naming the status. */
 const char *vspmm_status_string(vspmm_status st);

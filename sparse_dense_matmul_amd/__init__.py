@@ -49,8 +49,10 @@ EXPORTS = {
     "vspmm_transpose_csr": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_regroup_vcs": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_footprint": ([_vp, _P(_sz), _P(_sz)], ctypes.c_int),
+    "vspmm_workspace_size_width": ([_vp, ctypes.c_int, ctypes.c_int, _i64, _P(_sz)],
+                                   ctypes.c_int),
     "vspmm_plan_info": ([_vp, _i64, ctypes.c_int, ctypes.c_int, _P(_i32), _P(_i32), _P(_i32),
-                         _P(_i32), _P(_i32), _P(_i32)], ctypes.c_int),
+                         _P(_i32), _P(_i32), _P(_i32), _P(_i32)], ctypes.c_int),
     "vspmm_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 
@@ -60,13 +62,30 @@ def _load():
         raise ImportError(f"{LIB_PATH} is not built: run `python -m sparse_dense_matmul_amd.build`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (argtypes, restype) in EXPORTS.items():
-        fn = getattr(handle, name)
+        try:
+            fn = getattr(handle, name)
+        except AttributeError as e:
+            raise ImportError(f"{LIB_PATH} lacks {name}: rebuild it with "
+                              "`python -m sparse_dense_matmul_amd.build`") from e
         fn.argtypes = argtypes
         fn.restype = restype
     return handle
 
 
-lib = _load()
+class _Lib:
+    """The library, loaded on first use, so that importing the package (the
+    build module included) works before the library is built; any call then
+    fails loudly if it is missing or stale."""
+
+    _handle = None
+
+    def __getattr__(self, name):
+        if _Lib._handle is None:
+            _Lib._handle = _load()
+        return getattr(_Lib._handle, name)
+
+
+lib = _Lib()
 
 
 class VspmmError(RuntimeError):
@@ -172,15 +191,24 @@ class SparseMatrix:
             return self.spmm(B.unsqueeze(1), "BA")[:, 0]
         return self.spmm(B.t().contiguous(), "BA").t()
 
-    def workspace_size(self, direction: str = "BA", mode: str = "deterministic") -> int:
+    def workspace_size(self, direction: str = "BA", mode: str = "deterministic",
+                       width: int | None = None) -> int:
+        """Workspace bytes for ``spmm(..., mode=mode)``; with ``width``, enough for
+        the tiled schedule at that width when one applies."""
         n = _sz(0)
-        _check(lib.vspmm_workspace_size(self._h, DIRECTIONS[direction], MODES[mode],
-                                        ctypes.byref(n)), "vspmm_workspace_size")
+        if width is None:
+            _check(lib.vspmm_workspace_size(self._h, DIRECTIONS[direction], MODES[mode],
+                                            ctypes.byref(n)), "vspmm_workspace_size")
+        else:
+            _check(lib.vspmm_workspace_size_width(self._h, DIRECTIONS[direction], MODES[mode],
+                                                  width, ctypes.byref(n)),
+                   "vspmm_workspace_size_width")
         return int(n.value)
 
-    def workspace(self, direction: str = "BA", mode: str = "deterministic") -> torch.Tensor:
+    def workspace(self, direction: str = "BA", mode: str = "deterministic",
+                  width: int | None = None) -> torch.Tensor:
         """A fresh device workspace of the required size (256-byte aligned)."""
-        nbytes = self.workspace_size(direction, mode)
+        nbytes = self.workspace_size(direction, mode, width)
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
 
     def validate(self) -> bool:
@@ -196,14 +224,15 @@ class SparseMatrix:
         return int(a.value), int(b.value)
 
     def plan_info(self, width: int, direction: str = "AB", mode: str = "atomic") -> dict:
-        vals = [_i32(0) for _ in range(6)]
+        vals = [_i32(0) for _ in range(7)]
         _check(lib.vspmm_plan_info(self._h, width, DIRECTIONS[direction], MODES[mode],
                                    *[ctypes.byref(v) for v in vals]), "vspmm_plan_info")
-        keys = ("entry_lanes", "width_lanes", "vec", "slices_per_wave", "lds_staged", "kernel")
+        keys = ("entry_lanes", "width_lanes", "vec", "slices_per_wave", "lds_staged", "kernel",
+                "tiles")
         info = {k: int(v.value) for k, v in zip(keys, vals)}
         # the walked layout: the handle's own, or the opposite one in deterministic mode
         aligned = (self.layout != "vcsc") == (direction == "AB")
-        walked = self.layout if aligned or mode == "atomic" else \
+        walked = self.layout if aligned or mode == "atomic" or info["tiles"] else \
             {"vcsr": "vcsc", "vcsc": "vcsr", "csr": "csr"}[self.layout]
         vcs = walked != "csr"
         info["kernel_name"] = {0: "k_aligned", 1: "k_vcs_rows" if vcs else "k_short",

@@ -60,6 +60,10 @@ struct WalkArgs {
     T *out;           // dense output, n_slices x w, row-major
     int w;
     int n_in;
+    // k_vcs_rows only: the slices as `tiles` runs, each over n_in rows of B
+    // (the last one cut at n_b_rows); 1 and n_in for an untiled walk
+    int tiles = 1;
+    int n_b_rows = 0;
 };
 
 // The operands of one scatter walk (slices of the walked layout = rows of B).

@@ -336,6 +336,65 @@ k_group_major_ptr(int n_minor, int nnz, const int *__restrict__ tptr, const int 
     }
 }
 
+// ------------------------------------------------------------ tiled layout
+
+// Keys of the tiled layout: entry e sits at output row m and input row n of
+// the product (m = its slice and n = its index when the walked layout already
+// runs along the output (MAJOR_IS_OUT), the other way round otherwise). Input
+// rows are cut into tiles of tr rows: the entry's virtual slice is
+// (n / tr) * n_out + m and its index the row inside the tile, n % tr.
+// minor_of (the entry's slice on input) is overwritten with that index.
+template <bool MAJOR_IS_OUT>
+__global__ void __launch_bounds__(256)
+k_tile_keys(int nnz, const int *__restrict__ idx, int *__restrict__ minor_of, int tr, int n_out,
+            int *__restrict__ vkey) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
+        const int m = MAJOR_IS_OUT ? minor_of[e] : idx[e];
+        const int n = MAJOR_IS_OUT ? idx[e] : minor_of[e];
+        const int t = n / tr;
+        vkey[e] = t * n_out + m;
+        minor_of[e] = n - t * tr;
+    }
+}
+
+// tptr[b] = the first position of key b in the sorted keys, or the position
+// of the next larger key (nnz past the last): the bins in (keys[e-1], keys[e]]
+// all start at e.
+__global__ void __launch_bounds__(256)
+k_bin_starts(int nnz, const uint32_t *__restrict__ keys, int n_bins, int *__restrict__ tptr) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e <= nnz; e += stride) {
+        const int lo = e == 0 ? 0 : (int)keys[e - 1] + 1;
+        const int hi = e == nnz ? n_bins : (int)keys[e];
+        for (int b = lo; b <= hi; ++b) tptr[b] = e;
+    }
+}
+
+// out[k] = sum over t = 0 .. tiles-1, in that order, of part[t * n + k]: the
+// tiles' partial rows of a tiled walk, added in a fixed order. A thread per
+// element issues the loads of 32 tiles at once before adding them, so the
+// short kernel is not a chain of dependent load latencies.
+__global__ void __launch_bounds__(256)
+k_tile_sum(const float *__restrict__ part, float *__restrict__ out, int tiles, size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) {
+        float a = 0.f;
+        for (int t0 = 0; t0 < tiles; t0 += 32) {
+            float x[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j)
+                x[j] = t0 + j < tiles ? __builtin_nontemporal_load(part + (size_t)(t0 + j) * n + k)
+                                      : 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                if (t0 + j < tiles) a = (t0 + j == 0) ? x[j] : a + x[j];
+            }
+        }
+        out[k] = a;
+    }
+}
+
 // ----------------------------------------------------------- utilities
 
 // Fill n bytes (a multiple of 4) at p with zeros; p is 4-byte aligned.

@@ -51,9 +51,31 @@ namespace {
 
 std::atomic<uint64_t> g_next_id{1};
 
-// Workspaces holding a built opposite layout: ws address -> (handle id, dir).
+// Workspaces holding a built layout: ws address -> what it holds (handle id,
+// direction, and the tile rows of a tiled layout, 0 for the opposite layout).
+struct WsKey {
+    uint64_t id;
+    int dir;
+    int tr;
+    bool operator==(const WsKey &o) const { return id == o.id && dir == o.dir && tr == o.tr; }
+};
 std::mutex g_ws_mutex;
-std::unordered_map<const void *, std::pair<uint64_t, int>> g_ws_cache;
+std::unordered_map<const void *, WsKey> g_ws_cache;
+
+// True when ws already holds `want`; otherwise records it as holding it (the
+// caller builds it next, and drops the record if that fails).
+bool ws_claim(void *ws, const WsKey &want) {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    auto it = g_ws_cache.find(ws);
+    if (it != g_ws_cache.end() && it->second == want) return true;
+    g_ws_cache[ws] = want;
+    return false;
+}
+
+void ws_drop(void *ws) {
+    std::lock_guard<std::mutex> lk(g_ws_mutex);
+    g_ws_cache.erase(ws);
+}
 
 struct DeviceInfo {
     int n_cu = 0;
@@ -215,8 +237,10 @@ void launch_zero(void *p, size_t bytes, hipStream_t s) {
 template <typename T>
 WalkArgs<T> walk_args(int64_t n_slices, const int32_t *sptr, const int32_t *vptr, const void *vals,
                       const int32_t *idx, const void *B, void *out, int w, int64_t n_in) {
-    return WalkArgs<T>{int(n_slices), sptr, vptr, static_cast<const T *>(vals), idx,
-                       static_cast<const T *>(B), static_cast<T *>(out), w, int(n_in)};
+    WalkArgs<T> a{int(n_slices), sptr, vptr, static_cast<const T *>(vals), idx,
+                  static_cast<const T *>(B), static_cast<T *>(out), w, int(n_in)};
+    a.n_b_rows = int(n_in);
+    return a;
 }
 
 // Dispatches one aligned walk to its kernel family.
@@ -312,16 +336,19 @@ struct Bump {
     }
 };
 
-// The opposite layout (result, kept across calls) plus the sort's scratch.
+// A built layout (result, kept across calls) plus the build's scratch: the
+// opposite layout (n_bins = the handle's minor count) or a tiled one (n_bins
+// virtual slices, with a per-entry key array and the product's partial rows).
 struct OppositeWs {
     // result
-    int32_t *t_ptr = nullptr;      // n_minor + 1 (CSR row pointers / VCS major_ptr)
+    int32_t *t_ptr = nullptr;      // n_bins + 1 (CSR row pointers / VCS major_ptr)
     void *t_vals = nullptr;        // CSR: nnz values; VCS: nnz group values (worst case)
     int32_t *t_vptr = nullptr;     // VCS: nnz + 1
     int32_t *t_idx = nullptr;      // nnz
     int32_t *t_ngroups = nullptr;  // VCS: 1
+    float *partial = nullptr;      // tiled: the product's partial rows (n_bins x width)
     // scratch
-    int32_t *slice_of = nullptr, *group_of = nullptr;
+    int32_t *slice_of = nullptr, *group_of = nullptr, *vkey = nullptr;
     uint32_t *keys_a = nullptr, *keys_b = nullptr;
     int32_t *pay_a = nullptr, *pay_b = nullptr;
     int32_t *flag = nullptr, *gid = nullptr, *cnt = nullptr;
@@ -329,20 +356,25 @@ struct OppositeWs {
     size_t bytes = 0;
 };
 
-OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base) {
+OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base, int64_t n_bins = -1,
+                          int64_t partial_elems = 0) {
     OppositeWs w;
     Bump b{static_cast<char *>(base)};
-    const size_t nnz = size_t(h.nnz), nmin = size_t(h.n_minor());
+    const size_t nnz = size_t(h.nnz);
+    const size_t nb = size_t(n_bins < 0 ? h.n_minor() : n_bins);
     const bool vcs = h.layout != VSPMM_CSR;
-    w.t_ptr = b.take<int32_t>(nmin + 1);
+    const bool tiled = partial_elems > 0;
+    w.t_ptr = b.take<int32_t>(nb + 1);
     w.t_vals = b.take<char>(nnz * h.elt());
     if (vcs) {
         w.t_vptr = b.take<int32_t>(nnz + 1);
         w.t_ngroups = b.take<int32_t>(1);
     }
     w.t_idx = b.take<int32_t>(nnz);
+    if (tiled) w.partial = b.take<float>(size_t(partial_elems));
     w.slice_of = b.take<int32_t>(nnz);
     if (vcs) w.group_of = b.take<int32_t>(nnz);
+    if (tiled) w.vkey = b.take<int32_t>(nnz);
     w.keys_a = b.take<uint32_t>(nnz);
     w.keys_b = b.take<uint32_t>(nnz);
     w.pay_a = b.take<int32_t>(nnz);
@@ -351,10 +383,10 @@ OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base) {
         w.flag = b.take<int32_t>(nnz);
         w.gid = b.take<int32_t>(nnz);
     }
-    w.cnt = b.take<int32_t>(nmin + 1);
+    w.cnt = b.take<int32_t>(nb + 1);
     const size_t nblocks = (nnz + kSortTile - 1) / kSortTile;
     w.hist = b.take<int32_t>(256 * std::max<size_t>(nblocks, 1));
-    const size_t scan_len = std::max({nnz, nmin + 1, 256 * std::max<size_t>(nblocks, 1)});
+    const size_t scan_len = std::max({nnz, nb + 1, 256 * std::max<size_t>(nblocks, 1)});
     w.bsums = b.take<int32_t>((scan_len + kScanTile - 1) / kScanTile + 1);
     w.scalars = b.take<int32_t>(4);
     w.bytes = align256(b.off);
@@ -479,6 +511,129 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
                        tptr, w.gid, n_groups, t_major_ptr, t_value_ptr, t_n_groups);
 }
 
+// ------------------------------------------------------------ tiled layout
+
+// A tiled walk: the product's input rows (B's rows) are cut into tiles of tr
+// rows, each small enough for one CU's LDS next to the walk's own LDS, and
+// every entry goes to the virtual slice (tile, output row). The virtual
+// slices form a VCS of tiles x n_out slices with tile-local indices, walked by
+// k_vcs_rows with each block staging its tile of B; the tiles' partial rows
+// are then added in tile order. Worth it only when B does not fit in LDS
+// whole and the virtual slices stay long enough (at least 32 entries on
+// average) that the partial rows cost little next to the entries.
+struct TilePlan {
+    bool ok = false;
+    int tr = 0;          // B rows per tile (a multiple of 4)
+    int tiles = 0;
+    int64_t n_out = 0;   // output rows (virtual slices per tile)
+    int64_t n_in = 0;    // B's rows
+    Plan pl;             // the k_vcs_rows launch over the tiled layout
+    int64_t n_bins() const { return int64_t(tiles) * n_out; }
+};
+
+TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool split_matrix,
+                   const void *B, const void *part) {
+    TilePlan tp;
+    if (h.layout == VSPMM_CSR || h.dtype != VSPMM_F32 || w <= 0 || h.nnz <= 0) return tp;
+    n_cu = std::max(n_cu, 1);
+    const int64_t no = n_out(h, dir), ni = n_in(h, dir);
+    const size_t row_bytes = size_t(w) * 4;
+    const size_t fixed = size_t(16) * kRowsWaveLds + 16;
+    // B fits whole: the plain walks stage it already
+    if (size_t(ni) * row_bytes + fixed + 8 * size_t(rows_header_cap(int(std::min<int64_t>(no, kI32Max)), n_cu)) <= kLdsMax)
+        return tp;
+    const size_t header_margin = 8 * 1024;  // the block's slice-header table
+    int64_t tr = int64_t((kLdsMax - fixed - header_margin) / row_bytes) & ~int64_t(3);
+    if (tr < 64) return tp;  // rows too wide for a useful tile
+    const int64_t tiles = (ni + tr - 1) / tr;
+    tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);  // balanced tiles
+    const int64_t nv = tiles * no;
+    if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
+    const int64_t mean = h.nnz / nv;
+    if (mean < 32 || mean >= kLongMean) return tp;
+    const int64_t bpt = std::max<int64_t>(1, n_cu / tiles);
+    const int64_t grid = tiles * bpt;
+    const size_t b_al = (size_t(tr) * row_bytes + 15) & ~size_t(15);
+    const size_t lds = b_al + fixed + 8 * size_t(rows_header_cap(int(nv), int(grid)));
+    if (lds > kLdsMax) return tp;
+    Plan pl = make_plan(nv, h.nnz, w, 4, split_matrix, h.force_group, B, part, n_cu, tr, true);
+    if (pl.kind != kShort || pl.R != 1) return tp;
+    pl.lds = true;
+    pl.lds_bytes = lds;
+    pl.block = 1024;
+    pl.grid = int(grid);
+    tp.ok = true;
+    tp.tr = int(tr);
+    tp.tiles = int(tiles);
+    tp.n_out = no;
+    tp.n_in = ni;
+    tp.pl = pl;
+    return tp;
+}
+
+// Workspace bytes of a tiled product at width w.
+size_t tiled_ws_bytes(const vspmm_matrix_s &h, const TilePlan &tp, int64_t w) {
+    return carve_opposite(h, nullptr, tp.n_bins(), tp.n_bins() * w).bytes;
+}
+
+// Builds the tiled layout of a VCS handle into w: entries keyed by virtual
+// slice, each slice's entries grouped by value (stable radix sorts by value,
+// then by virtual slice), tile-local indices.
+void build_tiled(const vspmm_matrix_s &h, const OppositeWs &w, const TilePlan &tp,
+                 bool major_is_out, int n_cu, hipStream_t s) {
+    const int64_t nnz = h.nnz, nb = tp.n_bins();
+    const int grid = grid_for(nnz, n_cu);
+    const float *vals = static_cast<const float *>(h.vals);
+    int32_t *n_groups = w.scalars;
+    expand_slices(h, w, n_cu, s);
+    if (major_is_out)
+        hipLaunchKernelGGL(k_tile_keys<true>, dim3(grid), dim3(256), 0, s, int(nnz), h.idx,
+                           w.slice_of, tp.tr, int(tp.n_out), w.vkey);
+    else
+        hipLaunchKernelGGL(k_tile_keys<false>, dim3(grid), dim3(256), 0, s, int(nnz), h.idx,
+                           w.slice_of, tp.tr, int(tp.n_out), w.vkey);
+    uint32_t *ka = w.keys_a, *kb = w.keys_b;
+    int32_t *pa = w.pay_a, *pb = w.pay_b;
+    hipLaunchKernelGGL(k_value_keys, dim3(grid), dim3(256), 0, s, int(nnz), w.group_of, vals, ka,
+                       pa);
+    radix_sort(&ka, &pa, &kb, &pb, nnz, 32, w.hist, w.bsums, s);
+    hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.vkey, ka);
+    radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(nb), w.hist, w.bsums, s);
+    hipLaunchKernelGGL(k_bin_starts, dim3(grid_for(nnz + 1, n_cu)), dim3(256), 0, s, int(nnz),
+                       ka, int(nb), w.cnt);
+    hipLaunchKernelGGL(k_group_flags, dim3(grid), dim3(256), 0, s, int(nnz), pa, ka, w.group_of,
+                       vals, w.flag);
+    scan_excl(w.flag, w.gid, nnz, w.bsums, n_groups, s);
+    hipLaunchKernelGGL(k_group_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
+                       w.group_of, vals, w.flag, w.gid, (float *)w.t_vals, w.t_vptr, w.t_idx);
+    hipLaunchKernelGGL(k_group_major_ptr, dim3(grid_for(nb + 1, n_cu)), dim3(256), 0, s, int(nb),
+                       int(nnz), w.cnt, w.gid, n_groups, w.t_ptr, w.t_vptr, w.t_ngroups);
+}
+
+// The tiled product: build (or reuse) the layout in ws, walk it, add the
+// tiles' partial rows into out.
+vspmm_status run_tiled(const vspmm_matrix_s &h, const TilePlan &tp, const void *B, void *out,
+                       int w, int dir, void *ws, int n_cu, hipStream_t s) {
+    const OppositeWs wl = carve_opposite(h, ws, tp.n_bins(), tp.n_bins() * w);
+    if (!ws_claim(ws, WsKey{h.id, dir, tp.tr})) {
+        build_tiled(h, wl, tp, is_aligned(h, dir), n_cu, s);
+        if (vspmm_status st = hip_status()) {
+            ws_drop(ws);
+            return st;
+        }
+    }
+    WalkArgs<float> a = walk_args<float>(tp.n_bins(), wl.t_ptr, wl.t_vptr, wl.t_vals, wl.t_idx,
+                                         B, wl.partial, w, tp.tr);
+    a.tiles = tp.tiles;
+    a.n_b_rows = int(tp.n_in);
+    launch_aligned<float>(true, tp.pl, a, s);
+    const size_t n = size_t(tp.n_out) * size_t(w);
+    const int grid = int(std::min<size_t>((n + 255) / 256, size_t(n_cu) * 16));
+    hipLaunchKernelGGL(k_tile_sum, dim3(grid), dim3(256), 0, s, wl.partial, (float *)out,
+                       tp.tiles, n);
+    return hip_status();
+}
+
 // ---------------------------------------------------------------- checks
 
 vspmm_status check_handle(const vspmm_matrix_s *h) { return h ? VSPMM_OK : VSPMM_ERR_NULL; }
@@ -513,6 +668,11 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
         return hip_status();
     }
+    if (mode == VSPMM_DETERMINISTIC && ws && aligned(ws, 256)) {
+        const TilePlan tp = tile_plan(h, dir, w, n_cu, split_matrix, B, ws);
+        if (tp.ok && ws_bytes >= tiled_ws_bytes(h, tp, w))
+            return run_tiled(h, tp, B, out, w, dir, ws, n_cu, s);
+    }
     if (is_aligned(h, dir)) {
         const int64_t ni = h.n_minor();
         const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
@@ -536,14 +696,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     const OppositeWs need = carve_opposite(h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
     const OppositeWs wl = carve_opposite(h, ws);
-    bool built;
-    {
-        std::lock_guard<std::mutex> lk(g_ws_mutex);
-        auto it = g_ws_cache.find(ws);
-        built = it != g_ws_cache.end() && it->second.first == h.id && it->second.second == dir;
-        if (!built) g_ws_cache[ws] = {h.id, dir};
-    }
-    if (!built) {
+    if (!ws_claim(ws, WsKey{h.id, dir, 0})) {
         if (vcs)
             build_regroup(h, wl, wl.t_ptr, (float *)wl.t_vals, wl.t_vptr, wl.t_idx, wl.t_ngroups,
                           n_cu, s);
@@ -551,8 +704,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
             build_transpose(h, wl, wl.t_ptr, wl.t_idx, wl.t_vals, n_cu, s);
         st = hip_status();
         if (st) {
-            std::lock_guard<std::mutex> lk(g_ws_mutex);
-            g_ws_cache.erase(ws);
+            ws_drop(ws);
             return st;
         }
     }
@@ -679,7 +831,7 @@ vspmm_status vspmm_destroy(vspmm_matrix h) {
     {
         std::lock_guard<std::mutex> lk(g_ws_mutex);
         for (auto it = g_ws_cache.begin(); it != g_ws_cache.end();) {
-            if (it->second.first == h->id) it = g_ws_cache.erase(it);
+            if (it->second.id == h->id) it = g_ws_cache.erase(it);
             else ++it;
         }
     }
@@ -713,8 +865,20 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
 }
 
 vspmm_status vspmm_workspace_invalidate(void *ws) {
-    std::lock_guard<std::mutex> lk(g_ws_mutex);
-    g_ws_cache.erase(ws);
+    ws_drop(ws);
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
+                                        int64_t width, size_t *bytes) {
+    if (vspmm_status st = vspmm_workspace_size(h, dir, mode, bytes)) return st;
+    if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
+    if (mode != VSPMM_DETERMINISTIC) return VSPMM_OK;
+    const DeviceInfo di = device_info(h->device);
+    const bool split_matrix = (h->flags & VSPMM_SPLIT_MATRIX) != 0;
+    alignas(256) static const float probe[64] = {};
+    const TilePlan tp = tile_plan(*h, dir, width, di.ok ? di.n_cu : 256, split_matrix, probe, probe);
+    if (tp.ok) *bytes = tiled_ws_bytes(*h, tp, width);
     return VSPMM_OK;
 }
 
@@ -798,7 +962,7 @@ vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_byt
 vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
                              vspmm_mode mode, int32_t *entry_lanes, int32_t *width_lanes,
                              int32_t *vec, int32_t *slices_per_wave, int32_t *lds_staged,
-                             int32_t *kernel) {
+                             int32_t *kernel, int32_t *tiles) {
     if (vspmm_status st = check_handle(h)) return st;
     if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
     if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
@@ -811,13 +975,18 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     const int64_t ns = al || scatter ? h->n_major() : h->n_minor();
     const int64_t ni = al || scatter ? h->n_minor() : h->n_major();
     // alignment of the caller's buffers is unknown here: assume 16-byte aligned
-    alignas(16) static const float probe[4] = {0, 0, 0, 0};
+    alignas(256) static const float probe[64] = {};
     const DeviceInfo di = device_info(h->device);
     const int n_cu = di.ok ? di.n_cu : 256;
-    const Plan pl = scatter ? scatter_plan(h->nnz, width, n_out(*h, dir), h->elt(), n_cu,
-                                           h->force_group)
-                            : make_plan(ns, h->nnz, width, h->elt(), split_matrix,
-                                        h->force_group, probe, probe, n_cu, ni, vcs);
+    const TilePlan tp = mode == VSPMM_DETERMINISTIC
+                            ? tile_plan(*h, dir, width, n_cu, split_matrix, probe, probe)
+                            : TilePlan{};
+    const Plan pl = tp.ok ? tp.pl
+                    : scatter ? scatter_plan(h->nnz, width, n_out(*h, dir), h->elt(), n_cu,
+                                             h->force_group)
+                              : make_plan(ns, h->nnz, width, h->elt(), split_matrix,
+                                          h->force_group, probe, probe, n_cu, ni, vcs);
+    if (tiles) *tiles = tp.ok ? tp.tiles : 0;
     if (entry_lanes) *entry_lanes = 1 << pl.sp.log_g;
     if (width_lanes) *width_lanes = 1 << pl.sp.log_ww;
     if (vec) *vec = pl.vec;

@@ -412,11 +412,17 @@ __device__ __forceinline__ void rows_load(const RowRound &r, int (&W)[NWR], int 
 // into the CU's LDS first and gathered from there. Dynamic LDS: [B, 16-byte
 // aligned][per wave: kRowsWaveLds bytes of marks and group values][header
 // table: 2 x hcap ints][unit counter].
+//
+// Tiled (tiles > 1): the slices are `tiles` runs of n_slices / tiles, run t
+// reading B's rows [t * n_in, t * n_in + n_in) (n_in rows per tile, the last
+// tile cut at n_b_rows) with tile-local indices. The grid is tiles x bpt
+// blocks, block b taking part b % bpt of run b / bpt and staging its tile.
 template <int LOG_WW, bool LDS_B, int VEC>
 __global__ void __launch_bounds__(1024)
 k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
            const float *__restrict__ vals, const int *__restrict__ idx,
-           const float *__restrict__ B, float *__restrict__ out, int w, int n_in) {
+           const float *__restrict__ B, float *__restrict__ out, int w, int n_in, int tiles,
+           int n_b_rows) {
     using T = float;
     using Sum = SlotSum<LOG_WW, VEC>;
     using Gm = Geo<LOG_WW, VEC>;
@@ -438,8 +444,13 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     int *hp_l = reinterpret_cast<int *>(smem + b_bytes + (size_t)waves * kRowsWaveLds);
     int *he_l = hp_l + hcap;
     int *unit_ctr = he_l + hcap;
-    const int bb = (int)((long long)blockIdx.x * n_slices / gridDim.x);
-    const int be = (int)((long long)(blockIdx.x + 1) * n_slices / gridDim.x);
+    const int bpt = gridDim.x / tiles;  // blocks per tile
+    const int tile = blockIdx.x / bpt, part = blockIdx.x - tile * bpt;
+    const int n_run = n_slices / tiles;  // slices per tile
+    const int bb = tile * n_run + (int)((long long)part * n_run / bpt);
+    const int be = tile * n_run + (int)((long long)(part + 1) * n_run / bpt);
+    B += (size_t)tile * n_in * w;  // this tile's rows of B
+    const int b_rows = min(n_in, n_b_rows - tile * n_in);
     const int nch = (be - bb + CH - 1) / CH;
     const int npass = (w + chunk_w - 1) / chunk_w;
     const int nunits = nch * npass;
@@ -447,7 +458,7 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
 
     // B into LDS first, as direct global->LDS copies (16 bytes per lane, 1 KB
     // per wave instruction; no registers).
-    const size_t b_el = (size_t)n_in * w;
+    const size_t b_el = (size_t)b_rows * w;
     const bool b_dma = LDS_B && (b_el * sizeof(T)) % 16 == 0 && ((uintptr_t)B % 16) == 0;
     if constexpr (LDS_B) {
         if (b_dma) {

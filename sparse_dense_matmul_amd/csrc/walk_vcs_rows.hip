@@ -17,10 +17,12 @@ void launch_vcs_rows(const Plan &pl, const WalkArgs<float> &a, hipStream_t s) {
         if (pl.lds) {                                                                            \
             allow_lds(reinterpret_cast<const void *>(&k_vcs_rows<LW, true, VEC>));               \
             hipLaunchKernelGGL((k_vcs_rows<LW, true, VEC>), g, b, pl.lds_bytes, s, a.n_slices,   \
-                               a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in);          \
+                               a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, a.tiles,   \
+                               a.n_b_rows);                                                 \
         } else {                                                                                 \
             hipLaunchKernelGGL((k_vcs_rows<LW, false, VEC>), g, b, pl.lds_bytes, s, a.n_slices,  \
-                               a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in);          \
+                               a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, a.tiles,   \
+                               a.n_b_rows);                                                 \
         }                                                                                        \
     } while (0)
     switch (pl.sp.log_ww) {

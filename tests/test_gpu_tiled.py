@@ -1,0 +1,124 @@
+"""The tiled schedule of deterministic mode: B's rows cut into tiles that fit
+in a CU's LDS, each output row's entries split by tile and grouped by value
+per (tile, output row), partial rows added in tile order. Checked on the
+60,000 x 2,000 count matrix in both directions whose dense input (60,000 rows)
+is too large for LDS, at widths where tiling applies (8, 16, 32) and where it
+does not (1, 64: the untiled paths run instead); on a matrix whose last tile
+is short and holds runs of empty groups; across workspaces and widths sharing
+one workspace; and against the float64 oracle, exactly on integer data."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import check_close, dims, need_gpu, to_dev, vcs_handle, with_empty_groups
+
+pytestmark = pytest.mark.gpu
+
+# (layout, direction) pairs whose input rows are the 60,000 matrix rows
+LONG = [("vcsr", "BA"), ("vcsc", "BA")]
+
+
+@pytest.fixture(scope="module")
+def count60k():
+    t = W.count_60k()
+    return {"vcsr": W.build_vcs(t, "vcsr"), "vcsc": W.build_vcs(t, "vcsc")}
+
+
+@pytest.fixture(scope="module")
+def ragged():
+    """50,003 x 1,500, Poisson(60) per row: the last of 23 tiles is short;
+    runs of 70 empty groups inserted in some slices."""
+    t = W.count_matrix(50_003, 1_500, 60.0, 255, W.rng_for(43))
+    out = {lay: W.build_vcs(t, lay) for lay in ("vcsr", "vcsc")}
+    out["vcsc_empty"] = with_empty_groups(out["vcsc"], W.rng_for(44), n_rows=10, per_row=70)
+    return out
+
+
+def run_det(A, L, direction, width, seed=0, ws=None, integer=False):
+    dev = A.device
+    rows, _ = dims(L, direction)
+    B = (W.dense_int(np.random.default_rng(seed), rows, width) if integer else
+         W.dense_normal(np.random.default_rng(seed), rows, width))
+    if ws is None:
+        ws = A.workspace(direction, "deterministic", width)
+    out = A.spmm(to_dev(B, dev), direction, mode="deterministic", workspace=ws)
+    return B, out, ws
+
+
+@pytest.mark.parametrize("width", [8, 16, 32])
+@pytest.mark.parametrize("layout,direction", LONG)
+def test_tiled_parity(orc, count60k, layout, direction, width):
+    dev = need_gpu()
+    L = count60k[layout]
+    A = vcs_handle(L, dev)
+    info = A.plan_info(width, direction, "deterministic")
+    assert info["tiles"] > 1 and info["kernel_name"] == "k_vcs_rows" and info["lds_staged"] == 1
+    B, out, ws = run_det(A, L, direction, width)
+    check_close(orc, L, direction, B, out, where=f"tiled {layout} {direction} w={width}")
+    again = A.spmm(to_dev(B, dev), direction, mode="deterministic", workspace=ws)
+    assert torch.equal(again.view(torch.int32), out.view(torch.int32))
+    # a second workspace builds the same schedule: the same bits
+    _, other, _ = run_det(A, L, direction, width)
+    assert torch.equal(other.view(torch.int32), out.view(torch.int32))
+
+
+@pytest.mark.parametrize("width", [1, 64])
+@pytest.mark.parametrize("layout,direction", LONG)
+def test_untiled_widths(orc, count60k, layout, direction, width):
+    """Width 1 (two tiles would leave too few slices) and 64 (slices too
+    short): no tiled schedule; the workspace asked for serves the plain paths."""
+    dev = need_gpu()
+    L = count60k[layout]
+    A = vcs_handle(L, dev)
+    assert A.plan_info(width, direction, "deterministic")["tiles"] == 0
+    B, out, _ = run_det(A, L, direction, width)
+    check_close(orc, L, direction, B, out, where=f"untiled {layout} {direction} w={width}")
+
+
+@pytest.mark.parametrize("name,direction", [("vcsr", "BA"), ("vcsc", "BA"), ("vcsc_empty", "BA")])
+def test_tiled_ragged(orc, ragged, name, direction):
+    dev = need_gpu()
+    L = ragged[name]
+    A = vcs_handle(L, dev)
+    assert A.plan_info(16, direction, "deterministic")["tiles"] > 1
+    for integer in (False, True):
+        B, out, _ = run_det(A, L, direction, 16, seed=5, integer=integer)
+        if integer:
+            want = orc.spmm(L, direction, B)
+            assert np.array_equal(out.cpu().numpy().astype(np.float64), want), name
+        else:
+            check_close(orc, L, direction, B, out, where=f"ragged {name}")
+
+
+def test_workspace_shared_across_widths(orc, count60k):
+    """One workspace large enough for both widths: the schedule is rebuilt when
+    the tile size changes and reused when it does not."""
+    dev = need_gpu()
+    L = count60k["vcsr"]
+    A = vcs_handle(L, dev)
+    n = max(A.workspace_size("BA", "deterministic", w) for w in (8, 16))
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    first = {}
+    for width in (16, 8, 16, 8):
+        B, out, _ = run_det(A, L, "BA", width, seed=width, ws=ws)
+        if width in first:
+            assert torch.equal(out.view(torch.int32), first[width].view(torch.int32))
+        else:
+            check_close(orc, L, "BA", B, out, where=f"shared ws w={width}")
+            first[width] = out.clone()
+
+
+def test_small_workspace_falls_back(orc, count60k):
+    """A workspace sized without the width holds only the opposite layout: the
+    misaligned product takes the untiled two-pass path, the aligned one the
+    plain walk; both stay correct."""
+    dev = need_gpu()
+    for layout in ("vcsr", "vcsc"):
+        L = count60k[layout]
+        A = vcs_handle(L, dev)
+        small = A.workspace("BA", "deterministic")
+        assert small.numel() < A.workspace_size("BA", "deterministic", 16)
+        B, out, _ = run_det(A, L, "BA", 16, ws=small)
+        check_close(orc, L, "BA", B, out, where=f"fallback {layout}")
