@@ -545,8 +545,12 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     const size_t header_margin = 8 * 1024;  // the block's slice-header table
     int64_t tr = int64_t((kLdsMax - fixed - header_margin) / row_bytes) & ~int64_t(3);
     if (tr < 64) return tp;  // rows too wide for a useful tile
-    const int64_t tiles = (ni + tr - 1) / tr;
+    int64_t tiles = (ni + tr - 1) / tr;
+    // a multiple of 8 tiles lets each XCD (8 on the chip) own whole tiles,
+    // so a tile of B is fetched into one XCD's L2 instead of all eight
+    if (tiles >= 4) tiles = (tiles + 7) / 8 * 8;
     tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);  // balanced tiles
+    tiles = (ni + tr - 1) / tr;                           // (rounding tr may drop one)
     const int64_t nv = tiles * no;
     if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
     const int64_t mean = h.nnz / nv;

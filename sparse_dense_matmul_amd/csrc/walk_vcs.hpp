@@ -416,7 +416,8 @@ __device__ __forceinline__ void rows_load(const RowRound &r, int (&W)[NWR], int 
 // Tiled (tiles > 1): the slices are `tiles` runs of n_slices / tiles, run t
 // reading B's rows [t * n_in, t * n_in + n_in) (n_in rows per tile, the last
 // tile cut at n_b_rows) with tile-local indices. The grid is tiles x bpt
-// blocks, block b taking part b % bpt of run b / bpt and staging its tile.
+// blocks, each taking one of the bpt parts of one run and staging its tile;
+// with a multiple of 8 tiles the blocks of a tile share an XCD.
 template <int LOG_WW, bool LDS_B, int VEC>
 __global__ void __launch_bounds__(1024)
 k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
@@ -445,7 +446,14 @@ k_vcs_rows(int n_slices, const int *__restrict__ sptr, const int *__restrict__ v
     int *he_l = hp_l + hcap;
     int *unit_ctr = he_l + hcap;
     const int bpt = gridDim.x / tiles;  // blocks per tile
-    const int tile = blockIdx.x / bpt, part = blockIdx.x - tile * bpt;
+    int tile = blockIdx.x / bpt, part = blockIdx.x - tile * bpt;
+    if (tiles % 8 == 0) {
+        // blocks go to the 8 XCDs round robin (block b to XCD b % 8): give
+        // each XCD whole tiles, so a tile of B is fetched into one L2 only
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        tile = x * (tiles >> 3) + j / bpt;
+        part = j - (j / bpt) * bpt;
+    }
     const int n_run = n_slices / tiles;  // slices per tile
     const int bb = tile * n_run + (int)((long long)part * n_run / bpt);
     const int be = tile * n_run + (int)((long long)(part + 1) * n_run / bpt);
