@@ -151,7 +151,7 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * entries are split by tile, every (tile, output row) part grouped by value
  * as in the pages' value-grouped layouts. The product walks it with each
  * block's tile of B in LDS, writes one partial row per (tile, output row) into
- * ws and adds them in tile order; it repeats bit for bit. The copy is reused
+ * ws and adds them in a fixed order; it repeats bit for bit. The copy is reused
  * like the opposite layout (it also depends on the tile size, which follows
  * the width). A smaller ws falls back to the path above (aligned: the plain
  * walk, ws unused).

@@ -239,32 +239,6 @@ k_gather_index(int nnz, const int *__restrict__ pay, const int *__restrict__ idx
         keys[e] = (uint32_t)idx[pay[e]];
 }
 
-// Entries per new slice (cnt zeroed beforehand).
-__global__ void __launch_bounds__(256)
-k_count(int nnz, const int *__restrict__ idx, int *__restrict__ cnt) {
-    const int stride = gridDim.x * blockDim.x;
-    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride)
-        atomicAdd(&cnt[idx[p]], 1);
-}
-
-// The same with a per-block histogram in LDS (n_bins ints of dynamic LDS),
-// for few bins hit many times per block: each block counts a contiguous range
-// of entries locally and adds its non-zero bins to cnt once.
-__global__ void __launch_bounds__(1024)
-k_count_lds(int nnz, const int *__restrict__ idx, int *__restrict__ cnt, int n_bins) {
-    extern __shared__ int hist[];
-    for (int b = threadIdx.x; b < n_bins; b += blockDim.x) hist[b] = 0;
-    __syncthreads();
-    const int p0 = (int)((long long)blockIdx.x * nnz / gridDim.x);
-    const int p1 = (int)((long long)(blockIdx.x + 1) * nnz / gridDim.x);
-    for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&hist[idx[p]], 1);
-    __syncthreads();
-    for (int b = threadIdx.x; b < n_bins; b += blockDim.x) {
-        const int c = hist[b];
-        if (c) atomicAdd(&cnt[b], c);
-    }
-}
-
 // ------------------------------------------------------------- transpose
 
 template <typename T>
@@ -371,27 +345,42 @@ k_bin_starts(int nnz, const uint32_t *__restrict__ keys, int n_bins, int *__rest
     }
 }
 
-// out[k] = sum over t = 0 .. tiles-1, in that order, of part[t * n + k]: the
-// tiles' partial rows of a tiled walk, added in a fixed order. A thread per
-// element issues the loads of 32 tiles at once before adding them, so the
-// short kernel is not a chain of dependent load latencies.
+// out[k] = the sum over t = 0 .. tiles-1 of part[t * n + k]: the tiles'
+// partial rows of a tiled walk, added in a fixed order. A block of 256 threads
+// takes 64 consecutive elements; its four thread quarters each add a run of
+// consecutive tiles in order (all of a run's loads issued before its adds),
+// then quarter 0 adds the four runs in order. Spreading an element over four
+// threads keeps the short kernel from being one long chain of load latencies.
 __global__ void __launch_bounds__(256)
 k_tile_sum(const float *__restrict__ part, float *__restrict__ out, int tiles, size_t n) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) {
+    __shared__ float run[4][64];
+    const int e = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int per = (tiles + 3) >> 2;  // tiles per run
+    const int t0 = q * per, t1 = min(tiles, t0 + per);
+    for (size_t base = (size_t)blockIdx.x * 64; base < n; base += (size_t)gridDim.x * 64) {
+        const size_t k = base + e;
         float a = 0.f;
-        for (int t0 = 0; t0 < tiles; t0 += 32) {
-            float x[32];
+        if (k < n) {
+            for (int tb = t0; tb < t1; tb += 16) {
+                float x[16];
 #pragma unroll
-            for (int j = 0; j < 32; ++j)
-                x[j] = t0 + j < tiles ? __builtin_nontemporal_load(part + (size_t)(t0 + j) * n + k)
-                                      : 0.f;
+                for (int j = 0; j < 16; ++j)
+                    x[j] = tb + j < t1 ? __builtin_nontemporal_load(part + (size_t)(tb + j) * n + k) : 0.f;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                if (t0 + j < tiles) a = (t0 + j == 0) ? x[j] : a + x[j];
+                for (int j = 0; j < 16; ++j) {
+                    if (tb + j < t1) a = (tb + j == t0) ? x[j] : a + x[j];
+                }
             }
         }
-        out[k] = a;
+        run[q][e] = a;
+        __syncthreads();
+        if (q == 0 && k < n) {
+            float s = run[0][e];
+            for (int r = 1; r < 4; ++r)
+                if (r * per < tiles) s += run[r][e];
+            out[k] = s;
+        }
+        __syncthreads();
     }
 }
 

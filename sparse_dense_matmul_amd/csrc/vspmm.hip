@@ -429,24 +429,6 @@ int grid_for(int64_t n, int n_cu) {
     return int(std::max<int64_t>(1, std::min<int64_t>(want, int64_t(std::max(n_cu, 1)) * 16)));
 }
 
-// Entries per new slice and their exclusive scan (tptr, n_minor + 1 ints).
-void count_and_scan(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *tptr, int n_cu,
-                    hipStream_t s) {
-    const int64_t nmin = h.n_minor();
-    launch_zero(w.cnt, size_t(nmin) * 4, s);
-    const int64_t blocks = std::max(n_cu, 1);
-    if (h.nnz > 0 && nmin <= 32768 && nmin * 4 <= h.nnz / blocks) {
-        // few bins, each hit many times per block: count in LDS first
-        allow_lds(reinterpret_cast<const void *>(&k_count_lds));
-        hipLaunchKernelGGL(k_count_lds, dim3(unsigned(blocks)), dim3(1024), size_t(nmin) * 4, s,
-                           int(h.nnz), h.idx, w.cnt, int(nmin));
-    } else if (h.nnz > 0) {
-        hipLaunchKernelGGL(k_count, dim3(grid_for(h.nnz, n_cu)), dim3(256), 0, s, int(h.nnz),
-                           h.idx, w.cnt);
-    }
-    scan_excl(w.cnt, tptr, nmin, w.bsums, tptr + nmin, s);
-}
-
 void expand_slices(const vspmm_matrix_s &h, const OppositeWs &w, int n_cu, hipStream_t s) {
     const int64_t nmaj = h.n_major();
     if (nmaj <= 0 || h.nnz <= 0) return;
@@ -459,17 +441,29 @@ void expand_slices(const vspmm_matrix_s &h, const OppositeWs &w, int n_cu, hipSt
                            h.vptr, w.slice_of, w.group_of);
 }
 
+// tptr[b] (b = 0 .. n_bins) = the first position of bin b in the sorted keys:
+// the new slices' entry offsets, read off the sort instead of counted with
+// atomics (nnz may be 0: then every offset is 0 and keys is not read).
+void bin_starts(const uint32_t *keys, int64_t nnz, int64_t n_bins, int32_t *tptr, int n_cu,
+                hipStream_t s) {
+    hipLaunchKernelGGL(k_bin_starts, dim3(grid_for(nnz + 1, n_cu)), dim3(256), 0, s, int(nnz),
+                       keys, int(n_bins), tptr);
+}
+
 // The exact CSR transpose into (t_ptr, t_idx, t_val).
 void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_ptr,
                      int32_t *t_idx, void *t_val, int n_cu, hipStream_t s) {
-    count_and_scan(h, w, t_ptr, n_cu, s);
-    if (h.nnz <= 0) return;
+    if (h.nnz <= 0) {
+        bin_starts(nullptr, 0, h.n_minor(), t_ptr, n_cu, s);
+        return;
+    }
     expand_slices(h, w, n_cu, s);
     const int grid = grid_for(h.nnz, n_cu);
     uint32_t *ka = w.keys_a, *kb = w.keys_b;
     int32_t *pa = w.pay_a, *pb = w.pay_b;
     hipLaunchKernelGGL(k_index_keys, dim3(grid), dim3(256), 0, s, int(h.nnz), h.idx, ka, pa);
     radix_sort(&ka, &pa, &kb, &pb, h.nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
+    bin_starts(ka, h.nnz, h.n_minor(), t_ptr, n_cu, s);
     if (h.dtype == VSPMM_F64)
         hipLaunchKernelGGL(k_transpose_emit<double>, dim3(grid), dim3(256), 0, s, int(h.nnz), pa,
                            w.slice_of, (const double *)h.vals, t_idx, (double *)t_val);
@@ -483,8 +477,7 @@ void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_pt
 void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_major_ptr,
                    float *t_values, int32_t *t_value_ptr, int32_t *t_indices,
                    int32_t *t_n_groups, int n_cu, hipStream_t s) {
-    int32_t *tptr = w.cnt;  // entry offsets of the new slices (in place over the counts)
-    count_and_scan(h, w, tptr, n_cu, s);
+    int32_t *tptr = w.cnt;  // entry offsets of the new slices
     const int64_t nnz = h.nnz;
     const int grid = grid_for(std::max<int64_t>(nnz, 1), n_cu);
     int32_t *n_groups = w.scalars;
@@ -497,6 +490,7 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
         radix_sort(&ka, &pa, &kb, &pb, nnz, 32, w.hist, w.bsums, s);
         hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, h.idx, ka);
         radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
+        bin_starts(ka, nnz, h.n_minor(), tptr, n_cu, s);
         hipLaunchKernelGGL(k_group_flags, dim3(grid), dim3(256), 0, s, int(nnz), pa, ka,
                            w.group_of, (const float *)h.vals, w.flag);
         scan_excl(w.flag, w.gid, nnz, w.bsums, n_groups, s);
@@ -505,6 +499,7 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
                            t_value_ptr, t_indices);
     } else {
         launch_zero(n_groups, 4, s);
+        bin_starts(nullptr, 0, h.n_minor(), tptr, n_cu, s);
     }
     const int g2 = grid_for(h.n_minor() + 1, n_cu);
     hipLaunchKernelGGL(k_group_major_ptr, dim3(g2), dim3(256), 0, s, int(h.n_minor()), int(nnz),
@@ -518,7 +513,7 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
 // every entry goes to the virtual slice (tile, output row). The virtual
 // slices form a VCS of tiles x n_out slices with tile-local indices, walked by
 // k_vcs_rows with each block staging its tile of B; the tiles' partial rows
-// are then added in tile order. Worth it only when B does not fit in LDS
+// are then added in a fixed order. Worth it only when B does not fit in LDS
 // whole and the virtual slices stay long enough (at least 32 entries on
 // average) that the partial rows cost little next to the entries.
 struct TilePlan {
@@ -603,8 +598,7 @@ void build_tiled(const vspmm_matrix_s &h, const OppositeWs &w, const TilePlan &t
     radix_sort(&ka, &pa, &kb, &pb, nnz, 32, w.hist, w.bsums, s);
     hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.vkey, ka);
     radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(nb), w.hist, w.bsums, s);
-    hipLaunchKernelGGL(k_bin_starts, dim3(grid_for(nnz + 1, n_cu)), dim3(256), 0, s, int(nnz),
-                       ka, int(nb), w.cnt);
+    bin_starts(ka, nnz, nb, w.cnt, n_cu, s);
     hipLaunchKernelGGL(k_group_flags, dim3(grid), dim3(256), 0, s, int(nnz), pa, ka, w.group_of,
                        vals, w.flag);
     scan_excl(w.flag, w.gid, nnz, w.bsums, n_groups, s);
@@ -632,7 +626,7 @@ vspmm_status run_tiled(const vspmm_matrix_s &h, const TilePlan &tp, const void *
     a.n_b_rows = int(tp.n_in);
     launch_aligned<float>(true, tp.pl, a, s);
     const size_t n = size_t(tp.n_out) * size_t(w);
-    const int grid = int(std::min<size_t>((n + 255) / 256, size_t(n_cu) * 16));
+    const int grid = int(std::min<size_t>((n + 63) / 64, size_t(n_cu) * 16));
     hipLaunchKernelGGL(k_tile_sum, dim3(grid), dim3(256), 0, s, wl.partial, (float *)out,
                        tp.tiles, n);
     return hip_status();

@@ -1,6 +1,6 @@
 """The tiled schedule of deterministic mode: B's rows cut into tiles that fit
 in a CU's LDS, each output row's entries split by tile and grouped by value
-per (tile, output row), partial rows added in tile order. Checked on the
+per (tile, output row), partial rows added in a fixed order. Checked on the
 60,000 x 2,000 count matrix in both directions whose dense input (60,000 rows)
 is too large for LDS, at widths where tiling applies (8, 16, 32) and where it
 does not (1, 64: the untiled paths run instead); on a matrix whose last tile
