@@ -513,9 +513,12 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
 // every entry goes to the virtual slice (tile, output row). The virtual
 // slices form a VCS of tiles x n_out slices with tile-local indices, walked by
 // k_vcs_rows with each block staging its tile of B; the tiles' partial rows
-// are then added in a fixed order. Worth it only when B does not fit in LDS
-// whole and the virtual slices stay long enough (at least 32 entries on
-// average) that the partial rows cost little next to the entries.
+// are then added in a fixed order. It pays where the untiled walks are bound
+// by L2 gather requests: B does not fit in LDS whole, B's rows are at most 64
+// bytes (one request each; wider rows gather from L2 at a better rate per
+// byte, and there the tiles measured slower) and the virtual slices keep at
+// least 16 entries on average, so the partial rows cost little next to the
+// entries.
 struct TilePlan {
     bool ok = false;
     int tr = 0;          // B rows per tile (a multiple of 4)
@@ -533,11 +536,14 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     n_cu = std::max(n_cu, 1);
     const int64_t no = n_out(h, dir), ni = n_in(h, dir);
     const size_t row_bytes = size_t(w) * 4;
+    if (row_bytes > 64) return tp;  // wider rows gather from L2 at a better rate per byte
     const size_t fixed = size_t(16) * kRowsWaveLds + 16;
     // B fits whole: the plain walks stage it already
     if (size_t(ni) * row_bytes + fixed + 8 * size_t(rows_header_cap(int(std::min<int64_t>(no, kI32Max)), n_cu)) <= kLdsMax)
         return tp;
-    const size_t header_margin = 8 * 1024;  // the block's slice-header table
+    // the block's slice-header table: 8 bytes per slice, at most 2,048 slices
+    // per block (blocks per tile are chosen below to keep it so)
+    const size_t header_margin = 8 * (2048 + 8);
     int64_t tr = int64_t((kLdsMax - fixed - header_margin) / row_bytes) & ~int64_t(3);
     if (tr < 64) return tp;  // rows too wide for a useful tile
     int64_t tiles = (ni + tr - 1) / tr;
@@ -549,9 +555,12 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     const int64_t nv = tiles * no;
     if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
     const int64_t mean = h.nnz / nv;
-    if (mean < 32 || mean >= kLongMean) return tp;
-    const int64_t bpt = std::max<int64_t>(1, n_cu / tiles);
+    if (mean < 16 || mean >= kLongMean) return tp;
+    // blocks per tile: enough to fill the chip, and enough that a block's
+    // slice-header table (8 bytes per slice, in LDS) stays at 2,048 slices
+    const int64_t bpt = std::max<int64_t>({int64_t(1), n_cu / tiles, (no + 2047) / 2048});
     const int64_t grid = tiles * bpt;
+    if (!fits_i32(grid)) return tp;
     const size_t b_al = (size_t(tr) * row_bytes + 15) & ~size_t(15);
     const size_t lds = b_al + fixed + 8 * size_t(rows_header_cap(int(nv), int(grid)));
     if (lds > kLdsMax) return tp;

@@ -105,3 +105,33 @@ def test_large_integer_exact(orc, large):
         ref = orc.spmm(L, direction, B, want=want)[want]
         assert np.array_equal(got, ref), (layout, direction, mode)
         del out, ws
+
+
+@pytest.mark.parametrize("width", [8, 16])
+@pytest.mark.parametrize("layout", ["vcsr", "vcsc"])
+def test_large_tiled(orc, large, layout, width):
+    """B @ A on the tiled schedule: B's 1,000,000 rows in 248 tiles at width 8
+    (4.96M virtual slices of ~40 entries) or 496 at width 16 (~20 entries),
+    ten blocks per tile so a block's header table stays small."""
+    L, dev = large["L"], large["dev"]
+    A = large[layout]
+    want = large["want"]["BA"]
+    info = A.plan_info(width, "BA", "deterministic")
+    assert info["tiles"] > 8 and info["kernel_name"] == "k_vcs_rows"
+    B = W.dense_normal(np.random.default_rng(81), L.shape[0], width)
+    Bd = to_dev(B, dev)
+    t0 = time.time()
+    ws = A.workspace("BA", "deterministic", width)
+    out = A.spmm(Bd, "BA", mode="deterministic", workspace=ws)
+    torch.cuda.synchronize()
+    got = out[torch.from_numpy(want).to(dev)].cpu().numpy()
+    rel = check_close(orc, L, "BA", B, got, want=want, where=f"large tiled {layout}")
+    log(f"tiled {layout} B@A w={width} ({info['tiles']} tiles): max rel error {rel:.2e} "
+        f"({time.time() - t0:.1f} s)")
+    torch.cuda.synchronize()
+    t1 = time.time()
+    again = A.spmm(Bd, "BA", mode="deterministic", workspace=ws)
+    torch.cuda.synchronize()
+    log(f"tiled {layout} B@A w={width}: {1e3 * (time.time() - t1):.2f} ms for a product on the built schedule")
+    assert torch.equal(again.view(torch.int32), out.view(torch.int32))
+    del out, again, ws

@@ -2,8 +2,9 @@
 in a CU's LDS, each output row's entries split by tile and grouped by value
 per (tile, output row), partial rows added in a fixed order. Checked on the
 60,000 x 2,000 count matrix in both directions whose dense input (60,000 rows)
-is too large for LDS, at widths where tiling applies (8, 16, 32) and where it
-does not (1, 64: the untiled paths run instead); on a matrix whose last tile
+is too large for LDS, at widths where tiling applies (4, 8, 16) and where it
+does not (1: too few virtual slices; 32, 64: rows wider than 64 bytes; the
+untiled paths run instead); on a matrix whose last tile
 is short and holds runs of empty groups; across workspaces and widths sharing
 one workspace; and against the float64 oracle, exactly on integer data."""
 
@@ -47,7 +48,7 @@ def run_det(A, L, direction, width, seed=0, ws=None, integer=False):
     return B, out, ws
 
 
-@pytest.mark.parametrize("width", [8, 16, 32])
+@pytest.mark.parametrize("width", [4, 8, 16])
 @pytest.mark.parametrize("layout,direction", LONG)
 def test_tiled_parity(orc, count60k, layout, direction, width):
     dev = need_gpu()
@@ -64,11 +65,12 @@ def test_tiled_parity(orc, count60k, layout, direction, width):
     assert torch.equal(other.view(torch.int32), out.view(torch.int32))
 
 
-@pytest.mark.parametrize("width", [1, 64])
+@pytest.mark.parametrize("width", [1, 32, 64])
 @pytest.mark.parametrize("layout,direction", LONG)
 def test_untiled_widths(orc, count60k, layout, direction, width):
-    """Width 1 (two tiles would leave too few slices) and 64 (slices too
-    short): no tiled schedule; the workspace asked for serves the plain paths."""
+    """Width 1 (two tiles would leave too few, too long virtual slices) and 32,
+    64 (rows wider than 64 bytes): no tiled schedule; the workspace asked for
+    serves the plain paths."""
     dev = need_gpu()
     L = count60k[layout]
     A = vcs_handle(L, dev)
