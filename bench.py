@@ -28,7 +28,9 @@ rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this script, each scaled
 by what the same counter reads for a plain device copy of known size
 (--copy-calibration). The figures sit in a record under profiles/ keyed by a
 hash of the kernel sources; when the sources have changed since, traffic is
-null.
+null. roofline.secondary is the walk's measured secondary ceiling from the
+same kind of record (SQ counters: instructions per entry, VALU busy fraction):
+the walk is bound by instruction issue and latency, not by HBM.
 
 Prints ONE JSON line. --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -99,6 +101,27 @@ def traffic_record(kernel, direction, width):
                     int(kv.get("width", -1)) == width and kv.get("source_sha256") == want):
                 return int(kv["hbm_bytes"]), os.path.relpath(f, ROOT)
     return None, None
+
+
+def ceiling_record(kernel):
+    """The walk's measured secondary ceiling from the counter record in
+    profiles/ (instruction counts per entry and how busy the VALU is), when its
+    source hash matches the sources built now; else None."""
+    want = kernel_source_hash()
+    pat = re.compile(r"^ceiling-record:\s*(.*)$")
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(f):
+            m = pat.match(line.strip())
+            if not m:
+                continue
+            kv = dict(tok.split("=", 1) for tok in m.group(1).split())
+            if kv.get("kernel") == kernel and kv.get("source_sha256") == want:
+                out = {k: float(v) for k, v in kv.items()
+                       if k not in ("kernel", "source_sha256", "bound")}
+                out["bound"] = kv.get("bound")
+                out["source"] = os.path.relpath(f, ROOT)
+                return out
+    return None
 
 
 def copy_calibration(mib):
@@ -311,7 +334,9 @@ def main():
                      "frac": per_dir[dom]["frac"], "traffic": traffic,
                      "traffic_source": traffic_src,
                      "algorithmic_bytes": per_dir[dom]["min_bytes"],
-                     "launch_us": per_dir[dom]["us"]},
+                     "launch_us": per_dir[dom]["us"],
+                     # what bounds the walk below the HBM roofline (SQ counters)
+                     "secondary": ceiling_record("k_vcs_rows")},
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
