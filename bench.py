@@ -32,7 +32,7 @@ null. roofline.secondary is the walk's measured secondary ceiling from the
 same kind of record (SQ counters: instructions per entry, VALU busy fraction):
 the walk is bound by instruction issue and latency, not by HBM.
 
-Prints ONE JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints ONE JSON line. --gpus above 1 is refused: the benchmark measures one GPU.
 """
 
 from __future__ import annotations
@@ -173,8 +173,9 @@ def main():
                     help="only run a plain device copy of MIB MiB three times (counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
-              "build (the product shards by major slices; see the design notes)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (a multi-GPU "
+              "product would shard the matrix by major slices; only the one-GPU path exists)",
+              file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

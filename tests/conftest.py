@@ -21,6 +21,7 @@ def orc():
 
 
 def gpu_required() -> bool:
-    """On a GPU machine (VSPMM_REQUIRE_GPU=1) a missing device is a failure, not a
-    skip, so a GPU job cannot pass green having tested nothing."""
+    """With VSPMM_REQUIRE_GPU=1 (set where a GPU is expected) a missing device
+    is a failure, not a skip, so a GPU job cannot pass green having tested
+    nothing."""
     return os.environ.get("VSPMM_REQUIRE_GPU", "") == "1"

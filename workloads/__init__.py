@@ -17,9 +17,9 @@ Layouts produced (all index arrays int32, as the device library takes them):
 Canonical order, used by every builder here: within a slice the groups are in
 ascending value, and within a group the minor indices ascend.
 
-Workloads (shapes and distributions as the survey of the pages fixes them; the
-pages' own matrices and the regridding data are not available, so these stand
-in for them):
+Workloads (the shapes and distributions the pages describe; the pages' own
+matrices and the regridding data are not available, so these stand in for
+them):
 
 * ``config1``: CSR 2,000 x 500, Poisson(10) entries per row, U(0,1) values.
 * ``count_matrix(60_000, 2_000, 100, 64)``: the 60k x 2k, ~6M-entry count
