@@ -64,6 +64,11 @@ struct WalkArgs {
     // (the last one cut at n_b_rows); 1 and n_in for an untiled walk
     int tiles = 1;
     int n_b_rows = 0;
+    // CSR short/plain walks: slices longer than long_len are left to k_long
+    // over long_list (n_long slices); a huge long_len skips nothing
+    int long_len = 0x7fffffff;
+    const int *long_list = nullptr;
+    int n_long = 0;
 };
 
 // The operands of one scatter walk (slices of the walked layout = rows of B).

@@ -310,6 +310,23 @@ k_group_major_ptr(int n_minor, int nnz, const int *__restrict__ tptr, const int 
     }
 }
 
+// ------------------------------------------------------------- long rows
+
+// Rows longer than min_len: counted into *count, or, with list, appended to
+// list at an atomic cursor (*count zeroed first; the order is arbitrary,
+// which does not matter: each listed row is walked on its own).
+__global__ void __launch_bounds__(256)
+k_long_rows(int n_rows, const int *__restrict__ row_ptr, int min_len, int *__restrict__ count,
+            int *__restrict__ list) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < n_rows; r += stride) {
+        if (row_ptr[r + 1] - row_ptr[r] > min_len) {
+            const int c = atomicAdd(count, 1);
+            if (list) list[c] = r;
+        }
+    }
+}
+
 // ------------------------------------------------------------ tiled layout
 
 // Keys of the tiled layout: entry e sits at output row m and input row n of

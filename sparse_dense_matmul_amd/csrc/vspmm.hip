@@ -32,6 +32,11 @@ struct vspmm_matrix_s {
     int force_group;
     int device;
     uint64_t id;
+    // CSR: rows longer than long_len (device list, owned), walked by k_long
+    // apart from the short walks so one long row does not hold up a wave
+    int32_t *long_rows = nullptr;
+    int64_t n_long = 0;
+    int long_len = 0x7fffffff;
     int64_t n_major() const { return layout == VSPMM_VCSC ? n_cols : n_rows; }
     int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
     size_t elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
@@ -270,6 +275,33 @@ void launch_aligned(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t 
         if (vcs) return launch_plain<true, T>(pl, a, s);
     }
     launch_plain<false, T>(pl, a, s);
+}
+
+// An aligned walk over the handle's own layout. For CSR with long rows, the
+// short or plain walk leaves the rows longer than long_len to k_long, which
+// gives each listed row a block of 8 waves (the same matrix-driven entry
+// lanes, so a column's arithmetic still does not depend on the width).
+template <typename T>
+void launch_csr_or_vcs(const vspmm_matrix_s &h, bool vcs, const Plan &pl, WalkArgs<T> a,
+                       int n_cu, hipStream_t s) {
+    const bool split_long = !vcs && pl.kind != kLong && h.n_long > 0;
+    if (split_long) {
+        a.long_len = h.long_len;
+        a.long_list = h.long_rows;
+        a.n_long = int(h.n_long);
+    }
+    launch_aligned<T>(vcs, pl, a, s);
+    if (split_long) {
+        Plan pl2 = pl;
+        pl2.kind = kLong;
+        pl2.sp.log_ww = 6 - pl.sp.log_g;
+        pl2.R = 1;
+        pl2.lds = false;
+        pl2.lds_bytes = 0;
+        pl2.block = 512;
+        pl2.grid = int(std::max<int64_t>(1, std::min<int64_t>(h.n_long, int64_t(n_cu) * 16)));
+        launch_long<false, T>(pl2, a, s);
+    }
 }
 
 // The scatter walk's plan: one column per lane, WW = w lanes per entry
@@ -685,11 +717,13 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
                                   B, out, n_cu, ni, vcs);
         if (h.dtype == VSPMM_F64)
-            launch_aligned<double>(vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr, h.vals,
-                                                              h.idx, B, out, w, ni), s);
+            launch_csr_or_vcs<double>(h, vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr,
+                                                                   h.vals, h.idx, B, out, w, ni),
+                                      n_cu, s);
         else
-            launch_aligned<float>(vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr, h.vals,
-                                                            h.idx, B, out, w, ni), s);
+            launch_csr_or_vcs<float>(h, vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr,
+                                                                 h.vals, h.idx, B, out, w, ni),
+                                     n_cu, s);
         return hip_status();
     }
     if (mode == VSPMM_ATOMIC) {
@@ -728,6 +762,48 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     return hip_status();
 }
 
+// Rows longer than one round of the short CSR walk (64 * 24 entries for
+// float32, 64 * 12 for float64): the short walks leave them to k_long.
+int csr_long_len(int dtype) { return dtype == VSPMM_F64 ? 64 * 12 : 64 * 24; }
+
+// Lists a CSR handle's long rows on the device (count, read back, then fill
+// an owned list). Waits for the stream once.
+vspmm_status list_long_rows(vspmm_matrix_s *m, hipStream_t s) {
+    m->long_len = csr_long_len(m->dtype);
+    if (m->nnz <= 0 || m->n_rows <= 0) return VSPMM_OK;
+    const DeviceInfo di = device_info(m->device);
+    const int grid = grid_for(m->n_rows, di.ok ? di.n_cu : 256);
+    int32_t *cnt = nullptr;
+    if (hipMalloc(&cnt, sizeof(int32_t)) != hipSuccess) return VSPMM_ERR_HIP;
+    int32_t host = 0;
+    vspmm_status st = VSPMM_OK;
+    launch_zero(cnt, sizeof(int32_t), s);
+    hipLaunchKernelGGL(k_long_rows, dim3(grid), dim3(256), 0, s, int(m->n_rows), m->sptr,
+                       m->long_len, cnt, (int32_t *)nullptr);
+    if (hipMemcpyAsync(&host, cnt, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        st = VSPMM_ERR_HIP;
+    } else if (host > 0) {
+        if (hipMalloc(&m->long_rows, size_t(host) * sizeof(int32_t)) != hipSuccess) {
+            st = VSPMM_ERR_HIP;
+        } else {
+            m->n_long = host;
+            launch_zero(cnt, sizeof(int32_t), s);
+            hipLaunchKernelGGL(k_long_rows, dim3(grid), dim3(256), 0, s, int(m->n_rows), m->sptr,
+                               m->long_len, cnt, m->long_rows);
+            if (hipStreamSynchronize(s) != hipSuccess) st = VSPMM_ERR_HIP;
+        }
+    }
+    (void)hipFree(cnt);
+    if (st == VSPMM_OK) st = hip_status();
+    return st;
+}
+
+void free_handle(vspmm_matrix_s *m) {
+    if (m->long_rows) (void)hipFree(m->long_rows);
+    delete m;
+}
+
 vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
     if (hipGetDevice(&m->device) != hipSuccess) {
         delete m;
@@ -738,6 +814,13 @@ vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
         const vspmm_status st = vspmm_validate(m, s);
         if (st) {
             delete m;
+            return st;
+        }
+    }
+    if (m->layout == VSPMM_CSR) {
+        const vspmm_status st = list_long_rows(m, s);
+        if (st) {
+            free_handle(m);
             return st;
         }
     }
@@ -842,7 +925,7 @@ vspmm_status vspmm_destroy(vspmm_matrix h) {
             else ++it;
         }
     }
-    delete h;
+    free_handle(h);
     return VSPMM_OK;
 }
 

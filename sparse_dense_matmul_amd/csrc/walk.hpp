@@ -229,7 +229,7 @@ template <bool VCS, typename T, int VEC, bool UNIFORM>
 __global__ void __launch_bounds__(256)
 k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
           const T *__restrict__ vals, const int *__restrict__ idx,
-          const T *__restrict__ B, T *__restrict__ out, int w, Split sp) {
+          const T *__restrict__ B, T *__restrict__ out, int w, Split sp, int long_len) {
     const int lane = threadIdx.x & 63;
     const int waves = blockDim.x >> 6;
     const int log_sub = sp.log_ww + sp.log_g;
@@ -253,9 +253,13 @@ k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             e0 = sptr[s];
             e1 = sptr[s + 1];
         }
+        // a slice longer than long_len is left to the long walk (k_long over
+        // the handle's list of long slices): walked here as empty, not written
+        const bool skip = e1 - e0 > long_len;
+        if (skip) e1 = e0;
         for (int c0 = 0; c0 < w; c0 += chunk) {
             const int col = c0 + cl * VEC;
-            const bool act = col < w;
+            const bool act = col < w && !skip;
             T acc[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = T(0);

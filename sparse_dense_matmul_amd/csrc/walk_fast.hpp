@@ -518,12 +518,14 @@ __device__ __forceinline__ void big_slice(int s, int lane, int slot, int cl, con
 
 // Short slices; requires G * WW == 64. Each wave walks a contiguous block of
 // slices in rounds. LDS_B stages B (n_in x w) in dynamic LDS first (one
-// 1024-thread block per CU), so gathers use the LDS pipe.
+// 1024-thread block per CU), so gathers use the LDS pipe. A slice too long
+// for one round (more than 64 * NWR entries) is walked by the wave alone, or,
+// with skip_big, left to k_long over the list of such slices.
 template <bool VCS, typename T, int VEC, bool LDS_B>
 __global__ void __launch_bounds__(1024)
 k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
         const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
-        T *__restrict__ out, int w, int n_in, Split sp) {
+        T *__restrict__ out, int w, int n_in, Split sp, int skip_big) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int GWR = 4;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
@@ -569,7 +571,9 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
     int sa = s_beg;
     while (sa < s_end) {
         if (r.nsl < 0) {  // one slice larger than a round
-            big_slice<VCS, T, VEC, SB>(sa, lane, slot, cl, sp, sptr, vptr, vals, idx, Bs, out, w);
+            // (with skip_big the long walk over the list of such slices writes it)
+            if (!skip_big)
+                big_slice<VCS, T, VEC, SB>(sa, lane, slot, cl, sp, sptr, vptr, vals, idx, Bs, out, w);
             sa += 1;
         } else {
             round_compute<VCS, T, VEC, NWR, GWR, SB>(r, W, V, GS, GV, 0, lane, slot, cl, sp, Bs,
@@ -589,7 +593,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 // ------------------------------------------------------------------- long
 
 // Long slices: one block of up to 8 waves per slice (grid-stride over
-// slices); requires G * WW == 64. Wave k takes the k-th of `waves` contiguous
+// slices, or over the slices in `list` when it is given); requires G * WW == 64. Wave k takes the k-th of `waves` contiguous
 // pieces of the slice's entries; a piece (up to 64*NWR entries per pass) and
 // the slice's group window are loaded at once, then walked from registers.
 // The waves' partial rows are added in wave order.
@@ -597,7 +601,7 @@ template <bool VCS, typename T, int VEC>
 __global__ void __launch_bounds__(512)
 k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
        const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
-       T *__restrict__ out, int w, Split sp) {
+       T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
     __shared__ T part[8][64 * VEC];
@@ -608,7 +612,9 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
     const int slot = lane >> sp.log_ww;
     const int cl = lane & ((1 << sp.log_ww) - 1);
     const int chunk_w = VEC << sp.log_ww;
-    for (int s = blockIdx.x; s < n_slices; s += gridDim.x) {
+    const int n_walk = list ? n_list : n_slices;
+    for (int li = blockIdx.x; li < n_walk; li += gridDim.x) {
+        const int s = list ? list[li] : li;
         int e0, e1, ka = 0, kb = 0;
         if constexpr (VCS) {
             ka = sptr[s];

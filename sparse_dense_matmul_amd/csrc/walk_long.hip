@@ -9,7 +9,7 @@ void launch_long(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     const dim3 g(pl.grid), b(pl.block);
 #define VSPMM_LONG(V)                                                                            \
     hipLaunchKernelGGL((k_long<VCS, T, V>), g, b, 0, s, a.n_slices, a.sptr, a.vptr, a.vals,      \
-                       a.idx, a.B, a.out, a.w, pl.sp)
+                       a.idx, a.B, a.out, a.w, pl.sp, a.long_list, a.n_long)
     if constexpr (sizeof(T) == 4) {
         if (pl.vec == 4) {
             VSPMM_LONG(4);

@@ -10,7 +10,7 @@ void launch_plain(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     // a slice per wave (R == 1) lets VCS walks keep the slice bounds uniform
 #define VSPMM_PLAIN(V, U)                                                                        \
     hipLaunchKernelGGL((k_aligned<VCS, T, V, U>), g, b, 0, s, a.n_slices, a.sptr, a.vptr,        \
-                       a.vals, a.idx, a.B, a.out, a.w, pl.sp)
+                       a.vals, a.idx, a.B, a.out, a.w, pl.sp, a.long_len)
 #define VSPMM_PLAIN_V(V)                                                                         \
     do {                                                                                         \
         if (VCS && pl.R == 1) VSPMM_PLAIN(V, VCS);                                               \

@@ -17,10 +17,12 @@ void launch_short_v(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     if (pl.lds) {
         allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true>));
         hipLaunchKernelGGL((k_short<false, T, VEC, true>), g, b, pl.lds_bytes, s, a.n_slices,
-                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp);
+                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
+                           a.long_list ? 1 : 0);
     } else {
         hipLaunchKernelGGL((k_short<false, T, VEC, false>), g, b, pl.lds_bytes, s, a.n_slices,
-                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp);
+                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
+                           a.long_list ? 1 : 0);
     }
 }
 

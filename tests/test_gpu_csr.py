@@ -156,3 +156,42 @@ def test_csr_edge_cases():
     assert not out.any()
     T = A.transpose()
     assert T.row_ptr.cpu().tolist() == [0, 0, 0, 0, 0]
+
+
+def heavy_tail(dtype, rng):
+    """3,000 x 50,000: Poisson(20) rows plus 60 rows of 2,000-6,000 entries and
+    rows of exactly the long-row bound and one past it (1,536 / 1,537 entries
+    for float32, 768 / 769 for float64)."""
+    m, n = 3_000, 50_000
+    lengths = rng.poisson(20, size=m)
+    long_rows = rng.choice(m, size=64, replace=False)
+    lengths[long_rows[:60]] = rng.integers(2_000, 6_000, size=60)
+    bound = 1_536 if dtype == np.float32 else 768
+    lengths[long_rows[60:]] = [bound - 1, bound, bound + 1, bound + 2]
+    rows, cols = W.sample_columns(rng, lengths, n)
+    vals = rng.random(rows.size).astype(dtype)
+    return W.build_csr(W.Triplets((m, n), rows, cols, vals))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_long_rows_split(orc, dtype):
+    """Rows longer than one round of the short walk go to the long walk over
+    the handle's list of long rows: parity at widths 1, 8, 32 (plain, short
+    and long walks together), batch columns equal to solo products bit for
+    bit, and repeats bit for bit."""
+    dev = need_gpu()
+    np_t = np.float32 if dtype == "f32" else np.float64
+    C = heavy_tail(np_t, np.random.default_rng(61))
+    A = csr_handle(C, dev)
+    for width in (1, 8, 32):
+        B = W.dense_normal(np.random.default_rng(width), C.shape[1], width, dtype=np_t)
+        out = A.spmm(to_dev(B, dev), "AB")
+        tol = 1e-12 if dtype == "f64" else 1e-5
+        check_close(orc, C, "AB", B, out, tol=tol, where=f"long rows {dtype} w={width}")
+        again = A.spmm(to_dev(B, dev), "AB")
+        assert torch.equal(again, out)
+    Bb = to_dev(W.dense_normal(np.random.default_rng(5), C.shape[1], 32, dtype=np_t), dev)
+    batch = A.spmm(Bb, "AB")
+    for c in (0, 5, 31):
+        solo = A.spmm(Bb[:, c:c + 1].contiguous(), "AB")
+        assert torch.equal(batch[:, c], solo[:, 0]), (dtype, c)
