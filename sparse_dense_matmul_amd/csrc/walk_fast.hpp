@@ -344,25 +344,46 @@ struct RingEntry {
     T v;
 };
 
-// out[s] for each slice of a loaded round (width chunk c0). Windows are
-// turned into (index, value) pairs one at a time; every step whose entries
-// are already in the ring is then walked, finishing slices as they end.
-template <bool VCS, typename T, int VEC, int NWR, int GWR, int SB>
+// out[s] for each slice of a loaded round, width chunks c0 .. c0 + NC - 1
+// (a chunk is the VEC << log_ww columns the width lanes cover at once).
+// Windows are turned into (index, value) pairs one at a time; every step
+// whose entries are already in the ring is then walked, finishing slices as
+// they end. Taking NC chunks in one walk reads each step's (index, value) pair
+// once for all of them; a column's arithmetic is the same for any NC.
+template <bool VCS, typename T, int VEC, int NWR, int GWR, int SB, int NC>
 __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR],
                                               const T (&V)[NWR], const int (&GS)[GWR],
                                               const T (&GV)[GWR], int c0, int lane, int slot,
                                               int cl, const Split &sp, const T *Bs,
                                               RingEntry<T> *ring, T *__restrict__ out, int w) {
+    constexpr int SBN = SB / NC > 0 ? SB / NC : 1;  // steps whose gathers are in flight together
     const int G = 1 << sp.log_g;
-    const int col = c0 + cl * VEC;
-    const bool act = col < w;
+    const int chunk = VEC << sp.log_ww;
+    int col[NC];
+    bool act[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        col[j] = c0 + j * chunk + cl * VEC;
+        act[j] = col[j] < w;
+    }
     int i = 0;                       // slice of the round being accumulated
     int q = r.E0;                    // its next step
     int e1 = readlane(r.he, 1);      // its end
     int g = 0;                       // VCS: group (round-relative) of the window's first position
-    T acc[VEC];
+    T acc[NC][VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[j][e] = T(0);
+    auto finish = [&]() {  // slice i is complete: reduce, store, reset
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            xor_reduce<T, VEC>(acc[j], 1 << sp.log_ww, 64);
+            if (slot == 0 && act[j]) store_vec<T, VEC>(out + (size_t)(r.sa + i) * w + col[j], acc[j]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[j][e] = T(0);
+        }
+    };
 #pragma unroll
     for (int k = 0; k < NWR; ++k) {
         const int wbase = r.E0 + 64 * k;
@@ -386,10 +407,7 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
         const int ready = min(wbase + 64, r.E1);
         for (;;) {
             while (q >= e1) {  // slice i is complete
-                xor_reduce<T, VEC>(acc, 1 << sp.log_ww, 64);
-                if (slot == 0 && act) store_vec<T, VEC>(out + (size_t)(r.sa + i) * w + col, acc);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+                finish();
                 ++i;
                 q = e1;  // slice i starts where slice i - 1 ends
                 if (i >= r.nsl) break;
@@ -402,27 +420,33 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
             if (avail <= q) break;
             int nb = avail == e1 ? (avail - q + G - 1) >> sp.log_g : (avail - q) >> sp.log_g;
             if (nb == 0) break;
-            nb = min(nb, SB);
-            RingEntry<T> re[SB];
+            nb = min(nb, SBN);
+            RingEntry<T> re[SBN];
 #pragma unroll
-            for (int t = 0; t < SB; ++t)
+            for (int t = 0; t < SBN; ++t)
                 if (t < nb) re[t] = ring[(q + t * G + slot - r.E0) & (kRing - 1)];
-            T bv[SB][VEC];
+            T bv[SBN][NC][VEC];
 #pragma unroll
-            for (int t = 0; t < SB; ++t) {
-                if (t < nb && act && q + t * G + slot < e1) {
-                    load_vec<T, VEC>(Bs + (size_t)re[t].ix * w + col, bv[t]);
-                } else {
+            for (int t = 0; t < SBN; ++t) {
+                const bool live = t < nb && q + t * G + slot < e1;
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) bv[t][e] = T(0);
+                for (int j = 0; j < NC; ++j) {
+                    if (live && act[j]) {
+                        load_vec<T, VEC>(Bs + (size_t)re[t].ix * w + col[j], bv[t][j]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) bv[t][j][e] = T(0);
+                    }
                 }
             }
 #pragma unroll
-            for (int t = 0; t < SB; ++t) {
+            for (int t = 0; t < SBN; ++t) {
                 if (t < nb) {
                     const T v = q + t * G + slot < e1 ? re[t].v : T(0);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[e] = fma_t(v, bv[t][e], acc[e]);
+                    for (int j = 0; j < NC; ++j)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) acc[j][e] = fma_t(v, bv[t][j][e], acc[j][e]);
                 }
             }
             q += nb * G;
@@ -431,10 +455,7 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
     // slices left after the last window are empty (no entries): zeros
     while (i < r.nsl) {
         if (q >= e1) {
-            xor_reduce<T, VEC>(acc, 1 << sp.log_ww, 64);
-            if (slot == 0 && act) store_vec<T, VEC>(out + (size_t)(r.sa + i) * w + col, acc);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+            finish();
             ++i;
             q = e1;
             if (i < r.nsl) e1 = readlane(r.he, i + 1);
@@ -520,8 +541,10 @@ __device__ __forceinline__ void big_slice(int s, int lane, int slot, int cl, con
 // slices in rounds. LDS_B stages B (n_in x w) in dynamic LDS first (one
 // 1024-thread block per CU), so gathers use the LDS pipe. A slice too long
 // for one round (more than 64 * NWR entries) is walked by the wave alone, or,
-// with skip_big, left to k_long over the list of such slices.
-template <bool VCS, typename T, int VEC, bool LDS_B>
+// with skip_big, left to k_long over the list of such slices. NC width chunks
+// are walked together (1, 2 or 4, so that NC chunks cover the width or come
+// closest to it).
+template <bool VCS, typename T, int VEC, bool LDS_B, int NC>
 __global__ void __launch_bounds__(1024)
 k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
         const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
@@ -576,11 +599,9 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
                 big_slice<VCS, T, VEC, SB>(sa, lane, slot, cl, sp, sptr, vptr, vals, idx, Bs, out, w);
             sa += 1;
         } else {
-            round_compute<VCS, T, VEC, NWR, GWR, SB>(r, W, V, GS, GV, 0, lane, slot, cl, sp, Bs,
-                                                     ring, out, w);
-            for (int c0 = chunk; c0 < w; c0 += chunk)
-                round_compute<VCS, T, VEC, NWR, GWR, SB>(r, W, V, GS, GV, c0, lane, slot, cl, sp,
-                                                         Bs, ring, out, w);
+            for (int c0 = 0; c0 < w; c0 += NC * chunk)
+                round_compute<VCS, T, VEC, NWR, GWR, SB, NC>(r, W, V, GS, GV, c0, lane, slot, cl,
+                                                             sp, Bs, ring, out, w);
             sa += r.nsl;
         }
         if (sa < s_end) {
@@ -597,14 +618,15 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 // pieces of the slice's entries; a piece (up to 64*NWR entries per pass) and
 // the slice's group window are loaded at once, then walked from registers.
 // The waves' partial rows are added in wave order.
-template <bool VCS, typename T, int VEC>
+template <bool VCS, typename T, int VEC, int NC>
 __global__ void __launch_bounds__(512)
 k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
        const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
        T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
-    __shared__ T part[8][64 * VEC];
+    constexpr int SBN = SB / NC > 0 ? SB / NC : 1;  // steps whose gathers are in flight together
+    __shared__ T part[8][NC * 64 * VEC];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int waves = blockDim.x >> 6;
@@ -628,12 +650,21 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
         const long long len = e1 - e0;
         const int ps = e0 + (int)(len * wave / waves);
         const int pe = e0 + (int)(len * (wave + 1) / waves);
-        for (int c0 = 0; c0 < w; c0 += chunk_w) {
-            const int col = c0 + cl * VEC;
-            const bool act = col < w;
-            T acc[VEC];
+        // NC width chunks per walk of the piece (a column's arithmetic is the
+        // same for any NC)
+        for (int c0 = 0; c0 < w; c0 += NC * chunk_w) {
+            int col[NC];
+            bool act[NC];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = T(0);
+            for (int j = 0; j < NC; ++j) {
+                col[j] = c0 + j * chunk_w + cl * VEC;
+                act[j] = col[j] < w;
+            }
+            T acc[NC][VEC];
+#pragma unroll
+            for (int j = 0; j < NC; ++j)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[j][e] = T(0);
             for (int P0 = ps; P0 < pe; P0 += 64 * NWR) {
                 const int P1 = min(pe, P0 + 64 * NWR);
                 int W[NWR];
@@ -652,11 +683,11 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
                     groups_load(g0, ka, kb, lane, vptr, vals);
                     groups_seek(g, g0, ka, kb, P0, lane, vptr, vals);
                 }
-                for (int q0 = P0; q0 < P1; q0 += SB * G) {
-                    T bv[SB][VEC];
-                    T vj[SB];
+                for (int q0 = P0; q0 < P1; q0 += SBN * G) {
+                    T bv[SBN][NC][VEC];
+                    T vj[SBN];
 #pragma unroll
-                    for (int t = 0; t < SB; ++t) {
+                    for (int t = 0; t < SBN; ++t) {
                         const int q = q0 + t * G;
                         const int p = q + slot;
                         const bool live = q < P1;  // wave-uniform
@@ -670,35 +701,48 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
                             const T v = live ? window_pick(V, o, slot, G) : T(0);
                             vj[t] = p < P1 ? v : T(0);  // all lanes shuffle first
                         }
-                        if (live && act && p < P1) {
-                            load_vec<T, VEC>(B + (size_t)ix * w + col, bv[t]);
-                        } else {
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e) bv[t][e] = T(0);
+                        for (int j = 0; j < NC; ++j) {
+                            if (live && act[j] && p < P1) {
+                                load_vec<T, VEC>(B + (size_t)ix * w + col[j], bv[t][j]);
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < VEC; ++e) bv[t][j][e] = T(0);
+                            }
                         }
                     }
 #pragma unroll
-                    for (int t = 0; t < SB; ++t) {
+                    for (int t = 0; t < SBN; ++t) {
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc[e] = fma_t(vj[t], bv[t][e], acc[e]);
+                        for (int j = 0; j < NC; ++j)
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e)
+                                acc[j][e] = fma_t(vj[t], bv[t][j][e], acc[j][e]);
                     }
                 }
             }
-            xor_reduce<T, VEC>(acc, 1 << sp.log_ww, 64);
-            if (slot == 0) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) part[wave][cl * VEC + e] = acc[e];
+            for (int j = 0; j < NC; ++j) {
+                xor_reduce<T, VEC>(acc[j], 1 << sp.log_ww, 64);
+                if (slot == 0) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) part[wave][j * chunk_w + cl * VEC + e] = acc[j][e];
+                }
             }
             __syncthreads();
-            if (wave == 0 && slot == 0 && act) {
-                T tot[VEC];
+            if (wave == 0 && slot == 0) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) tot[e] = part[0][cl * VEC + e];
-                for (int k = 1; k < waves; ++k) {
+                for (int j = 0; j < NC; ++j) {
+                    if (!act[j]) continue;
+                    T tot[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) tot[e] += part[k][cl * VEC + e];
+                    for (int e = 0; e < VEC; ++e) tot[e] = part[0][j * chunk_w + cl * VEC + e];
+                    for (int k = 1; k < waves; ++k) {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) tot[e] += part[k][j * chunk_w + cl * VEC + e];
+                    }
+                    store_vec<T, VEC>(out + (size_t)s * w + col[j], tot);
                 }
-                store_vec<T, VEC>(out + (size_t)s * w + col, tot);
             }
             __syncthreads();
         }

@@ -11,19 +11,30 @@ namespace vspmm {
 
 namespace {
 
-template <typename T, int VEC>
-void launch_short_v(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
+template <typename T, int VEC, int NC>
+void launch_short_nc(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     const dim3 g(pl.grid), b(pl.block);
     if (pl.lds) {
-        allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true>));
-        hipLaunchKernelGGL((k_short<false, T, VEC, true>), g, b, pl.lds_bytes, s, a.n_slices,
+        allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true, NC>));
+        hipLaunchKernelGGL((k_short<false, T, VEC, true, NC>), g, b, pl.lds_bytes, s, a.n_slices,
                            a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
                            a.long_list ? 1 : 0);
     } else {
-        hipLaunchKernelGGL((k_short<false, T, VEC, false>), g, b, pl.lds_bytes, s, a.n_slices,
+        hipLaunchKernelGGL((k_short<false, T, VEC, false, NC>), g, b, pl.lds_bytes, s, a.n_slices,
                            a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
                            a.long_list ? 1 : 0);
     }
+}
+
+// Width chunks walked together: the power of two (at most 4) that comes
+// closest to covering the width in one walk.
+template <typename T, int VEC>
+void launch_short_v(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
+    const int chunk = VEC << pl.sp.log_ww;
+    const int n_chunks = (a.w + chunk - 1) / chunk;
+    if (n_chunks >= 4) launch_short_nc<T, VEC, 4>(pl, a, s);
+    else if (n_chunks >= 2) launch_short_nc<T, VEC, 2>(pl, a, s);
+    else launch_short_nc<T, VEC, 1>(pl, a, s);
 }
 
 }  // namespace
