@@ -44,7 +44,8 @@
  *    Argument checks run on the host before anything is enqueued; a failed
  *    check enqueues nothing. Launch errors return VSPMM_ERR_HIP.
  *  - Work is enqueued on the given stream and returns before it finishes,
- *    except vspmm_validate, which waits for its result.
+ *    except vspmm_validate, which waits for its result, and
+ *    vspmm_create_csr, which waits once for its list of long rows.
  *  - Handles are immutable after creation apart from the workspace cache
  *    tag (guarded by a lock), so products on different streams may run
  *    concurrently if their outputs and workspaces are distinct.
@@ -103,7 +104,8 @@ enum { VSPMM_SPLIT_WIDTH = 1u, VSPMM_SPLIT_MATRIX = 2u, VSPMM_VALIDATE = 4u };
  *  flags       VSPMM_SPLIT_* / VSPMM_VALIDATE.
  *  force_group 0, or a power of two 1..64 fixing the number of entry lanes
  *              per slice (tests use it to cover every split).
- *  stream      stream used by VSPMM_VALIDATE.
+ *  stream      stream used by VSPMM_VALIDATE (and, for CSR, the long-row
+ *              list).
  * Errors: VSPMM_ERR_NULL, _DIM, _ENUM, _STRUCTURE (with VSPMM_VALIDATE),
  * _HIP, _ALLOC. *h is set only on success. */
 vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_rows,
@@ -116,7 +118,13 @@ vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_ro
  *  row_ptr device int32[n_rows + 1]; col device int32[nnz];
  *  val device float[nnz] (VSPMM_F32) or double[nnz] (VSPMM_F64).
  *  The dense operands of every product on this handle have the same dtype
- *  and the sums are carried in it. Other arguments as vspmm_create_vcs. */
+ *  and the sums are carried in it. Other arguments as vspmm_create_vcs.
+ *  The handle also lists, in device memory it owns (freed by vspmm_destroy),
+ *  the rows longer than 1,536 entries (float32) or 768 (float64): products
+ *  walk those rows with a block each instead of one wave, so a few long rows
+ *  do not hold up the rest (regridding page, section "How it is built", on
+ *  giving a row a group of threads sized to it). Building the list reads
+ *  row_ptr on `stream` and waits for it once. */
 vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, int64_t nnz,
                               const int32_t *row_ptr, const int32_t *col, const void *val,
                               vspmm_dtype dtype, uint32_t flags, int32_t force_group,
