@@ -159,6 +159,80 @@ def cpu_baseline(layouts, width, budget_s):
                       f"width {width}, float64, single-threaded C ({total_s:.1f} s)"}
 
 
+def csr_products(dev, steps, copies=8):
+    """The CSR rows of the path, reported beside the headline (not in it): the
+    regridding-shaped operator (20,000 x ~373,500, ~1.1M weights) in float32
+    and float64, forward (A @ x) and backprojection (x @ A, misaligned: atomic,
+    and deterministic on the built transpose), at widths 1 and 32. Algorithmic
+    bytes: 4(m+1) + (4+s) nnz + s w (n_in + n_out), s = 4 or 8."""
+    import torch
+
+    import sparse_dense_matmul_amd as sdm
+    import workloads as W
+
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    for np_t, tname in ((np.float32, "f32"), (np.float64, "f64")):
+        _, C = W.config4(np_t)
+        m, n = C.shape
+        s = np.dtype(np_t).itemsize
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        hs = [sdm.CsrMatrix.from_arrays(C.shape, up(C.row_ptr), up(C.col), up(C.val))
+              for _ in range(copies)]
+        for w in (1, 32):
+            for direction in ("AB", "BA"):
+                n_in, n_out = (n, m) if direction == "AB" else (m, n)
+                Bs = [up(np.random.default_rng(k).standard_normal((n_in, w)).astype(np_t))
+                      for k in range(copies)]
+                Os = [torch.empty((n_out, w), dtype=Bs[0].dtype, device=dev) for _ in range(copies)]
+                modes = ["atomic"] if direction == "AB" else ["atomic", "deterministic"]
+                for mode in modes:
+                    wss = [h.workspace(direction, mode) for h in hs] if mode != "atomic" else \
+                        [None] * copies
+                    run = lambda k: hs[k % copies].spmm(Bs[k % copies], direction, mode=mode,
+                                                        out=Os[k % copies],
+                                                        workspace=wss[k % copies])
+                    for k in range(copies):
+                        run(k)  # warm-up; builds the deterministic schedules
+                    torch.cuda.synchronize()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for k in range(steps):
+                        run(k)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    us = 1e3 * a.elapsed_time(b) / steps
+                    nbytes = 4 * (m + 1) + (4 + s) * C.nnz + s * w * (n_in + n_out)
+                    key = f"{tname} w={w} {'A@x' if direction == 'AB' else 'x@A'}" + \
+                          ("" if direction == "AB" else f" {mode}")
+                    out[key] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                "kernel": hs[0].plan_info(w, direction, mode)["kernel_name"]}
+                    del wss
+        # the exact transpose on the device (vspmm_transpose_csr), once per copy
+        h0 = hs[0]
+        ws = h0.workspace("BA")
+        t_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        t_col = torch.empty(C.nnz, dtype=torch.int32, device=dev)
+        t_val = torch.empty(C.nnz, dtype=hs[0].dtype, device=dev)
+        ts = []
+        for k in range(copies):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st = sdm.lib.vspmm_transpose_csr(hs[k]._h, t_ptr.data_ptr(), t_col.data_ptr(),
+                                             t_val.data_ptr(), ws.data_ptr(), ws.numel(),
+                                             sdm._stream(dev))
+            b.record(stream)
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"vspmm_transpose_csr failed with status {st}")
+            ts.append(a.elapsed_time(b))
+        out[f"{tname} transpose"] = {"us": round(1e3 * float(np.median(ts)), 1),
+                                     "kernel": "index keys + radix sort + bin starts + emit"}
+        del hs, ws
+    return {"workload": "CSR regridding operator 20,000 x ~373,500, ~1.1M weights "
+                        "(log-normal rows), U(0,1) values; cold copies rotated", "products": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +243,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-mode timings")
+    ap.add_argument("--no-csr", action="store_true", help="skip the CSR operator timings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter scale)")
     args = ap.parse_args()
@@ -341,6 +416,9 @@ def main():
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_csr:
+        log("timing the CSR operator (reported beside the headline)")
+        result["csr"] = csr_products(dev, args.steps)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(layouts, w, args.cpu_budget)

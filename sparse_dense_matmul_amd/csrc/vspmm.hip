@@ -1007,10 +1007,7 @@ vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_
     if (!t_row_ptr || (h->nnz > 0 && (!t_col || !t_val))) return VSPMM_ERR_NULL;
     const OppositeWs need = carve_opposite(*h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-    {
-        std::lock_guard<std::mutex> lk(g_ws_mutex);
-        g_ws_cache.erase(ws);
-    }
+    ws_drop(ws);  // ws no longer holds a cached layout
     const DeviceInfo di = device_info(h->device);
     build_transpose(*h, carve_opposite(*h, ws), t_row_ptr, t_col, t_val, di.ok ? di.n_cu : 256,
                     stream);
@@ -1026,10 +1023,7 @@ vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_va
     if (h->nnz > 0 && (!t_values || !t_indices)) return VSPMM_ERR_NULL;
     const OppositeWs need = carve_opposite(*h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-    {
-        std::lock_guard<std::mutex> lk(g_ws_mutex);
-        g_ws_cache.erase(ws);
-    }
+    ws_drop(ws);  // ws no longer holds a cached layout
     const DeviceInfo di = device_info(h->device);
     build_regroup(*h, carve_opposite(*h, ws), t_major_ptr, t_values, t_value_ptr, t_indices,
                   t_n_groups, di.ok ? di.n_cu : 256, stream);
