@@ -207,9 +207,13 @@ class SparseMatrix:
 
     def workspace(self, direction: str = "BA", mode: str = "deterministic",
                   width: int | None = None) -> torch.Tensor:
-        """A fresh device workspace of the required size (256-byte aligned)."""
+        """A fresh device workspace of the required size (256-byte aligned). The
+        library caches a built layout by workspace address; a fresh tensor may
+        reuse the address of a freed one, so its cache tag is dropped here."""
         nbytes = self.workspace_size(direction, mode, width)
-        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        lib.vspmm_workspace_invalidate(_ptr(ws))
+        return ws
 
     def validate(self) -> bool:
         st = lib.vspmm_validate(self._h, _stream(self.device))

@@ -248,3 +248,24 @@ def test_bad_arguments_raise():
     assert st == 1
     st = sdm.lib.vspmm_spmm(A.handle, None, None, 4, 9, None)
     assert st == 3
+
+
+def test_fresh_workspace_at_a_reused_address(orc, small):
+    """A workspace freed and reallocated at the same address (the caching
+    allocator's habit) after other data overwrote it: the binding's fresh
+    workspace drops the cache tag, so the schedule is rebuilt, not reused."""
+    dev = need_gpu()
+    L = small["vcsr"]
+    A = vcs_handle(L, dev)
+    B = W.dense_normal(np.random.default_rng(3), L.shape[0], 16)
+    Bd = to_dev(B, dev)
+    ws = A.workspace("BA", "deterministic")
+    first = A.spmm(Bd, "BA", mode="deterministic", workspace=ws).clone()
+    addr, n = ws.data_ptr(), ws.numel()
+    ws.fill_(0x5A)  # another user of the memory
+    del ws
+    ws2 = A.workspace("BA", "deterministic")
+    assert ws2.numel() == n
+    out = A.spmm(Bd, "BA", mode="deterministic", workspace=ws2)
+    check_close(orc, L, "BA", B, out, where=f"reused address {ws2.data_ptr() == addr}")
+    assert torch.equal(out.view(torch.int32), first.view(torch.int32))
