@@ -233,6 +233,63 @@ def csr_products(dev, steps, copies=8):
                         "(log-normal rows), U(0,1) values; cold copies rotated", "products": out}
 
 
+def other_widths(layouts, dev, widths, steps, copies=8):
+    """The same four directions at other widths of the pages' workload (by
+    default 1, 8, 32 and 64), beside the headline (not in it): each direction the way the
+    headline runs it (deterministic, every workspace sized for the width),
+    cold copies rotated. Returns per width the microseconds per direction and
+    the aggregate GB/s over the same byte count as the headline."""
+    import torch
+
+    import sparse_dense_matmul_amd as sdm
+    import workloads as W
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    m, n = layouts["vcsr"].shape
+    hs = [{lay: sdm.VcsMatrix.from_arrays(lay, L.shape, *[up(a) for a in (L.major_ptr, L.values,
+                                                                          L.value_ptr, L.indices)])
+           for lay, L in layouts.items()} for _ in range(copies)]
+    for w in widths:
+        rng = np.random.default_rng(w)
+        Bs = [{"AB": up(W.dense_normal(rng, n, w)), "BA": up(W.dense_normal(rng, m, w))}
+              for _ in range(copies)]
+        per, tot_us, tot_b = {}, 0.0, 0
+        for name, lay, direction, walk in DIRECTIONS:
+            L = layouts[lay]
+            out = [torch.empty((m if direction == "AB" else n, w), device=dev) for _ in range(copies)]
+            size = hs[0][lay].workspace_size(direction, "deterministic", w)
+            wss = [h[lay].workspace(direction, "deterministic", w) if size else None for h in hs]
+            mode = "deterministic" if size else "atomic"
+            run = lambda k: hs[k % copies][lay].spmm(Bs[k % copies][direction], direction,
+                                                     mode=mode, workspace=wss[k % copies],
+                                                     out=out[k % copies])
+            for k in range(copies):
+                run(k)  # builds the schedules
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for k in range(steps):
+                run(k)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / steps
+            other = layouts["vcsc" if lay == "vcsr" else "vcsr"]
+            nb = (L.nbytes() if walk == "aligned" else other.nbytes()) + dense_bytes(L.shape,
+                                                                                   direction, w)
+            info = hs[0][lay].plan_info(w, direction, mode)
+            per[name] = {"us": round(us, 2), "kernel": info["kernel_name"] +
+                         (f" (tiled, {info['tiles']} tiles) + k_tile_sum" if info["tiles"] else "")}
+            tot_us += us
+            tot_b += nb
+            del wss, out
+        res[f"w={w}"] = {"GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1), "directions": per}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +301,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-mode timings")
     ap.add_argument("--no-csr", action="store_true", help="skip the CSR operator timings")
+    ap.add_argument("--other-widths", default="1,8,32,64",
+                    help="widths also timed beside the headline (comma list, empty for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter scale)")
     args = ap.parse_args()
@@ -416,6 +475,10 @@ def main():
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
+    if args.other_widths:
+        log("timing the other widths (reported beside the headline)")
+        result["other_widths"] = other_widths(
+            layouts, dev, [int(x) for x in args.other_widths.split(",")], args.steps)
     if not args.no_csr:
         log("timing the CSR operator (reported beside the headline)")
         result["csr"] = csr_products(dev, args.steps)
