@@ -62,16 +62,9 @@ __device__ __forceinline__ void atomic_add_t(double *p, double v) { unsafeAtomic
 // bits of the lane id (bits log_ww .. log_ww + log_g - 1), highest bit first:
 // at each level a lane adds the partial of the lane whose id differs in that
 // bit. The pairing and order depend only on G, never on the width lanes, so
-// a column gets the same bits in any batch. slot_reduce_xor does it with
-// lane shuffles (any sub-wave size); slot_reduce_dpp does the same pairing
-// with cross-lane VALU ops for a full wave (G * WW == 64).
-template <typename T, int VEC>
-__device__ __forceinline__ void slot_reduce_xor(T (&acc)[VEC], int log_ww, int log_sub) {
-    for (int off = (1 << log_sub) >> 1; off >= (1 << log_ww); off >>= 1) {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
-    }
-}
+// a column gets the same bits in any batch. slot_reduce_dpp does it with
+// cross-lane VALU ops for a full wave (G * WW == 64), slot_reduce_sub for
+// sub-waves.
 
 // One butterfly level on a 32-bit value: partner differs in lane bit `bit`.
 __device__ __forceinline__ float level_f(float v, int bit) {
@@ -141,9 +134,36 @@ __device__ __forceinline__ double partner_d(double v, int bit) {
     return __longlong_as_double((long long)(((unsigned long long)phi << 32) | plo));
 }
 
+// The levels are unrolled so each one's lane pattern is an immediate; a
+// level below the width lanes is skipped by one uniform branch.
 template <typename T, int VEC>
 __device__ __forceinline__ void slot_reduce_dpp(T (&acc)[VEC], int log_ww) {
-    for (int bit = 5; bit >= log_ww; --bit) {
+#pragma unroll
+    for (int bit = 5; bit >= 0; --bit) {
+        if (bit < log_ww) break;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if constexpr (sizeof(T) == 4) acc[e] = level_f(acc[e], bit);
+            else acc[e] = acc[e] + partner_d(acc[e], bit);
+        }
+    }
+}
+
+// The same tree for sub-waves of 2^log_sub lanes, with the full-wave
+// patterns where they pair lanes exactly like xor: the swaps at bits 5 and 4
+// and the in-row rotations at bits 3, 1 and 0 always do; the rotation at bit
+// 2 does once bit 3 is summed (log_sub > 3), else a lane shuffle is used.
+template <typename T, int VEC>
+__device__ __forceinline__ void slot_reduce_sub(T (&acc)[VEC], int log_ww, int log_sub) {
+#pragma unroll
+    for (int bit = 5; bit >= 0; --bit) {
+        if (bit >= log_sub) continue;
+        if (bit < log_ww) break;
+        if (bit == 2 && log_sub == 3) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], 4);
+            continue;
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             if constexpr (sizeof(T) == 4) acc[e] = level_f(acc[e], bit);
@@ -164,11 +184,19 @@ __device__ __forceinline__ void walk_slice(int lane, int slot, int G, int ka, in
                                            const T *__restrict__ vals,
                                            const int *__restrict__ idx, Body &&body) {
     if constexpr (!VCS) {
+        // the next step's index and value are loaded (clamped to the slice)
+        // before this step's body, so they are in flight with its gathers
+        if (e0 >= e1) return;
+        int pn = min(e0 + slot, e1 - 1);
+        int i_n = idx[pn];
+        T v_n = vals[pn];
         for (int q = e0; q < e1; q += G) {
-            const int p = q + slot;
-            const bool valid = p < e1;
-            const int i = valid ? idx[p] : 0;
-            const T v = valid ? vals[p] : T(0);
+            const bool valid = q + slot < e1;
+            const int i = i_n;
+            const T v = v_n;
+            pn = min(q + G + slot, e1 - 1);
+            i_n = idx[pn];
+            v_n = vals[pn];
             body(valid, i, v);
         }
     } else if constexpr (UNIFORM) {
@@ -265,15 +293,19 @@ k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             for (int e = 0; e < VEC; ++e) acc[e] = T(0);
             walk_slice<VCS, UNIFORM, T>(lane, slot, G, ka, kb, e0, e1, vptr, vals, idx,
                                         [&](bool valid, int i, T v) {
+                                            // the gather is issued by every
+                                            // lane (row 0 / column 0 when
+                                            // idle); only the FMA is masked
+                                            T b[VEC];
+                                            load_vec<T, VEC>(B + (size_t)(valid ? i : 0) * w +
+                                                                 (act ? col : 0), b);
                                             if (valid && act) {
-                                                T b[VEC];
-                                                load_vec<T, VEC>(B + (size_t)i * w + col, b);
 #pragma unroll
                                                 for (int e = 0; e < VEC; ++e)
                                                     acc[e] = fma_t(v, b[e], acc[e]);
                                             }
                                         });
-            slot_reduce_xor<T, VEC>(acc, sp.log_ww, log_sub);
+            slot_reduce_sub<T, VEC>(acc, sp.log_ww, log_sub);
             if (slot == 0 && act) store_vec<T, VEC>(out + (size_t)s * w + col, acc);
         }
     }

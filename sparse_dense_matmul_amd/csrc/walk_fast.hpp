@@ -356,7 +356,9 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
                                               const T (&GV)[GWR], int c0, int lane, int slot,
                                               int cl, const Split &sp, const T *Bs,
                                               RingEntry<T> *ring, T *__restrict__ out, int w) {
-    constexpr int SBN = SB / NC > 0 ? SB / NC : 1;  // steps whose gathers are in flight together
+    // steps whose gathers are in flight together (float64 keeps two at any
+    // NC; float32 at NC = 4 has no registers left for a second)
+    constexpr int SBN = sizeof(T) == 8 ? 2 : (SB / NC > 0 ? SB / NC : 1);
     const int G = 1 << sp.log_g;
     const int chunk = VEC << sp.log_ww;
     int col[NC];
@@ -421,32 +423,33 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
             int nb = avail == e1 ? (avail - q + G - 1) >> sp.log_g : (avail - q) >> sp.log_g;
             if (nb == 0) break;
             nb = min(nb, SBN);
+            // gathers are issued for every lane of the batch without branches
+            // (a lane past the slice's end, or past what the ring holds, reads
+            // row 0; a lane past the width reads column 0), so the batch's
+            // loads are in flight together; only the FMAs are masked. An FMA
+            // skipped here would have added 0 * 0 to an accumulator that is
+            // never -0, so the result is the same bit for bit.
             RingEntry<T> re[SBN];
 #pragma unroll
-            for (int t = 0; t < SBN; ++t)
-                if (t < nb) re[t] = ring[(q + t * G + slot - r.E0) & (kRing - 1)];
+            for (int t = 0; t < SBN; ++t) re[t] = ring[(q + t * G + slot - r.E0) & (kRing - 1)];
             T bv[SBN][NC][VEC];
+            bool live[SBN];
 #pragma unroll
             for (int t = 0; t < SBN; ++t) {
-                const bool live = t < nb && q + t * G + slot < e1;
+                live[t] = t < nb && q + t * G + slot < e1;
+                const size_t row = (size_t)(live[t] ? re[t].ix : 0) * w;
 #pragma unroll
-                for (int j = 0; j < NC; ++j) {
-                    if (live && act[j]) {
-                        load_vec<T, VEC>(Bs + (size_t)re[t].ix * w + col[j], bv[t][j]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < VEC; ++e) bv[t][j][e] = T(0);
-                    }
-                }
+                for (int j = 0; j < NC; ++j)
+                    load_vec<T, VEC>(Bs + row + (act[j] ? col[j] : 0), bv[t][j]);
             }
 #pragma unroll
             for (int t = 0; t < SBN; ++t) {
-                if (t < nb) {
-                    const T v = q + t * G + slot < e1 ? re[t].v : T(0);
+                if (live[t]) {
 #pragma unroll
                     for (int j = 0; j < NC; ++j)
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc[j][e] = fma_t(v, bv[t][j][e], acc[j][e]);
+                        for (int e = 0; e < VEC; ++e)
+                            acc[j][e] = fma_t(re[t].v, bv[t][j][e], acc[j][e]);
                 }
             }
             q += nb * G;
@@ -625,7 +628,9 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
        T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
-    constexpr int SBN = SB / NC > 0 ? SB / NC : 1;  // steps whose gathers are in flight together
+    // steps whose gathers are in flight together (a few blocks run this
+    // walk, so registers are not what limits it)
+    constexpr int SBN = SB;
     __shared__ T part[8][NC * 64 * VEC];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -669,13 +674,13 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
                 const int P1 = min(pe, P0 + 64 * NWR);
                 int W[NWR];
                 T V[NWR];
+                // every window is loaded (clamped to the pass), so the loads
+                // carry no branches and go out back to back
 #pragma unroll
                 for (int k = 0; k < NWR; ++k) {
-                    if (P0 + 64 * k < P1) {
-                        const int p = min(P0 + 64 * k + lane, P1 - 1);
-                        W[k] = idx[p];
-                        if constexpr (!VCS) V[k] = vals[p];
-                    }
+                    const int p = min(P0 + 64 * k + lane, P1 - 1);
+                    W[k] = idx[p];
+                    if constexpr (!VCS) V[k] = vals[p];
                 }
                 Groups<T> g;
                 if constexpr (VCS) {
@@ -684,40 +689,38 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
                     groups_seek(g, g0, ka, kb, P0, lane, vptr, vals);
                 }
                 for (int q0 = P0; q0 < P1; q0 += SBN * G) {
+                    // as in round_compute: gathers without branches (dead
+                    // lanes read row 0 or column 0 of the pass), masked FMAs
                     T bv[SBN][NC][VEC];
                     T vj[SBN];
+                    bool lv[SBN];
 #pragma unroll
                     for (int t = 0; t < SBN; ++t) {
                         const int q = q0 + t * G;
                         const int p = q + slot;
                         const bool live = q < P1;  // wave-uniform
-                        const int o = q - P0;
-                        const int ix = live ? window_pick(W, o, slot, G) : 0;
+                        const int o = live ? q - P0 : 0;
+                        lv[t] = live && p < P1;
+                        const int ix = window_pick(W, o, slot, G);  // the windows are clamped
                         if constexpr (VCS)
                             vj[t] = live ? groups_value(g, p, min(q + G, P1), lane, vptr, vals)
                                          : T(0);
                         else
-                        {
-                            const T v = live ? window_pick(V, o, slot, G) : T(0);
-                            vj[t] = p < P1 ? v : T(0);  // all lanes shuffle first
-                        }
+                            vj[t] = window_pick(V, o, slot, G);
+                        const size_t row = (size_t)(lv[t] ? ix : 0) * w;
 #pragma unroll
-                        for (int j = 0; j < NC; ++j) {
-                            if (live && act[j] && p < P1) {
-                                load_vec<T, VEC>(B + (size_t)ix * w + col[j], bv[t][j]);
-                            } else {
-#pragma unroll
-                                for (int e = 0; e < VEC; ++e) bv[t][j][e] = T(0);
-                            }
-                        }
+                        for (int j = 0; j < NC; ++j)
+                            load_vec<T, VEC>(B + row + (act[j] ? col[j] : 0), bv[t][j]);
                     }
 #pragma unroll
                     for (int t = 0; t < SBN; ++t) {
+                        if (lv[t]) {
 #pragma unroll
-                        for (int j = 0; j < NC; ++j)
+                            for (int j = 0; j < NC; ++j)
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e)
-                                acc[j][e] = fma_t(vj[t], bv[t][j][e], acc[j][e]);
+                                for (int e = 0; e < VEC; ++e)
+                                    acc[j][e] = fma_t(vj[t], bv[t][j][e], acc[j][e]);
+                        }
                     }
                 }
             }

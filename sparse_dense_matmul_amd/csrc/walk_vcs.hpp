@@ -165,9 +165,10 @@ __device__ __forceinline__ int window_stream(const int (&W)[NWR], int nwin, int 
         }
 #pragma unroll
         for (int t = 0; t < Gm::SBV; ++t) {
+            // with 64 entry lanes a lane's entry is its own (no shuffle)
             const int src = (j0 + t) * Gm::G + slot;
-            const int ix = __shfl(wi, src);
-            st.vj[t] = __shfl(vk, src);
+            const int ix = Gm::G == 64 ? wi : __shfl(wi, src);
+            st.vj[t] = Gm::G == 64 ? vk : __shfl(vk, src);
             const uint32_t off = __umul24((uint32_t)ix, w4) + coff4;
             load_vec<float, VEC>(reinterpret_cast<const float *>(Bb + off), st.bv[t]);
         }
