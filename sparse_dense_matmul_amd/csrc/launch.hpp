@@ -69,6 +69,11 @@ struct WalkArgs {
     int long_len = 0x7fffffff;
     const int *long_list = nullptr;
     int n_long = 0;
+    // CSR short walk: with n_parts equal to the grid's waves, wave k walks
+    // the rows [parts[k], parts[k + 1]) (about equal entry counts), else an
+    // equal share of the rows
+    const int *parts = nullptr;
+    int n_parts = 0;
 };
 
 // The operands of one scatter walk (slices of the walked layout = rows of B).

@@ -327,6 +327,24 @@ k_long_rows(int n_rows, const int *__restrict__ row_ptr, int min_len, int *__res
     }
 }
 
+// Entry-balanced row ranges: parts[p] is the first row whose entries start at
+// or after p * nnz / n_parts (parts[n_parts] = n_rows), a binary search over
+// row_ptr per part.
+__global__ void __launch_bounds__(256)
+k_row_parts(int n_rows, const int *__restrict__ row_ptr, long long nnz, int n_parts,
+            int *__restrict__ parts) {
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p > n_parts) return;
+    const long long target = nnz * p / n_parts;
+    int lo = 0, hi = n_rows;  // first r in [0, n_rows] with row_ptr[r] >= target
+    while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        if (row_ptr[mid] >= target) hi = mid;
+        else lo = mid + 1;
+    }
+    parts[p] = p == n_parts ? n_rows : lo;
+}
+
 // ------------------------------------------------------------ tiled layout
 
 // Keys of the tiled layout: entry e sits at output row m and input row n of

@@ -37,6 +37,10 @@ struct vspmm_matrix_s {
     int32_t *long_rows = nullptr;
     int64_t n_long = 0;
     int long_len = 0x7fffffff;
+    // CSR: entry-balanced row ranges for the short walk, one per wave of its
+    // grid (16 waves per CU), device array of n_parts + 1 (owned)
+    int32_t *parts = nullptr;
+    int n_parts = 0;
     int64_t n_major() const { return layout == VSPMM_VCSC ? n_cols : n_rows; }
     int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
     size_t elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
@@ -163,6 +167,10 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
         const int64_t mean = n_slices > 0 ? nnz / n_slices : 0;
         log_g = std::min(6, ilog2_floor(std::max<int64_t>(mean, 1)));
         log_ww = std::min(log_need, 6 - log_g);
+        // CSR with 16 or more entry lanes: idle width lanes fill the wave so
+        // the short walk (one slice per wave, entry-balanced row ranges)
+        // takes it; the entry lanes, and so a column's arithmetic, are the same
+        if (!vcs && log_g >= 4) log_ww = 6 - log_g;
     } else {
         log_ww = log_need;
         log_g = 6 - log_ww;
@@ -289,6 +297,10 @@ void launch_csr_or_vcs(const vspmm_matrix_s &h, bool vcs, const Plan &pl, WalkAr
         a.long_len = h.long_len;
         a.long_list = h.long_rows;
         a.n_long = int(h.n_long);
+    }
+    if (!vcs) {
+        a.parts = h.parts;
+        a.n_parts = h.n_parts;
     }
     launch_aligned<T>(vcs, pl, a, s);
     if (split_long) {
@@ -762,16 +774,40 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     return hip_status();
 }
 
-// Rows longer than one round of the short CSR walk (64 * 24 entries for
-// float32, 64 * 12 for float64): the short walks leave them to k_long.
-int csr_long_len(int dtype) { return dtype == VSPMM_F64 ? 64 * 12 : 64 * 24; }
+// Waves of the short CSR walk's grid (16 per CU), one entry-balanced row
+// range each.
+int csr_parts(int n_cu) { return 16 * std::max(n_cu, 1); }
+
+// Rows the short walks leave to k_long: longer than one wave's share of the
+// entries (nnz over the walk's waves, at least 64), and always those longer
+// than one round of the short walk (64 * 24 entries for float32, 64 * 12 for
+// float64). With entry-balanced row ranges a wave then walks about its share.
+int csr_long_len(int dtype, int64_t nnz, int n_parts) {
+    const int64_t round = dtype == VSPMM_F64 ? 64 * 12 : 64 * 24;
+    const int64_t share = nnz / std::max(n_parts, 1);
+    return int(std::min(round, std::max<int64_t>(64, share)));
+}
+
+// The handle's entry-balanced row ranges (no wait).
+vspmm_status make_row_parts(vspmm_matrix_s *m, int n_cu, hipStream_t s) {
+    if (m->n_rows <= 0) return VSPMM_OK;
+    const int np = csr_parts(n_cu);
+    if (hipMalloc(&m->parts, size_t(np + 1) * sizeof(int32_t)) != hipSuccess) {
+        m->parts = nullptr;
+        return VSPMM_ERR_HIP;
+    }
+    m->n_parts = np;
+    hipLaunchKernelGGL(k_row_parts, dim3((np + 1 + 255) / 256), dim3(256), 0, s, int(m->n_rows),
+                       m->sptr, (long long)m->nnz, np, m->parts);
+    return hip_status();
+}
 
 // Lists a CSR handle's long rows on the device (count, read back, then fill
 // an owned list). Waits for the stream once.
 vspmm_status list_long_rows(vspmm_matrix_s *m, hipStream_t s) {
-    m->long_len = csr_long_len(m->dtype);
-    if (m->nnz <= 0 || m->n_rows <= 0) return VSPMM_OK;
     const DeviceInfo di = device_info(m->device);
+    m->long_len = csr_long_len(m->dtype, m->nnz, csr_parts(di.ok ? di.n_cu : 256));
+    if (m->nnz <= 0 || m->n_rows <= 0) return VSPMM_OK;
     const int grid = grid_for(m->n_rows, di.ok ? di.n_cu : 256);
     int32_t *cnt = nullptr;
     if (hipMalloc(&cnt, sizeof(int32_t)) != hipSuccess) return VSPMM_ERR_HIP;
@@ -801,6 +837,7 @@ vspmm_status list_long_rows(vspmm_matrix_s *m, hipStream_t s) {
 
 void free_handle(vspmm_matrix_s *m) {
     if (m->long_rows) (void)hipFree(m->long_rows);
+    if (m->parts) (void)hipFree(m->parts);
     delete m;
 }
 
@@ -818,7 +855,9 @@ vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
         }
     }
     if (m->layout == VSPMM_CSR) {
-        const vspmm_status st = list_long_rows(m, s);
+        const DeviceInfo di = device_info(m->device);
+        vspmm_status st = make_row_parts(m, di.ok ? di.n_cu : 256, s);
+        if (!st) st = list_long_rows(m, s);
         if (st) {
             free_handle(m);
             return st;

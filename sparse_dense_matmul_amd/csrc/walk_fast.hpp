@@ -272,15 +272,21 @@ struct Round {
 template <bool VCS, int NWR, int GWR>
 __device__ __forceinline__ void round_plan(Round &r, int sa, int s_end, int n_slices,
                                            int lane, const int *__restrict__ sptr,
-                                           const int *__restrict__ vptr) {
+                                           const int *__restrict__ vptr,
+                                           int long_len = 0x7fffffff) {
     r.sa = sa;
     r.hp = sptr[min(sa + lane, n_slices)];
     if constexpr (VCS) r.he = vptr[r.hp];
     else r.he = r.hp;
     const int e_first = readlane(r.he, 0);
     const int k_first = readlane(r.hp, 0);
+    // the round stops before the first slice longer than long_len (a round
+    // starting at one is empty: the caller skips that slice)
+    const int len = __shfl_down(r.he, 1) - r.he;  // slice sa + lane (lanes 0..62)
+    const unsigned long long lng = __ballot(lane < 63 && sa + lane < s_end && len > long_len);
+    const int first_long = lng ? __builtin_ctzll(lng) : 64;
     const bool fits = (sa + lane <= s_end) && (r.he - e_first <= 64 * NWR) &&
-                      (!VCS || r.hp - k_first <= 64 * GWR - 1);
+                      lane <= first_long && (!VCS || r.hp - k_first <= 64 * GWR - 1);
     const int last = __popcll(__ballot(fits)) - 1;  // fits is a prefix of the lanes
     r.nsl = last > 0 ? last : -1;
     r.E0 = e_first;
@@ -551,7 +557,8 @@ template <bool VCS, typename T, int VEC, bool LDS_B, int NC>
 __global__ void __launch_bounds__(1024)
 k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
         const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
-        T *__restrict__ out, int w, int n_in, Split sp, int skip_big) {
+        T *__restrict__ out, int w, int n_in, Split sp, int skip_big, int long_len,
+        const int *__restrict__ parts, int n_parts) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int GWR = 4;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
@@ -567,14 +574,18 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
     RingEntry<T> *ring = reinterpret_cast<RingEntry<T> *>(smem + b_bytes) + wave * kRing;
     const long long tw = (long long)gridDim.x * waves;
     const long long gw = (long long)blockIdx.x * waves + wave;
-    const int s_beg = (int)(gw * n_slices / tw);
-    const int s_end = (int)((gw + 1) * n_slices / tw);
+    int s_beg = (int)(gw * n_slices / tw);
+    int s_end = (int)((gw + 1) * n_slices / tw);
+    if (parts && n_parts == tw) {  // entry-balanced row ranges
+        s_beg = parts[gw];
+        s_end = parts[gw + 1];
+    }
 
     Round r;
     int W[NWR], GS[GWR];
     T V[NWR], GV[GWR];
     if (s_beg < s_end) {
-        round_plan<VCS, NWR, GWR>(r, s_beg, s_end, n_slices, lane, sptr, vptr);
+        round_plan<VCS, NWR, GWR>(r, s_beg, s_end, n_slices, lane, sptr, vptr, long_len);
         if (r.nsl > 0) round_load<VCS, T, NWR, GWR>(r, W, V, GS, GV, lane, vptr, vals, idx);
     }
 
@@ -596,7 +607,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 
     int sa = s_beg;
     while (sa < s_end) {
-        if (r.nsl < 0) {  // one slice larger than a round
+        if (r.nsl < 0) {  // one slice larger than a round, or than long_len
             // (with skip_big the long walk over the list of such slices writes it)
             if (!skip_big)
                 big_slice<VCS, T, VEC, SB>(sa, lane, slot, cl, sp, sptr, vptr, vals, idx, Bs, out, w);
@@ -608,7 +619,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
             sa += r.nsl;
         }
         if (sa < s_end) {
-            round_plan<VCS, NWR, GWR>(r, sa, s_end, n_slices, lane, sptr, vptr);
+            round_plan<VCS, NWR, GWR>(r, sa, s_end, n_slices, lane, sptr, vptr, long_len);
             if (r.nsl > 0) round_load<VCS, T, NWR, GWR>(r, W, V, GS, GV, lane, vptr, vals, idx);
         }
     }
@@ -628,8 +639,8 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
        T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
-    // steps whose gathers are in flight together (a few blocks run this
-    // walk, so registers are not what limits it)
+    // steps whose gathers are in flight together (a few 512-thread blocks
+    // run this walk, so registers are not what limits it)
     constexpr int SBN = SB;
     __shared__ T part[8][NC * 64 * VEC];
     const int lane = threadIdx.x & 63;

@@ -18,11 +18,11 @@ void launch_short_nc(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
         allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true, NC>));
         hipLaunchKernelGGL((k_short<false, T, VEC, true, NC>), g, b, pl.lds_bytes, s, a.n_slices,
                            a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
-                           a.long_list ? 1 : 0);
+                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts);
     } else {
         hipLaunchKernelGGL((k_short<false, T, VEC, false, NC>), g, b, pl.lds_bytes, s, a.n_slices,
                            a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
-                           a.long_list ? 1 : 0);
+                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts);
     }
 }
 

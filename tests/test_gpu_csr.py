@@ -159,15 +159,18 @@ def test_csr_edge_cases():
 
 
 def heavy_tail(dtype, rng):
-    """3,000 x 50,000: Poisson(20) rows plus 60 rows of 2,000-6,000 entries and
-    rows of exactly the long-row bound and one past it (1,536 / 1,537 entries
-    for float32, 768 / 769 for float64)."""
-    m, n = 3_000, 50_000
+    """4,541 x 50,000: Poisson(20) rows, 60 rows of 2,000-6,000 entries, and
+    one row of every length from 60 to 1,600 in random places. The long-row
+    bound (one wave's share of the entries, at least 64, at most one round of
+    the short walk) lies in that range on any device, so rows at it and one
+    past it are walked, long rows sit between short ones in a wave's range,
+    and rows past one round (1,536 float32 / 768 float64 entries) are there
+    too."""
+    m, n = 4_541, 50_000
     lengths = rng.poisson(20, size=m)
-    long_rows = rng.choice(m, size=64, replace=False)
-    lengths[long_rows[:60]] = rng.integers(2_000, 6_000, size=60)
-    bound = 1_536 if dtype == np.float32 else 768
-    lengths[long_rows[60:]] = [bound - 1, bound, bound + 1, bound + 2]
+    picked = rng.permutation(m)
+    lengths[picked[:60]] = rng.integers(2_000, 6_000, size=60)
+    lengths[picked[60:60 + 1_541]] = np.arange(60, 1_601)
     rows, cols = W.sample_columns(rng, lengths, n)
     vals = rng.random(rows.size).astype(dtype)
     return W.build_csr(W.Triplets((m, n), rows, cols, vals))
@@ -175,10 +178,10 @@ def heavy_tail(dtype, rng):
 
 @pytest.mark.parametrize("dtype", ["f32", "f64"])
 def test_long_rows_split(orc, dtype):
-    """Rows longer than one round of the short walk go to the long walk over
-    the handle's list of long rows: parity at widths 1, 8, 32 (plain, short
-    and long walks together), batch columns equal to solo products bit for
-    bit, and repeats bit for bit."""
+    """Rows longer than the long-row bound go to the long walk over the
+    handle's list of long rows, the others to the short walk over
+    entry-balanced row ranges: parity at widths 1, 8, 32, batch columns equal
+    to solo products bit for bit, and repeats bit for bit."""
     dev = need_gpu()
     np_t = np.float32 if dtype == "f32" else np.float64
     C = heavy_tail(np_t, np.random.default_rng(61))
