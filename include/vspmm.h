@@ -104,8 +104,8 @@ enum { VSPMM_SPLIT_WIDTH = 1u, VSPMM_SPLIT_MATRIX = 2u, VSPMM_VALIDATE = 4u };
  *  flags       VSPMM_SPLIT_* / VSPMM_VALIDATE.
  *  force_group 0, or a power of two 1..64 fixing the number of entry lanes
  *              per slice (tests use it to cover every split).
- *  stream      stream used by VSPMM_VALIDATE (and, for CSR, the long-row
- *              list).
+ *  stream      stream used by VSPMM_VALIDATE (and, for CSR, the row ranges
+ *              and the long-row list).
  * Errors: VSPMM_ERR_NULL, _DIM, _ENUM, _STRUCTURE (with VSPMM_VALIDATE),
  * _HIP, _ALLOC. *h is set only on success. */
 vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_rows,
@@ -119,18 +119,27 @@ vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_ro
  *  val device float[nnz] (VSPMM_F32) or double[nnz] (VSPMM_F64).
  *  The dense operands of every product on this handle have the same dtype
  *  and the sums are carried in it. Other arguments as vspmm_create_vcs.
- *  The handle also lists, in device memory it owns (freed by vspmm_destroy),
- *  the rows longer than 1,536 entries (float32) or 768 (float64): products
- *  walk those rows with a block each instead of one wave, so a few long rows
- *  do not hold up the rest (regridding page, section "How it is built", on
- *  giving a row a group of threads sized to it). Building the list reads
- *  row_ptr on `stream` and waits for it once. */
+ *  The handle also holds, in device memory it owns (freed by vspmm_destroy):
+ *  - one row range per wave of the short walk's grid (16 waves per CU), cut
+ *    so the ranges hold about equal numbers of entries (a binary search over
+ *    row_ptr per range), int32[16 * CUs + 1];
+ *  - the list of long rows: rows longer than one wave's share of the entries
+ *    (nnz / (16 * CUs), at least 64) or than one round of the short walk
+ *    (1,536 entries float32, 768 float64), whichever is smaller. Products
+ *    walk those rows with a block of waves each instead of inside one wave's
+ *    range, so a few long rows do not hold up the rest (regridding page,
+ *    section "How it is built", on giving a row a group of threads sized to
+ *    it).
+ *  Both are built from row_ptr on `stream`; counting the long rows waits for
+ *  it once. Which rows are long is fixed at creation, so it does not depend
+ *  on the width of a product. */
 vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, int64_t nnz,
                               const int32_t *row_ptr, const int32_t *col, const void *val,
                               vspmm_dtype dtype, uint32_t flags, int32_t force_group,
                               hipStream_t stream);
 
-/* Release the handle (host memory only; the borrowed arrays are untouched). */
+/* Release the handle: its host metadata and, for CSR, the device arrays it
+ * owns (row ranges and long-row list). The borrowed arrays are untouched. */
 vspmm_status vspmm_destroy(vspmm_matrix h);
 
 /* out = A @ B or B @ A (see Directions), atomic mode for misaligned

@@ -198,3 +198,29 @@ def test_long_rows_split(orc, dtype):
     for c in (0, 5, 31):
         solo = A.spmm(Bb[:, c:c + 1].contiguous(), "AB")
         assert torch.equal(batch[:, c], solo[:, 0]), (dtype, c)
+
+
+def test_long_rows_on_two_streams(regrid32):
+    """Products over a handle with long rows (two launches per product: the
+    short walk, then the long-row walk) on two streams at once, each followed
+    on its own stream by a copy of the output, equal the same products run one
+    at a time, bit for bit."""
+    dev = need_gpu()
+    A = csr_handle(regrid32, dev)
+    n = regrid32.shape[1]
+    Bs = [to_dev(W.dense_normal(np.random.default_rng(70 + k), n, w), dev)
+          for k, w in enumerate((1, 32, 8, 32))]
+    want = [A.spmm(B, "AB").clone() for B in Bs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    got = []
+    for k, B in enumerate(Bs):
+        st = streams[k % 2]
+        st.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(st):
+            out = torch.empty((regrid32.shape[0], B.shape[1]), device=dev)
+            A.spmm(B, "AB", out=out)
+            got.append(out.clone())  # runs on st after the join
+    torch.cuda.synchronize()
+    for k in range(len(Bs)):
+        assert torch.equal(got[k], want[k]), k
