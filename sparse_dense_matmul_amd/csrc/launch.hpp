@@ -74,6 +74,9 @@ struct WalkArgs {
     // equal share of the rows
     const int *parts = nullptr;
     int n_parts = 0;
+    // CSR short walk: blocks added in front of the grid that walk the long
+    // slices (kLongWaves waves per slice) in the same launch
+    int long_blocks = 0;
 };
 
 // The operands of one scatter walk (slices of the walked layout = rows of B).

@@ -224,6 +224,11 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
             pl.lds_bytes = 4 * ring + extra(g4);
             pl.block = 256;
             pl.grid = int(g4);
+            if (!vcs) {  // CSR: blocks of 8 waves, so a long-slice group fits one
+                pl.lds_bytes = 8 * ring;
+                pl.block = 512;
+                pl.grid = int(g1 * 2);
+            }
         }
         return pl;
     }
@@ -301,6 +306,13 @@ void launch_csr_or_vcs(const vspmm_matrix_s &h, bool vcs, const Plan &pl, WalkAr
     if (!vcs) {
         a.parts = h.parts;
         a.n_parts = h.n_parts;
+    }
+    if (split_long && pl.kind == kShort) {
+        // the long slices get blocks of their own in the short walk's launch
+        const int groups = pl.block / 512;
+        a.long_blocks = int(std::min<int64_t>((h.n_long + groups - 1) / groups, n_cu));
+        launch_aligned<T>(vcs, pl, a, s);
+        return;
     }
     launch_aligned<T>(vcs, pl, a, s);
     if (split_long) {

@@ -546,6 +546,16 @@ __device__ __forceinline__ void big_slice(int s, int lane, int slot, int cl, con
     }
 }
 
+constexpr int kLongWaves = 8;  // waves walking one long slice (see long_walk)
+
+template <bool VCS, typename T, int VEC, int NC, int SBN, int NWR>
+__device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
+                                          const int *__restrict__ list, int group, int wave,
+                                          T *part, const int *__restrict__ sptr,
+                                          const int *__restrict__ vptr, const T *__restrict__ vals,
+                                          const int *__restrict__ idx, const T *__restrict__ B,
+                                          T *__restrict__ out, int w, Split sp);
+
 // Short slices; requires G * WW == 64. Each wave walks a contiguous block of
 // slices in rounds. LDS_B stages B (n_in x w) in dynamic LDS first (one
 // 1024-thread block per CU), so gathers use the LDS pipe. A slice too long
@@ -558,7 +568,8 @@ __global__ void __launch_bounds__(1024)
 k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
         const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
         T *__restrict__ out, int w, int n_in, Split sp, int skip_big, int long_len,
-        const int *__restrict__ parts, int n_parts) {
+        const int *__restrict__ parts, int n_parts, const int *__restrict__ long_list,
+        int n_long, int long_blocks) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int GWR = 4;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
@@ -569,11 +580,24 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
     const int cl = lane & ((1 << sp.log_ww) - 1);
     const int chunk = VEC << sp.log_ww;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if ((int)blockIdx.x < long_blocks) {
+        // the first blocks walk the listed long slices, kLongWaves waves each
+        // (blocks of 8 or 16 waves: one or two groups), beside the short walk
+        const int groups = waves / kLongWaves;
+        const int group = wave / kLongWaves;
+        T *part = reinterpret_cast<T *>(smem) + group * (kLongWaves * NC * 64 * VEC);
+        // (under this kernel's register bound: one step's gathers per NC)
+        constexpr int LSBN = SB / NC > 0 ? SB / NC : 1;
+        long_walk<VCS, T, VEC, NC, LSBN, 8>(blockIdx.x * groups, long_blocks * groups, n_long, long_list,
+                                   group, wave - group * kLongWaves, part, sptr, vptr, vals, idx,
+                                   B, out, w, sp);
+        return;
+    }
     // dynamic LDS: [B staged (LDS_B), 16-byte aligned][one ring per wave]
     const size_t b_bytes = LDS_B ? (((size_t)n_in * w * sizeof(T) + 15) & ~size_t(15)) : 0;
     RingEntry<T> *ring = reinterpret_cast<RingEntry<T> *>(smem + b_bytes) + wave * kRing;
-    const long long tw = (long long)gridDim.x * waves;
-    const long long gw = (long long)blockIdx.x * waves + wave;
+    const long long tw = (long long)(gridDim.x - long_blocks) * waves;
+    const long long gw = (long long)(blockIdx.x - long_blocks) * waves + wave;
     int s_beg = (int)(gw * n_slices / tw);
     int s_end = (int)((gw + 1) * n_slices / tw);
     if (parts && n_parts == tw) {  // entry-balanced row ranges
@@ -627,34 +651,41 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 
 // ------------------------------------------------------------------- long
 
-// Long slices: one block of up to 8 waves per slice (grid-stride over
-// slices, or over the slices in `list` when it is given); requires G * WW == 64. Wave k takes the k-th of `waves` contiguous
-// pieces of the slice's entries; a piece (up to 64*NWR entries per pass) and
-// the slice's group window are loaded at once, then walked from registers.
-// The waves' partial rows are added in wave order.
-template <bool VCS, typename T, int VEC, int NC>
-__global__ void __launch_bounds__(512)
-k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
-       const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
-       T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
-    constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
-    constexpr int SB = sizeof(T) == 8 ? 2 : 4;
-    // steps whose gathers are in flight together (a few 512-thread blocks
-    // run this walk, so registers are not what limits it)
-    constexpr int SBN = SB;
-    __shared__ T part[8][NC * 64 * VEC];
+// Long slices: each is walked by a group of kLongWaves waves; wave k of the
+// group takes the k-th of kLongWaves contiguous pieces of the slice's
+// entries; a piece (up to 64*NWR entries per pass) and the slice's group
+// window are loaded at once, then walked from registers. The waves' partial
+// rows are added in wave order. The split depends only on the slice, so a
+// column's arithmetic is the same in every launch that walks it.
+//
+// long_walk: the block's `groups` groups take the slices li = first + group,
+// then li + stride, ... (li < n_walk; the slice is list[li], or li without a
+// list); every wave of the block runs the same iterations (the barriers are
+// block-wide). part: LDS for the group, kLongWaves x NC*64*VEC elements.
+// SBN steps have their gathers in flight together, and a pass loads NWR
+// windows; both set registers, not the arithmetic: a pass holds a multiple of
+// G entries, so each lane gets the same entries in the same order either way.
+template <bool VCS, typename T, int VEC, int NC, int SBN, int NWR>
+__device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
+                                          const int *__restrict__ list, int group, int wave,
+                                          T *part, const int *__restrict__ sptr,
+                                          const int *__restrict__ vptr, const T *__restrict__ vals,
+                                          const int *__restrict__ idx, const T *__restrict__ B,
+                                          T *__restrict__ out, int w, Split sp) {
+    constexpr int PW = NC * 64 * VEC;  // part elements per wave
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int waves = blockDim.x >> 6;
+    const int waves = kLongWaves;
     const int G = 1 << sp.log_g;
     const int slot = lane >> sp.log_ww;
     const int cl = lane & ((1 << sp.log_ww) - 1);
     const int chunk_w = VEC << sp.log_ww;
-    const int n_walk = list ? n_list : n_slices;
-    for (int li = blockIdx.x; li < n_walk; li += gridDim.x) {
-        const int s = list ? list[li] : li;
-        int e0, e1, ka = 0, kb = 0;
-        if constexpr (VCS) {
+    for (int base = first; base < n_walk; base += stride) {
+        const int li = base + group;
+        const bool live = li < n_walk;  // uniform in the group
+        const int s = live ? (list ? list[li] : li) : 0;
+        int e0 = 0, e1 = 0, ka = 0, kb = 0;
+        if (!live) {
+        } else if constexpr (VCS) {
             ka = sptr[s];
             kb = sptr[s + 1];
             e0 = vptr[ka];
@@ -740,20 +771,20 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
                 xor_reduce<T, VEC>(acc[j], 1 << sp.log_ww, 64);
                 if (slot == 0) {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) part[wave][j * chunk_w + cl * VEC + e] = acc[j][e];
+                    for (int e = 0; e < VEC; ++e) part[wave * PW + j * chunk_w + cl * VEC + e] = acc[j][e];
                 }
             }
             __syncthreads();
-            if (wave == 0 && slot == 0) {
+            if (live && wave == 0 && slot == 0) {
 #pragma unroll
                 for (int j = 0; j < NC; ++j) {
                     if (!act[j]) continue;
                     T tot[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) tot[e] = part[0][j * chunk_w + cl * VEC + e];
+                    for (int e = 0; e < VEC; ++e) tot[e] = part[j * chunk_w + cl * VEC + e];
                     for (int k = 1; k < waves; ++k) {
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) tot[e] += part[k][j * chunk_w + cl * VEC + e];
+                        for (int e = 0; e < VEC; ++e) tot[e] += part[k * PW + j * chunk_w + cl * VEC + e];
                     }
                     store_vec<T, VEC>(out + (size_t)s * w + col[j], tot);
                 }
@@ -761,6 +792,22 @@ k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
             __syncthreads();
         }
     }
+}
+
+
+// k_long: one group (a block of kLongWaves waves) per slice, grid-stride over
+// the slices, or over the slices in `list` when it is given; requires
+// G * WW == 64.
+template <bool VCS, typename T, int VEC, int NC>
+__global__ void __launch_bounds__(64 * kLongWaves)
+k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
+       const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
+       T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
+    __shared__ T part[kLongWaves * NC * 64 * VEC];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int SB = sizeof(T) == 8 ? 2 : 4;
+    long_walk<VCS, T, VEC, NC, SB, sizeof(T) == 8 ? 12 : 24>(blockIdx.x, gridDim.x, list ? n_list : n_slices, list, 0, wave,
+                                   part, sptr, vptr, vals, idx, B, out, w, sp);
 }
 
 }  // namespace vspmm

@@ -1,5 +1,7 @@
 // Launcher of k_short (short CSR slices). Built once per element type
 // (-DVSPMM_ELT=float or double), each object holding that type's instances.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "walk_fast.hpp"
 
@@ -11,18 +13,26 @@ namespace vspmm {
 
 namespace {
 
+// With long blocks, the grid grows by them and the dynamic LDS holds at least
+// their partial rows (kLongWaves x NC*64*VEC elements per group of waves).
 template <typename T, int VEC, int NC>
 void launch_short_nc(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
-    const dim3 g(pl.grid), b(pl.block);
+    const dim3 g(pl.grid + a.long_blocks), b(pl.block);
+    size_t lds = pl.lds_bytes;
+    if (a.long_blocks > 0)
+        lds = std::max(lds, size_t(pl.block / (64 * kLongWaves)) * kLongWaves * NC * 64 * VEC *
+                                sizeof(T));
     if (pl.lds) {
         allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true, NC>));
-        hipLaunchKernelGGL((k_short<false, T, VEC, true, NC>), g, b, pl.lds_bytes, s, a.n_slices,
+        hipLaunchKernelGGL((k_short<false, T, VEC, true, NC>), g, b, lds, s, a.n_slices,
                            a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
-                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts);
+                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
+                           a.n_long, a.long_blocks);
     } else {
-        hipLaunchKernelGGL((k_short<false, T, VEC, false, NC>), g, b, pl.lds_bytes, s, a.n_slices,
+        hipLaunchKernelGGL((k_short<false, T, VEC, false, NC>), g, b, lds, s, a.n_slices,
                            a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
-                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts);
+                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
+                           a.n_long, a.long_blocks);
     }
 }
 
