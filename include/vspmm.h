@@ -164,14 +164,17 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * Tiled schedule (VCSR/VCSC, float, either direction): when B's rows do not
  * fit in a CU's LDS and ws holds at least vspmm_workspace_size_width bytes
  * for this width, deterministic mode instead builds a tiled copy of the
- * matrix: B's rows are cut into tiles that fit in LDS and each output row's
- * entries are split by tile, every (tile, output row) part grouped by value
- * as in the pages' value-grouped layouts. The product walks it with each
- * block's tile of B in LDS, writes one partial row per (tile, output row) into
- * ws and adds them in a fixed order; it repeats bit for bit. The copy is reused
- * like the opposite layout (it also depends on the tile size, which follows
- * the width). A smaller ws falls back to the path above (aligned: the plain
- * walk, ws unused).
+ * matrix: B's rows are cut into tiles and each output row's entries are split
+ * by tile, every (tile, output row) part grouped by value as in the pages'
+ * value-grouped layouts. For rows of up to 64 bytes a tile fits in LDS and
+ * each block stages its tile there; for wider rows (when B is larger than
+ * 4 MB) tiles of about 2 MB, a multiple of 8 of them, each fit one XCD's L2
+ * and the blocks of a tile, all on one XCD, gather it from global memory. The
+ * product writes one partial row per (tile, output row) into ws and adds them
+ * in a fixed order; it repeats bit for bit. The copy is reused like the
+ * opposite layout (it also depends on the tile size, which follows the
+ * width). A smaller ws falls back to the path above (aligned: the plain walk,
+ * ws unused).
  *
  * ws: device, 256-byte aligned, at least vspmm_workspace_size bytes; unused
  * (may be NULL) when the size is 0. Errors: as vspmm_spmm, plus

@@ -188,8 +188,11 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
             pl.block = 512;
             if (vcs) {
                 // k_vcs_long: waves per slice so that the grid's waves fill the
-                // chip (16 per CU) about once
-                const int64_t target = int64_t(std::max(n_cu, 1)) * 16;
+                // chip (16 per CU) about once; twice over for rows of at most
+                // 16 bytes, whose gathers are cheap enough that shorter pieces
+                // pay (at wider rows the extra waves cost more L2 traffic)
+                const int64_t target = int64_t(std::max(n_cu, 1)) *
+                                       (size_t(w) * elt <= 16 ? 32 : 16);
                 int wps = 1;
                 while (wps < 8 && n_slices * wps * 2 <= target) wps *= 2;
                 pl.wps = wps;
@@ -585,6 +588,46 @@ struct TilePlan {
     int64_t n_bins() const { return int64_t(tiles) * n_out; }
 };
 
+// Rows wider than 64 bytes gather from L2 at a better rate per byte than from
+// LDS tiles, but a B larger than one XCD's L2 (4 MB) is then fetched from the
+// Infinity Cache by every XCD. L2 tiles: B cut into a multiple of 8 tiles of
+// about 2 MB, the blocks of a tile on one XCD (as for LDS tiles), the walk
+// gathering from global memory.
+TilePlan tile_plan_l2(const vspmm_matrix_s &h, int64_t no, int64_t ni, int64_t w, int n_cu,
+                      bool split_matrix, const void *B, const void *part) {
+    TilePlan tp;
+    const size_t row_bytes = size_t(w) * 4;
+    constexpr size_t kL2Tile = size_t(2) << 20;
+    const size_t b_bytes = size_t(ni) * row_bytes;
+    if (b_bytes <= 2 * kL2Tile) return tp;  // B fits one XCD's L2 already
+    int64_t tiles = int64_t((b_bytes + kL2Tile - 1) / kL2Tile);
+    tiles = (tiles + 7) / 8 * 8;
+    int64_t tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);
+    tiles = (ni + tr - 1) / tr;
+    if (tiles % 8 != 0) return tp;  // the XCD mapping needs whole tiles per XCD
+    const int64_t nv = tiles * no;
+    if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
+    const int64_t mean = h.nnz / nv;
+    if (mean < 16 || mean >= kLongMean) return tp;
+    // blocks of 4 waves, four per CU, and at most 2,048 slices per block
+    const int64_t bpt = std::max<int64_t>({int64_t(1), 4 * n_cu / tiles, (no + 2047) / 2048});
+    const int64_t grid = tiles * bpt;
+    if (!fits_i32(grid)) return tp;
+    Plan pl = make_plan(nv, h.nnz, w, 4, split_matrix, h.force_group, B, part, n_cu, tr, true);
+    if (pl.kind != kShort || pl.R != 1) return tp;
+    pl.lds = false;
+    pl.block = 256;
+    pl.grid = int(grid);
+    pl.lds_bytes = size_t(4) * kRowsWaveLds + 16 + 8 * size_t(rows_header_cap(int(nv), int(grid)));
+    tp.ok = true;
+    tp.tr = int(tr);
+    tp.tiles = int(tiles);
+    tp.n_out = no;
+    tp.n_in = ni;
+    tp.pl = pl;
+    return tp;
+}
+
 TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool split_matrix,
                    const void *B, const void *part) {
     TilePlan tp;
@@ -592,7 +635,7 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     n_cu = std::max(n_cu, 1);
     const int64_t no = n_out(h, dir), ni = n_in(h, dir);
     const size_t row_bytes = size_t(w) * 4;
-    if (row_bytes > 64) return tp;  // wider rows gather from L2 at a better rate per byte
+    if (row_bytes > 64) return tile_plan_l2(h, no, ni, w, n_cu, split_matrix, B, part);
     const size_t fixed = size_t(16) * kRowsWaveLds + 16;
     // B fits whole: the plain walks stage it already
     if (size_t(ni) * row_bytes + fixed + 8 * size_t(rows_header_cap(int(std::min<int64_t>(no, kI32Max)), n_cu)) <= kLdsMax)

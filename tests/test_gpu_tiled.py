@@ -1,12 +1,14 @@
-"""The tiled schedule of deterministic mode: B's rows cut into tiles that fit
-in a CU's LDS, each output row's entries split by tile and grouped by value
-per (tile, output row), partial rows added in a fixed order. Checked on the
-60,000 x 2,000 count matrix in both directions whose dense input (60,000 rows)
-is too large for LDS, at widths where tiling applies (4, 8, 16) and where it
-does not (1: too few virtual slices; 32, 64: rows wider than 64 bytes; the
-untiled paths run instead); on a matrix whose last tile
-is short and holds runs of empty groups; across workspaces and widths sharing
-one workspace; and against the float64 oracle, exactly on integer data."""
+"""The tiled schedule of deterministic mode: B's rows cut into tiles, each
+output row's entries split by tile and grouped by value per (tile, output
+row), partial rows added in a fixed order. Tiles fit a CU's LDS for rows of up
+to 64 bytes (staged there), and one XCD's L2 for wider rows (gathered from
+global memory, the blocks of a tile on one XCD). Checked on the 60,000 x 2,000
+count matrix in both directions whose dense input (60,000 rows) is too large
+for LDS, at widths where LDS tiles apply (4, 8, 16), where L2 tiles apply (32,
+64) and where neither does (1: too few, too long virtual slices; the untiled
+path runs instead); on a matrix whose last tile is short and holds runs of
+empty groups; across workspaces and widths sharing one workspace; and against
+the float64 oracle, exactly on integer data."""
 
 import numpy as np
 import pytest
@@ -65,12 +67,30 @@ def test_tiled_parity(orc, count60k, layout, direction, width):
     assert torch.equal(other.view(torch.int32), out.view(torch.int32))
 
 
-@pytest.mark.parametrize("width", [1, 32, 64])
+@pytest.mark.parametrize("width", [32, 64])
+@pytest.mark.parametrize("layout,direction", LONG)
+def test_l2_tiled_parity(orc, count60k, layout, direction, width):
+    """Rows of 128 and 256 bytes: B (7.7 / 15.4 MB) cut into 8 tiles of about
+    2 MB, one per XCD, gathered from L2 (no LDS staging); parity, repeats bit
+    for bit, and a second workspace gives the same bits."""
+    dev = need_gpu()
+    L = count60k[layout]
+    A = vcs_handle(L, dev)
+    info = A.plan_info(width, direction, "deterministic")
+    assert info["tiles"] == 8 and info["kernel_name"] == "k_vcs_rows" and info["lds_staged"] == 0
+    B, out, ws = run_det(A, L, direction, width)
+    check_close(orc, L, direction, B, out, where=f"L2 tiled {layout} {direction} w={width}")
+    again = A.spmm(to_dev(B, dev), direction, mode="deterministic", workspace=ws)
+    assert torch.equal(again.view(torch.int32), out.view(torch.int32))
+    _, other, _ = run_det(A, L, direction, width)
+    assert torch.equal(other.view(torch.int32), out.view(torch.int32))
+
+
+@pytest.mark.parametrize("width", [1])
 @pytest.mark.parametrize("layout,direction", LONG)
 def test_untiled_widths(orc, count60k, layout, direction, width):
-    """Width 1 (two tiles would leave too few, too long virtual slices) and 32,
-    64 (rows wider than 64 bytes): no tiled schedule; the workspace asked for
-    serves the plain paths."""
+    """Width 1 (two tiles would leave too few, too long virtual slices): no
+    tiled schedule; the workspace asked for serves the plain path."""
     dev = need_gpu()
     L = count60k[layout]
     A = vcs_handle(L, dev)
@@ -95,15 +115,17 @@ def test_tiled_ragged(orc, ragged, name, direction):
 
 
 def test_workspace_shared_across_widths(orc, count60k):
-    """One workspace large enough for both widths: the schedule is rebuilt when
-    the tile size changes and reused when it does not."""
+    """One workspace large enough for every width: the schedule is rebuilt when
+    the tile size changes and reused when it does not (widths 32 and 64 cut the
+    same 8 L2 tiles, so the second reuses the first's layout with its own
+    partial rows)."""
     dev = need_gpu()
     L = count60k["vcsr"]
     A = vcs_handle(L, dev)
-    n = max(A.workspace_size("BA", "deterministic", w) for w in (8, 16))
+    n = max(A.workspace_size("BA", "deterministic", w) for w in (8, 16, 32, 64))
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     first = {}
-    for width in (16, 8, 16, 8):
+    for width in (16, 8, 32, 64, 16, 8, 64, 32):
         B, out, _ = run_det(A, L, "BA", width, seed=width, ws=ws)
         if width in first:
             assert torch.equal(out.view(torch.int32), first[width].view(torch.int32))
