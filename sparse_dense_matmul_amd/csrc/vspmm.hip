@@ -294,9 +294,11 @@ void launch_aligned(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t 
 }
 
 // An aligned walk over the handle's own layout. For CSR with long rows, the
-// short or plain walk leaves the rows longer than long_len to k_long, which
-// gives each listed row a block of 8 waves (the same matrix-driven entry
-// lanes, so a column's arithmetic still does not depend on the width).
+// short or plain walk leaves the rows longer than long_len to the long walk,
+// which gives each listed row 8 waves (the same matrix-driven entry lanes and
+// the same pieces in either form, so a column's arithmetic does not depend on
+// the width): blocks of its own in front of the short walk's grid (same
+// launch), or k_long after the plain walk.
 template <typename T>
 void launch_csr_or_vcs(const vspmm_matrix_s &h, bool vcs, const Plan &pl, WalkArgs<T> a,
                        int n_cu, hipStream_t s) {

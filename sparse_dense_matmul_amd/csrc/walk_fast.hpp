@@ -2,30 +2,30 @@
 //
 // The plain walk issues one dependent chain per step (index load, then the
 // gather of B's row, then the fma), so a wave keeps ~64 bytes in flight and
-// the product runs far below the chip's bandwidth. These forms load a batch of
-// NS steps at once and keep the next batch in flight while the current one is
-// gathered and accumulated:
+// the product runs far below the chip's bandwidth. These forms load many
+// entries at once and keep several steps' gathers in flight:
 //
-//  - k_short: one wave walks a contiguous block of slices; each slice's first
-//    NS steps are one batch. With LDS_B the gathered operand is first copied
-//    into the CU's LDS (one 1024-thread block per CU), so gathers use the LDS
-//    pipe. Entries beyond a slice's first batch are walked batch by batch the
-//    same way.
-//  - k_long: a block of waves walks one slice; its entries are cut into
-//    chunks of NS steps dealt round-robin to the waves, and the waves'
-//    partial sums are added in wave order.
+//  - k_short: one wave walks a contiguous range of slices (for a CSR handle,
+//    its entry-balanced range) in rounds: a round's entry windows are loaded
+//    together, turned into (index, value) pairs in a per-wave LDS ring, and
+//    walked step by step, NC width chunks at a time. With LDS_B the gathered
+//    operand is first copied into the CU's LDS (one 1024-thread block per
+//    CU), so gathers use the LDS pipe. Slices longer than long_len are left to
+//    the long walk; with long blocks, the first blocks of the same launch run
+//    it beside the short slices.
+//  - long_walk (k_long, and the long blocks of k_short): kLongWaves waves walk
+//    one slice, wave k taking the k-th of kLongWaves contiguous pieces of its
+//    entries; the pieces' partial sums are added in wave order.
 //
-// Vector-memory loads complete in issue order, so each stage issues the
-// current batch's gathers first and only then the next batch's loads; waiting
-// for the gathers then never waits for the prefetch.
+// Gathers are issued by every lane without branches (an idle lane reads a
+// valid row), so a step's loads go out together; only the FMAs are masked.
 //
 // Arithmetic order: entry lane `slot` adds v * B[i] with one fma per element
-// over the slice's entries slot, slot + G, slot + 2G, ... in order (k_long:
-// over the entries of its wave's chunks, in order); the G entry lanes are
-// combined by a fixed xor tree, and k_long adds the waves' partials in wave
-// order. k_short gives the same bits as the plain walk. Results repeat bit for
-// bit and depend on the width only through the chunking of columns, never in a
-// column's own arithmetic.
+// over its entries slot, slot + G, slot + 2G, ... of the slice (of the wave's
+// piece, for the long walk) in order; the G entry lanes are combined by a
+// fixed xor tree, and the long walk adds the waves' partials in wave order.
+// Results repeat bit for bit and depend on the width only through the
+// chunking of columns, never in a column's own arithmetic.
 #pragma once
 
 #include <hip/hip_runtime.h>
