@@ -224,3 +224,42 @@ def test_long_rows_on_two_streams(regrid32):
     torch.cuda.synchronize()
     for k in range(len(Bs)):
         assert torch.equal(got[k], want[k]), k
+
+
+def _csr_from_lengths(lengths, n, dtype, seed):
+    rng = np.random.default_rng(seed)
+    rows, cols = W.sample_columns(rng, np.asarray(lengths), n)
+    vals = rng.random(rows.size).astype(dtype)
+    return W.build_csr(W.Triplets((len(lengths), n), rows, cols, vals))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("case", ["few_rows", "all_long", "one_row", "empty_runs"])
+def test_row_ranges_and_long_rows(orc, dtype, case):
+    """Entry-balanced row ranges and the long-row bound on shapes far from the
+    workloads: fewer rows than waves (most ranges empty), every row long, a
+    single non-empty row, and runs of empty rows around long ones; widths 1, 8
+    and 32, repeats bit for bit, and batch columns equal to solo products."""
+    dev = need_gpu()
+    np_t = np.float32 if dtype == "f32" else np.float64
+    n = 5_000
+    if case == "few_rows":
+        lengths = [3, 700, 0, 90, 2_500]
+    elif case == "all_long":
+        lengths = [900 + 37 * k for k in range(40)]
+    elif case == "one_row":
+        lengths = [0] * 300 + [1_800] + [0] * 300
+    else:
+        lengths = ([0] * 50 + [1_200] + [0] * 50 + [5] * 200) * 4
+    C = _csr_from_lengths(lengths, n, np_t, seed=len(lengths))
+    A = csr_handle(C, dev)
+    tol = 1e-5 if dtype == "f32" else 1e-12
+    for width in (1, 8, 32):
+        B = W.dense_normal(np.random.default_rng(width), n, width, dtype=np_t)
+        out = A.spmm(to_dev(B, dev), "AB")
+        check_close(orc, C, "AB", B, out, tol=tol, where=f"{case} {dtype} w={width}")
+        assert torch.equal(A.spmm(to_dev(B, dev), "AB"), out)
+    Bb = to_dev(W.dense_normal(np.random.default_rng(3), n, 32, dtype=np_t), dev)
+    batch = A.spmm(Bb, "AB")
+    for c in (0, 13, 31):
+        assert torch.equal(batch[:, c], A.spmm(Bb[:, c:c + 1].contiguous(), "AB")[:, 0]), (case, c)
