@@ -166,10 +166,11 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * for this width, deterministic mode instead builds a tiled copy of the
  * matrix: B's rows are cut into tiles and each output row's entries are split
  * by tile, every (tile, output row) part grouped by value as in the pages'
- * value-grouped layouts. For rows of up to 64 bytes a tile fits in LDS and
- * each block stages its tile there; for wider rows (when B is larger than
- * 4 MB) tiles of about 2 MB, a multiple of 8 of them, each fit one XCD's L2
- * and the blocks of a tile, all on one XCD, gather it from global memory. The
+ * value-grouped layouts. A B larger than 4 MB is cut into tiles of about
+ * 2 MB, a multiple of 8 of them, each fitting one XCD's L2: the blocks of a
+ * tile, all on one XCD and as many as the XCD holds at once, gather it from
+ * global memory. A smaller B with rows of up to 64 bytes is cut into tiles
+ * that fit in LDS, and each block stages its tile there. The
  * product writes one partial row per (tile, output row) into ws and adds them
  * in a fixed order; it repeats bit for bit. The copy is reused like the
  * opposite layout (it also depends on the tile size, which follows the

@@ -136,7 +136,9 @@ class SparseMatrix:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        # at interpreter exit the module's globals may already be gone; the
+        # process is ending and the driver frees the device memory then
+        if h and lib is not None:
             lib.vspmm_destroy(h)
             self._h = None
 

@@ -590,11 +590,14 @@ struct TilePlan {
     int64_t n_bins() const { return int64_t(tiles) * n_out; }
 };
 
-// Rows wider than 64 bytes gather from L2 at a better rate per byte than from
-// LDS tiles, but a B larger than one XCD's L2 (4 MB) is then fetched from the
-// Infinity Cache by every XCD. L2 tiles: B cut into a multiple of 8 tiles of
-// about 2 MB, the blocks of a tile on one XCD (as for LDS tiles), the walk
-// gathering from global memory.
+// A B larger than one XCD's L2 (4 MB) is fetched from the Infinity Cache by
+// every XCD when the walk gathers from global memory, and cut into LDS tiles
+// it needs so many tiles that their partial rows (written and read back per
+// (tile, output row)) outweigh the matrix. L2 tiles: B cut into a multiple of
+// 8 tiles of about 2 MB, the blocks of a tile on one XCD (as for LDS tiles),
+// as many blocks per tile as one XCD holds at once, so an XCD walks its tiles
+// one after another with one tile in its L2; the walk gathers from global
+// memory.
 TilePlan tile_plan_l2(const vspmm_matrix_s &h, int64_t no, int64_t ni, int64_t w, int n_cu,
                       bool split_matrix, const void *B, const void *part) {
     TilePlan tp;
@@ -611,8 +614,9 @@ TilePlan tile_plan_l2(const vspmm_matrix_s &h, int64_t no, int64_t ni, int64_t w
     if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
     const int64_t mean = h.nnz / nv;
     if (mean < 16 || mean >= kLongMean) return tp;
-    // blocks of 4 waves, four per CU, and at most 2,048 slices per block
-    const int64_t bpt = std::max<int64_t>({int64_t(1), 4 * n_cu / tiles, (no + 2047) / 2048});
+    // blocks of 4 waves, four per CU: a tile gets one XCD's worth (its CUs
+    // are an eighth of the chip), and at most 2,048 slices per block
+    const int64_t bpt = std::max<int64_t>({int64_t(1), 4 * n_cu / 8, (no + 2047) / 2048});
     const int64_t grid = tiles * bpt;
     if (!fits_i32(grid)) return tp;
     Plan pl = make_plan(nv, h.nnz, w, 4, split_matrix, h.force_group, B, part, n_cu, tr, true);
@@ -637,7 +641,12 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     n_cu = std::max(n_cu, 1);
     const int64_t no = n_out(h, dir), ni = n_in(h, dir);
     const size_t row_bytes = size_t(w) * 4;
-    if (row_bytes > 64) return tile_plan_l2(h, no, ni, w, n_cu, split_matrix, B, part);
+    // B over 4 MB: L2 tiles; else rows of up to 64 bytes: LDS tiles (wider
+    // rows gather from L2 at a better rate per byte)
+    {
+        const TilePlan t2 = tile_plan_l2(h, no, ni, w, n_cu, split_matrix, B, part);
+        if (t2.ok || row_bytes > 64) return t2;
+    }
     const size_t fixed = size_t(16) * kRowsWaveLds + 16;
     // B fits whole: the plain walks stage it already
     if (size_t(ni) * row_bytes + fixed + 8 * size_t(rows_header_cap(int(std::min<int64_t>(no, kI32Max)), n_cu)) <= kLdsMax)

@@ -107,12 +107,13 @@ def test_large_integer_exact(orc, large):
         del out, ws
 
 
-@pytest.mark.parametrize("width", [8, 16])
+@pytest.mark.parametrize("width", [8, 16, 32])
 @pytest.mark.parametrize("layout", ["vcsr", "vcsc"])
 def test_large_tiled(orc, large, layout, width):
-    """B @ A on the tiled schedule: B's 1,000,000 rows in 248 tiles at width 8
-    (4.96M virtual slices of ~40 entries) or 496 at width 16 (~20 entries),
-    ten blocks per tile so a block's header table stays small."""
+    """B @ A on the tiled schedule: B (1,000,000 rows, 32 / 64 / 128 MB) is
+    larger than one XCD's L2, so it is cut into L2 tiles of ~2 MB: 16 tiles at
+    width 8 (320,000 virtual slices of ~625 entries), 32 at width 16, 64 at
+    width 32, one XCD's worth of blocks per tile."""
     L, dev = large["L"], large["dev"]
     A = large[layout]
     want = large["want"]["BA"]
