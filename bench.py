@@ -301,6 +301,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-mode timings")
     ap.add_argument("--no-csr", action="store_true", help="skip the CSR operator timings")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--other-widths", default="1,8,32,64",
                     help="widths also timed beside the headline (comma list, empty for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -426,6 +427,38 @@ def main():
     value = step_bytes / (step_us * 1e-6) / 1e9
     dom = max(per_dir, key=lambda k: per_dir[k]["us"])
 
+    # the same steps replayed from a HIP graph (beside the headline): one
+    # graph holds a step on every copy, each direction in its headline mode
+    graph = None
+    if not args.no_graph:
+        modes = ["deterministic" if (lay, direction) in copies[0]["ws"] else "atomic"
+                 for _, lay, direction, _ in DIRECTIONS]
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for k in range(K):
+                    for d in range(len(DIRECTIONS)):
+                        run(k, d, modes[d])
+        torch.cuda.synchronize()
+        reps = max(2, -(-args.steps // K))
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        g_step_us = 1e3 * a.elapsed_time(b) / (reps * K)
+        graph = {"ms_per_step": round(g_step_us / 1e3, 5),
+                 "GBps": round(step_bytes / (g_step_us * 1e-6) / 1e9, 1),
+                 "steps": reps * K,
+                 "how": f"a HIP graph of {K} steps (one per operand copy, the four directions each in "
+                        "its headline mode), replayed; the same kernels and bytes as the headline"}
+        del g
+
     # guard: aligned and deterministic outputs repeat bit for bit
     c0 = copies[0]
     r1 = c0["A"]["vcsr"].spmm(c0["B"]["AB"], "AB").clone()
@@ -464,6 +497,7 @@ def main():
                         args.no_atomic else None, "unit": "GB/s",
                         "ms_per_step": round(atomic_us / 1e3, 5) if not args.no_atomic else None},
         "det_build_plus_first_product_ms": build_ms,
+        "graph_replay": graph,
         "roofline": {"bound": "hbm", "kernel": f"{per_dir[dom]['kernel']} ({dom})",
                      "achieved": per_dir[dom]["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": per_dir[dom]["frac"], "traffic": traffic,
