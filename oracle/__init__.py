@@ -15,8 +15,9 @@ are widened to float64, which is exact.
 Parity pins: the tests under ``tests/test_oracle_*.py`` tie each function to
 something other than itself (brute-force dense products, scipy.sparse, closed
 forms with all-ones operands, the dot-product identity, scipy's CSR->CSC
-conversion, the generator's own canonical layouts, the footprint ratios the
-vsparse page prints). No function here is "parity unpinned".
+conversion and index sort, hand-worked examples, the generator's own
+canonical layouts, the footprint ratios the vsparse page prints). No function
+here is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -195,6 +196,32 @@ def expand_vcs(major_ptr, values, value_ptr, indices, lib=None):
     lib.orc_expand_vcs(n_major, _p(major_ptr), _p(values), _p(value_ptr), _p(indices),
                        _p(ptr), _p(idx), _p(val))
     return ptr, idx, val
+
+
+def expand_vcs_format(layout, shape, major_ptr, values, value_ptr, indices, fmt="csr",
+                      sort_indices=True, lib=None):
+    """A VCSR or VCSC expanded to one value per entry as the CSR ("csr") or the
+    CSC ("csc") of A (vsparse page, section "Benchmarks": the expansion the
+    baseline runs on is index-sorted by default, with an opt-out, and takes a
+    format so that a VCSC-backed matrix can be expanded to CSR). In the
+    layout's own format (CSR from a VCSR, CSC from a VCSC) the stored-order
+    expansion is returned, or with sort_indices each slice's entries ordered
+    by index, a stable sort (repeated indices keep their stored order). In
+    the other format the result is the exact transpose of the stored-order
+    expansion, whose slices list their entries by ascending index already.
+    Returns (ptr, idx, val float32)."""
+    ptr, idx, val = expand_vcs(major_ptr, values, value_ptr, indices, lib=lib)
+    own = "csr" if layout == "vcsr" else "csc"
+    if fmt not in ("csr", "csc"):
+        raise ValueError(fmt)
+    if fmt == own:
+        if sort_indices:
+            slice_of = np.repeat(np.arange(ptr.size - 1), np.diff(ptr))
+            order = np.lexsort((idx, slice_of))  # by slice, then index; stable
+            idx, val = idx[order], val[order]
+        return ptr, idx, val
+    n_minor = shape[1] if layout == "vcsr" else shape[0]
+    return transpose_csr(n_minor, ptr, idx, val, lib=lib)
 
 
 def transpose_csr(n_minor, ptr, idx, val, lib=None):

@@ -49,3 +49,31 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
                           "-k", "not footprint"], cwd=ROOT, env=env, capture_output=True,
                          text=True, timeout=600)
     assert res.returncode != 0, f"planted mistake '{name}' passed every pin:\n{res.stdout[-2000:]}"
+
+
+# (name, text in oracle/__init__.py, replacement): mistakes in the Python steps
+PY_MUTANTS = [
+    ("expand_sort_keys_swapped", "np.lexsort((idx, slice_of))", "np.lexsort((slice_of, idx))"),
+    ("expand_sort_descending", "np.lexsort((idx, slice_of))", "np.lexsort((-idx, slice_of))"),
+    ("expand_other_format_untransposed", "    return transpose_csr(n_minor, ptr, idx, val, lib=lib)\n\n\ndef transpose_csr",
+     "    return ptr, idx, val\n\n\ndef transpose_csr"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_planted_python_mistake(tmp_path, name, old, new):
+    src = open(os.path.join(ROOT, "oracle", "__init__.py")).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(src.replace(old, new))
+    (pkg / "oracle.c").write_text(open(os.path.join(ROOT, "oracle", "oracle.c")).read())
+    lib = oracle.build(str(pkg / "oracle.c"), str(tmp_path / "liboracle_copy.so"))
+    # the mutant package comes first on the path (the child runs from tmp_path)
+    env = dict(os.environ, ORACLE_LIB=lib,
+               PYTHONPATH=os.pathsep.join([str(tmp_path), ROOT, os.environ.get("PYTHONPATH", "")]))
+    res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                          "--rootdir", ROOT, os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                          "-k", "not footprint"], cwd=str(tmp_path), env=env,
+                         capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"planted mistake '{name}' passed every pin:\n{res.stdout[-2000:]}"

@@ -343,3 +343,54 @@ def test_footprint_ratios_printed_on_page():
     csc = W.expanded_csr_nbytes(2_000, t.nnz)
     assert round(R.nbytes() / csr, 2) == g["printed_to_two_decimals"]["vcsr"]
     assert round(C.nbytes() / csc, 2) == g["printed_to_two_decimals"]["vcsc"]
+
+
+@pytest.mark.parametrize("layout", ["vcsr", "vcsc"])
+def test_expand_formats_match_scipy(orc, layout):
+    """VCS -> CSR / CSC of A, index-sorted: on a matrix without repeated
+    (row, column) pairs the sorted expansion is unique, and equals scipy's
+    (csr_matrix(...).sort_indices() in the layout's own format, .tocsc() /
+    .tocsr() of the stored-order expansion in the other)."""
+    t = W.count_matrix(300, 170, 12.0, 9, W.rng_for(71))
+    L = W.build_vcs(t, layout)
+    m, n = t.shape
+    own = "csr" if layout == "vcsr" else "csc"
+    other = "csc" if own == "csr" else "csr"
+    ptr, idx, val = orc.expand_vcs(L.major_ptr, L.values, L.value_ptr, L.indices)
+    M = (sp.csr_matrix if own == "csr" else sp.csc_matrix)((val, idx, ptr), shape=(m, n))
+    S = M.copy()
+    S.sort_indices()
+    got = orc.expand_vcs_format(layout, (m, n), L.major_ptr, L.values, L.value_ptr, L.indices,
+                                own, True)
+    assert np.array_equal(got[0], S.indptr) and np.array_equal(got[1], S.indices)
+    assert np.array_equal(got[2], S.data)
+    T = M.tocsc() if other == "csc" else M.tocsr()
+    T.sort_indices()
+    got = orc.expand_vcs_format(layout, (m, n), L.major_ptr, L.values, L.value_ptr, L.indices,
+                                other, True)
+    assert np.array_equal(got[0], T.indptr) and np.array_equal(got[1], T.indices)
+    assert np.array_equal(got[2], T.data)
+    # unsorted, own format: the stored order itself
+    got = orc.expand_vcs_format(layout, (m, n), L.major_ptr, L.values, L.value_ptr, L.indices,
+                                own, False)
+    assert np.array_equal(got[1], idx) and np.array_equal(got[2], val)
+
+
+def test_expand_sorted_repeated_indices(orc):
+    """Worked by hand: a 2 x 6 VCSR whose row 0 holds index 1 in two groups.
+    Row 0: value 2 at [5, 1], value 3 at [1]; row 1: value 7 at [4, 0].
+    Stored order: (5, 2) (1, 2) (1, 3) | (4, 7) (0, 7). Sorted by index, equal
+    indices in stored order: (1, 2) (1, 3) (5, 2) | (0, 7) (4, 7). The CSC: column
+    0: (1, 7); column 1: (0, 2) (0, 3); column 4: (1, 7); column 5: (0, 2)."""
+    major_ptr = np.array([0, 2, 3], np.int32)
+    values = np.array([2, 3, 7], np.float32)
+    value_ptr = np.array([0, 2, 3, 5], np.int32)
+    indices = np.array([5, 1, 1, 4, 0], np.int32)
+    ptr, idx, val = orc.expand_vcs_format("vcsr", (2, 6), major_ptr, values, value_ptr, indices,
+                                          "csr", True)
+    assert ptr.tolist() == [0, 3, 5]
+    assert idx.tolist() == [1, 1, 5, 0, 4] and val.tolist() == [2, 3, 2, 7, 7]
+    ptr, idx, val = orc.expand_vcs_format("vcsr", (2, 6), major_ptr, values, value_ptr, indices,
+                                          "csc", True)
+    assert ptr.tolist() == [0, 1, 3, 3, 3, 4, 5]
+    assert idx.tolist() == [1, 0, 0, 1, 0] and val.tolist() == [7, 2, 3, 7, 2]
