@@ -223,6 +223,35 @@ vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_va
                                int32_t *t_n_groups, void *ws, size_t ws_bytes,
                                hipStream_t stream);
 
+/* Formats of an expanded matrix (one value per entry): the CSR of A (row
+ * pointers over the rows, column indices) or its CSC (column pointers over
+ * the columns, row indices). */
+typedef enum { VSPMM_FORMAT_CSR = 0, VSPMM_FORMAT_CSC = 1 } vspmm_format;
+
+/* A VCS handle expanded to one value per entry (vsparse page, section
+ * "Benchmarks": the expansion its baseline runs on is index-sorted by
+ * default, with an opt-out, and takes a format so a VCSC-backed matrix can be
+ * expanded to CSR).
+ *  - The layout's own format (CSR from a VCSR, CSC from a VCSC): with
+ *    sort_indices == 0 the entries in stored order (each slice's groups in
+ *    turn, the group's value repeated on each of its entries); otherwise each
+ *    slice's entries ordered by index, repeated indices in stored order.
+ *  - The other format: the exact transpose of the stored-order expansion;
+ *    each slice lists its entries by ascending index (sort_indices has no
+ *    effect), repeated pairs in stored order.
+ * Outputs (device): ptr int32[n_rows + 1] (CSR) or int32[n_cols + 1] (CSC),
+ * idx int32[nnz], val float[nnz]. ws: device, 256-byte aligned, at least
+ * vspmm_workspace_size(h, dir, VSPMM_DETERMINISTIC) bytes for the handle's
+ * misaligned direction (VSPMM_BA for a VCSR, VSPMM_AB for a VCSC), needed
+ * unless the format is the layout's own and sort_indices == 0 (then it may
+ * be NULL). A workspace holding a built schedule is overwritten (the next
+ * deterministic product on it rebuilds). Bit-exact: the same entries and
+ * values as the definition, in the order above.
+ * Errors: _NULL, _ENUM (not VCS, unknown format), _WORKSPACE, _HIP. */
+vspmm_status vspmm_expand_vcs(vspmm_matrix h, vspmm_format format, int32_t sort_indices,
+                              int32_t *ptr, int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* Device bytes the handle's arrays occupy, and what the same matrix would take
  * expanded to one value per entry in the same major order (int32 pointers and
  * indices). Both host. */

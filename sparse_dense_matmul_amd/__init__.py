@@ -48,6 +48,7 @@ EXPORTS = {
     "vspmm_validate": ([_vp, _vp], ctypes.c_int),
     "vspmm_transpose_csr": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_regroup_vcs": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_expand_vcs": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_footprint": ([_vp, _P(_sz), _P(_sz)], ctypes.c_int),
     "vspmm_workspace_size_width": ([_vp, ctypes.c_int, ctypes.c_int, _i64, _P(_sz)],
                                    ctypes.c_int),
@@ -318,6 +319,30 @@ class VcsMatrix(SparseMatrix):
         return VcsMatrix.from_arrays(other, self.shape, t_mp, t_v[:g].clone(),
                                      t_vp[:g + 1].clone(), t_i[:nnz].clone(), flags=self.flags,
                                      force_group=self.force_group)
+
+
+    def expand(self, format: str = "csr", sort_indices: bool = True,
+               workspace: torch.Tensor | None = None):
+        """The matrix with one value per entry, as (ptr, idx, val) of its CSR
+        (``format="csr"``) or CSC (``"csc"``), index-sorted by default; see
+        ``vspmm_expand_vcs``."""
+        if format not in ("csr", "csc"):
+            raise ValueError("format must be 'csr' or 'csc'")
+        m, n = self.shape
+        nnz = self.indices.numel()
+        dev = self.device
+        ptr = torch.empty((m if format == "csr" else n) + 1, dtype=torch.int32, device=dev)
+        idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        val = torch.empty(max(nnz, 1), dtype=torch.float32, device=dev)
+        own = (format == "csr") == (self.layout == "vcsr")
+        ws = workspace
+        if ws is None and (sort_indices or not own):
+            ws = self.workspace("BA" if self.layout == "vcsr" else "AB")
+        st = lib.vspmm_expand_vcs(self._h, 0 if format == "csr" else 1, int(bool(sort_indices)),
+                                  _ptr(ptr), _ptr(idx), _ptr(val), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(dev))
+        _check(st, "vspmm_expand_vcs")
+        return ptr, idx[:nnz], val[:nnz]
 
 
 class CsrMatrix(SparseMatrix):

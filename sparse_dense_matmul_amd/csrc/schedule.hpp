@@ -204,6 +204,57 @@ k_expand(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vpt
     }
 }
 
+// ------------------------------------------------------------- expansion
+
+// Pointers of a VCS expanded to one value per entry: ptr[s] = value_ptr of
+// slice s's first group (s = 0 .. n_slices).
+__global__ void __launch_bounds__(256)
+k_expand_ptr(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
+             int *__restrict__ ptr) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int s = blockIdx.x * blockDim.x + threadIdx.x; s <= n_slices; s += stride)
+        ptr[s] = vptr[sptr[s]];
+}
+
+// A VCS expanded in stored order: idx_out[p] = idx[p], val_out[p] = the
+// value of p's group. One wave per slice, each lane with its own group cursor.
+__global__ void __launch_bounds__(256)
+k_expand_copy(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
+              const float *__restrict__ values, const int *__restrict__ idx,
+              int *__restrict__ idx_out, float *__restrict__ val_out) {
+    const int lane = threadIdx.x & 63;
+    const int waves = blockDim.x >> 6;
+    for (int s = blockIdx.x * waves + (threadIdx.x >> 6); s < n_slices; s += gridDim.x * waves) {
+        const int ka = sptr[s], kb = sptr[s + 1];
+        if (kb <= ka) continue;
+        const int e0 = vptr[ka], e1 = vptr[kb];
+        int kc = ka, kend = vptr[ka + 1];
+        for (int p = e0 + lane; p < e1; p += 64) {
+            while (p >= kend) {
+                ++kc;
+                kend = vptr[kc + 1];
+            }
+            idx_out[p] = idx[p];
+            val_out[p] = values[kc];
+        }
+    }
+}
+
+// Entries in sorted order (pay[q] = the stored position of the q-th):
+// idx_out[q] = src[pay[q]] (the entry's index, or its slice for the other
+// format), val_out[q] = the value of its group.
+__global__ void __launch_bounds__(256)
+k_expand_emit(int nnz, const int *__restrict__ pay, const int *__restrict__ src,
+              const int *__restrict__ group_of, const float *__restrict__ values,
+              int *__restrict__ idx_out, float *__restrict__ val_out) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < nnz; q += stride) {
+        const int p = pay[q];
+        idx_out[q] = src[p];
+        val_out[q] = values[group_of[p]];
+    }
+}
+
 // Order key of a float32 bit pattern: ascending value, -0 before +0, NaNs
 // beyond the infinities by payload. Equal keys iff equal bits.
 __device__ __forceinline__ uint32_t value_order(uint32_t bits) {

@@ -533,6 +533,50 @@ void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_pt
                            w.slice_of, (const float *)h.vals, t_idx, (float *)t_val);
 }
 
+// A VCS expanded to one value per entry (vsparse page, section "Benchmarks":
+// the expansion is index-sorted by default and takes a format). In the
+// layout's own format: stored order, or each slice sorted by index with two
+// stable radix sorts (by index, then by slice), so repeated indices keep their
+// stored order. In the other format: the exact transpose of the stored-order
+// expansion (a stable sort by index; each new slice lists its entries by
+// ascending old slice).
+void build_expand(const vspmm_matrix_s &h, bool own, bool sorted, const OppositeWs &w,
+                  int32_t *ptr, int32_t *idx_out, float *val_out, int n_cu, hipStream_t s) {
+    const int64_t nmaj = h.n_major(), nnz = h.nnz;
+    const float *values = static_cast<const float *>(h.vals);
+    const int grid = grid_for(std::max<int64_t>(nnz, 1), n_cu);
+    if (own) {
+        hipLaunchKernelGGL(k_expand_ptr, dim3(grid_for(nmaj + 1, n_cu)), dim3(256), 0, s,
+                           int(nmaj), h.sptr, h.vptr, ptr);
+        if (nnz <= 0) return;
+        if (!sorted) {
+            const int g = int(std::max<int64_t>(1, std::min<int64_t>((nmaj + 3) / 4, n_cu * 16)));
+            hipLaunchKernelGGL(k_expand_copy, dim3(g), dim3(256), 0, s, int(nmaj), h.sptr, h.vptr,
+                               values, h.idx, idx_out, val_out);
+            return;
+        }
+    } else if (nnz <= 0) {
+        bin_starts(nullptr, 0, h.n_minor(), ptr, n_cu, s);
+        return;
+    }
+    expand_slices(h, w, n_cu, s);
+    uint32_t *ka = w.keys_a, *kb = w.keys_b;
+    int32_t *pa = w.pay_a, *pb = w.pay_b;
+    hipLaunchKernelGGL(k_index_keys, dim3(grid), dim3(256), 0, s, int(nnz), h.idx, ka, pa);
+    radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
+    if (own) {
+        hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
+                           ka);
+        radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(nmaj), w.hist, w.bsums, s);
+        hipLaunchKernelGGL(k_expand_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, h.idx,
+                           w.group_of, values, idx_out, val_out);
+    } else {
+        bin_starts(ka, nnz, h.n_minor(), ptr, n_cu, s);
+        hipLaunchKernelGGL(k_expand_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
+                           w.group_of, values, idx_out, val_out);
+    }
+}
+
 // The VCS regrouped by the other axis into (t_major_ptr, t_values,
 // t_value_ptr, t_indices, t_n_groups).
 void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_major_ptr,
@@ -1132,6 +1176,27 @@ vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_va
     const DeviceInfo di = device_info(h->device);
     build_regroup(*h, carve_opposite(*h, ws), t_major_ptr, t_values, t_value_ptr, t_indices,
                   t_n_groups, di.ok ? di.n_cu : 256, stream);
+    return hip_status();
+}
+
+vspmm_status vspmm_expand_vcs(vspmm_matrix h, vspmm_format format, int32_t sort_indices,
+                              int32_t *ptr, int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                              hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (h->layout == VSPMM_CSR) return VSPMM_ERR_ENUM;
+    if (format != VSPMM_FORMAT_CSR && format != VSPMM_FORMAT_CSC) return VSPMM_ERR_ENUM;
+    const bool own = (format == VSPMM_FORMAT_CSR) == (h->layout == VSPMM_VCSR);
+    if (!ptr) return VSPMM_ERR_NULL;
+    if (h->nnz > 0 && (!idx || !val)) return VSPMM_ERR_NULL;
+    const bool needs_ws = !own || sort_indices;
+    if (needs_ws) {
+        const OppositeWs need = carve_opposite(*h, nullptr);
+        if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+        ws_drop(ws);  // ws no longer holds a cached layout
+    }
+    const DeviceInfo di = device_info(h->device);
+    build_expand(*h, own, sort_indices != 0, needs_ws ? carve_opposite(*h, ws) : OppositeWs{}, ptr,
+                 idx, val, di.ok ? di.n_cu : 256, stream);
     return hip_status();
 }
 
