@@ -233,6 +233,51 @@ def csr_products(dev, steps, copies=8):
                         "(log-normal rows), U(0,1) values; cold copies rotated", "products": out}
 
 
+def expansions(layouts, dev, steps, copies=8):
+    """VCS -> one value per entry on the device (vspmm_expand_vcs), beside the
+    headline: the 60k matrix from either layout into CSR or CSC, index-sorted
+    or in stored order, cold copies rotated. Bytes: the VCS read once plus
+    the expansion written, 4(n_major + 1) + 4 G_k + 4(G_k + 1) + 4 nnz
+    + 4(n_out_major + 1) + 8 nnz."""
+    import torch
+
+    import sparse_dense_matmul_amd as sdm
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    for lay, L in layouts.items():
+        hs = [sdm.VcsMatrix.from_arrays(lay, L.shape, *[up(a) for a in (L.major_ptr, L.values,
+                                                                       L.value_ptr, L.indices)])
+              for _ in range(copies)]
+        wss = [h.workspace("BA" if lay == "vcsr" else "AB") for h in hs]
+        m, n = L.shape
+        for fmt in ("csr", "csc"):
+            for sort in (True, False):
+                own = (fmt == "csr") == (lay == "vcsr")
+                if not own and not sort:
+                    continue  # the other format is always index-sorted
+                run = lambda k: hs[k % copies].expand(fmt, sort, workspace=wss[k % copies])
+                for k in range(copies):
+                    run(k)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for k in range(steps):
+                    run(k)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = 1e3 * a.elapsed_time(b) / steps
+                nb = L.nbytes() + 4 * ((m if fmt == "csr" else n) + 1) + 8 * L.nnz
+                key = f"{lay} -> {fmt}" + ("" if not own else (" sorted" if sort else " stored order"))
+                out[key] = {"us": round(us, 1), "GBps": round(nb / (us * 1e-6) / 1e9, 1)}
+        del hs, wss
+    return {"workload": "the 60k x 2k count matrix, 6,001,332 entries; outputs from torch's "
+                        "caching allocator (no device work), workspace given", "products": out}
+
+
 def other_widths(layouts, dev, widths, steps, copies=8):
     """The same four directions at other widths of the pages' workload (by
     default 1, 8, 32 and 64), beside the headline (not in it): each direction the way the
@@ -302,6 +347,7 @@ def main():
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-mode timings")
     ap.add_argument("--no-csr", action="store_true", help="skip the CSR operator timings")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-expand", action="store_true", help="skip the VCS expansion timings")
     ap.add_argument("--other-widths", default="1,8,32,64",
                     help="widths also timed beside the headline (comma list, empty for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -509,6 +555,9 @@ def main():
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_expand:
+        log("timing the expansions (reported beside the headline)")
+        result["expand"] = expansions(layouts, dev, args.steps)
     if args.other_widths:
         log("timing the other widths (reported beside the headline)")
         result["other_widths"] = other_widths(
