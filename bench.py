@@ -172,17 +172,21 @@ def csr_products(dev, steps, copies=8):
 
     out = {}
     stream = torch.cuda.current_stream(dev)
-    for np_t, tname in ((np.float32, "f32"), (np.float64, "f64")):
+    # (value type, dense type): float32 values summed in float64 as a third case
+    for np_t, d_t, tname in ((np.float32, np.float32, "f32"), (np.float64, np.float64, "f64"),
+                             (np.float32, np.float64, "f32 values, f64 sums")):
         _, C = W.config4(np_t)
         m, n = C.shape
-        s = np.dtype(np_t).itemsize
+        s = np.dtype(d_t).itemsize
+        sv = np.dtype(np_t).itemsize
         up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-        hs = [sdm.CsrMatrix.from_arrays(C.shape, up(C.row_ptr), up(C.col), up(C.val))
+        tdt = torch.float64 if d_t == np.float64 else torch.float32
+        hs = [sdm.CsrMatrix.from_arrays(C.shape, up(C.row_ptr), up(C.col), up(C.val), dtype=tdt)
               for _ in range(copies)]
         for w in (1, 32):
             for direction in ("AB", "BA"):
                 n_in, n_out = (n, m) if direction == "AB" else (m, n)
-                Bs = [up(np.random.default_rng(k).standard_normal((n_in, w)).astype(np_t))
+                Bs = [up(np.random.default_rng(k).standard_normal((n_in, w)).astype(d_t))
                       for k in range(copies)]
                 Os = [torch.empty((n_out, w), dtype=Bs[0].dtype, device=dev) for _ in range(copies)]
                 modes = ["atomic"] if direction == "AB" else ["atomic", "deterministic"]
@@ -202,7 +206,7 @@ def csr_products(dev, steps, copies=8):
                     b.record(stream)
                     torch.cuda.synchronize()
                     us = 1e3 * a.elapsed_time(b) / steps
-                    nbytes = 4 * (m + 1) + (4 + s) * C.nnz + s * w * (n_in + n_out)
+                    nbytes = 4 * (m + 1) + (4 + sv) * C.nnz + s * w * (n_in + n_out)
                     key = f"{tname} w={w} {'A@x' if direction == 'AB' else 'x@A'}" + \
                           ("" if direction == "AB" else f" {mode}")
                     out[key] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
@@ -213,7 +217,7 @@ def csr_products(dev, steps, copies=8):
         ws = h0.workspace("BA")
         t_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
         t_col = torch.empty(C.nnz, dtype=torch.int32, device=dev)
-        t_val = torch.empty(C.nnz, dtype=hs[0].dtype, device=dev)
+        t_val = torch.empty(C.nnz, dtype=hs[0].val.dtype, device=dev)
         ts = []
         for k in range(copies):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -78,7 +78,12 @@ typedef enum {
 
 typedef enum { VSPMM_CSR = 0, VSPMM_VCSR = 1, VSPMM_VCSC = 2 } vspmm_layout;
 typedef enum { VSPMM_AB = 0, VSPMM_BA = 1 } vspmm_direction;
-typedef enum { VSPMM_F32 = 0, VSPMM_F64 = 1 } vspmm_dtype;
+/* Element types of a CSR handle: VSPMM_F32 and VSPMM_F64 store values, take
+ * dense operands and carry sums in that type; VSPMM_F32_F64 stores float32
+ * values and takes float64 dense operands, with the sums in float64 (each
+ * value widened exactly; regridding page, section "Why not cuSPARSE", on
+ * summing float32 entries in float64). VCS handles are float32. */
+typedef enum { VSPMM_F32 = 0, VSPMM_F64 = 1, VSPMM_F32_F64 = 2 } vspmm_dtype;
 typedef enum { VSPMM_ATOMIC = 0, VSPMM_DETERMINISTIC = 1 } vspmm_mode;
 
 /* Creation flags. The lane split (vsparse page, section "The kernels";
@@ -116,9 +121,10 @@ vspmm_status vspmm_create_vcs(vspmm_matrix *h, vspmm_layout layout, int64_t n_ro
 
 /* Create a handle over a CSR held in device memory (rows are the major axis).
  *  row_ptr device int32[n_rows + 1]; col device int32[nnz];
- *  val device float[nnz] (VSPMM_F32) or double[nnz] (VSPMM_F64).
- *  The dense operands of every product on this handle have the same dtype
- *  and the sums are carried in it. Other arguments as vspmm_create_vcs.
+ *  val device float[nnz] (VSPMM_F32, VSPMM_F32_F64) or double[nnz]
+ *  (VSPMM_F64). The dense operands of every product on this handle are
+ *  float32 (VSPMM_F32) or float64 (VSPMM_F64, VSPMM_F32_F64), and the sums
+ *  are carried in that type. Other arguments as vspmm_create_vcs.
  *  The handle also holds, in device memory it owns (freed by vspmm_destroy):
  *  - one row range per wave of the short walk's grid (16 waves per CU), cut
  *    so the ranges hold about equal numbers of entries (a binary search over
@@ -204,7 +210,7 @@ vspmm_status vspmm_validate(vspmm_matrix h, hipStream_t stream);
  * page, section "How it is built": counts per row, then placement at the rows'
  * cursors in source order), equal bit for bit to a sequential counting sort.
  * Outputs (device): t_row_ptr int32[n_cols + 1], t_col int32[nnz], t_val of
- * the handle's dtype [nnz]. ws: device, vspmm_workspace_size(h, VSPMM_BA,
+ * the handle's value type [nnz] (float for VSPMM_F32_F64). ws: device, vspmm_workspace_size(h, VSPMM_BA,
  * VSPMM_DETERMINISTIC) bytes. Errors: _NULL, _ENUM (not CSR), _WORKSPACE,
  * _HIP. */
 vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_col,

@@ -346,14 +346,24 @@ class VcsMatrix(SparseMatrix):
 
 
 class CsrMatrix(SparseMatrix):
-    """CSR over device arrays, float32 or float64."""
+    """CSR over device arrays: float32 or float64 values; the dense operands
+    and the sums follow the values' type, or ``dtype=torch.float64`` with
+    float32 values sums them in float64 (``VSPMM_F32_F64``)."""
 
     @classmethod
-    def from_arrays(cls, shape, row_ptr, col, val, flags=0, force_group=0, validate=False):
+    def from_arrays(cls, shape, row_ptr, col, val, flags=0, force_group=0, validate=False,
+                    dtype=None):
         dev = torch.as_tensor(row_ptr).device
         val = torch.as_tensor(val)
         if val.dtype not in (torch.float32, torch.float64):
             raise TypeError(f"val must be float32 or float64, got {val.dtype}")
+        dtype = val.dtype if dtype is None else dtype
+        if dtype == val.dtype:
+            code = 1 if val.dtype == torch.float64 else 0
+        elif val.dtype == torch.float32 and dtype == torch.float64:
+            code = 2  # float32 values, float64 operands and sums
+        else:
+            raise TypeError(f"{val.dtype} values cannot be summed in {dtype}")
         row_ptr = _dev_tensor(row_ptr, torch.int32, dev, "row_ptr")
         col = _dev_tensor(col, torch.int32, dev, "col")
         val = _dev_tensor(val, val.dtype, dev, "val")
@@ -362,10 +372,9 @@ class CsrMatrix(SparseMatrix):
         h = _vp()
         with torch.cuda.device(dev):
             st = lib.vspmm_create_csr(ctypes.byref(h), m, n, col.numel(), _ptr(row_ptr),
-                                      _ptr(col), _ptr(val), 1 if val.dtype == torch.float64 else 0,
-                                      flags, force_group, _stream(dev))
+                                      _ptr(col), _ptr(val), code, flags, force_group, _stream(dev))
         _check(st, "vspmm_create_csr")
-        return cls(h, (row_ptr, col, val), (m, n), "csr", val.dtype, dev, flags, force_group)
+        return cls(h, (row_ptr, col, val), (m, n), "csr", dtype, dev, flags, force_group)
 
     @property
     def row_ptr(self):
@@ -387,10 +396,11 @@ class CsrMatrix(SparseMatrix):
         dev = self.device
         t_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
         t_col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
-        t_val = torch.empty(max(nnz, 1), dtype=self.dtype, device=dev)
+        t_val = torch.empty(max(nnz, 1), dtype=self.val.dtype, device=dev)
         ws = workspace if workspace is not None else self.workspace("BA")
         st = lib.vspmm_transpose_csr(self._h, _ptr(t_ptr), _ptr(t_col), _ptr(t_val), _ptr(ws),
                                      ws.numel(), _stream(dev))
         _check(st, "vspmm_transpose_csr")
         return CsrMatrix.from_arrays((n, m), t_ptr, t_col[:nnz], t_val[:nnz],
-                                     flags=self.flags & ~VALIDATE, force_group=self.force_group)
+                                     flags=self.flags & ~VALIDATE, force_group=self.force_group,
+                                     dtype=self.dtype)

@@ -77,7 +77,29 @@ struct WalkArgs {
     // CSR short walk: blocks added in front of the grid that walk the long
     // slices (kLongWaves waves per slice) in the same launch
     int long_blocks = 0;
+    // float32 CSR values with T = double: the sums run in float64 over the
+    // widened values (vals unused)
+    const float *vals32 = nullptr;
 };
+
+// Values of one type read as another (float32 CSR values summed in float64):
+// indexing widens each value; used as the `vals` operand where the walks take
+// a value-array type VP (a plain `const T *` otherwise).
+template <typename T, typename V>
+struct Widen {
+    const V *p;
+    __device__ __forceinline__ T operator[](int i) const { return T(p[i]); }
+};
+
+// Calls f with the walk's value array: the plain pointer, or, for float32
+// CSR values summed in float64 (T = double with vals32 set), a Widen view.
+template <typename T, typename Args, typename F>
+void with_vals(const Args &a, F &&f) {
+    if constexpr (sizeof(T) == 8) {
+        if (a.vals32) return f(Widen<T, float>{a.vals32});
+    }
+    f(a.vals);
+}
 
 // The operands of one scatter walk (slices of the walked layout = rows of B).
 template <typename T>
@@ -93,6 +115,7 @@ struct ScatterArgs {
     T *out;           // dense output, n_out x w, row-major, zeroed by the caller
     int w;
     int n_out;
+    const float *vals32 = nullptr;  // float32 CSR values with T = double (vals unused)
 };
 
 // Raises a kernel's dynamic LDS limit to a whole CU (once per kernel).

@@ -43,7 +43,9 @@ struct vspmm_matrix_s {
     int n_parts = 0;
     int64_t n_major() const { return layout == VSPMM_VCSC ? n_cols : n_rows; }
     int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
-    size_t elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
+    // bytes of a dense element (the type the sums run in) and of a stored value
+    size_t elt() const { return dtype == VSPMM_F32 ? 4 : 8; }
+    size_t val_elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
 };
 
 // Lets a kernel use up to the whole LDS of a CU as dynamic shared memory.
@@ -264,6 +266,16 @@ WalkArgs<T> walk_args(int64_t n_slices, const int32_t *sptr, const int32_t *vptr
     return a;
 }
 
+// For a float32-value CSR summed in float64: the walk reads its values (the
+// handle's, or the built transpose's) as float32 and widens each one.
+WalkArgs<double> values_of(const vspmm_matrix_s &h, WalkArgs<double> a) {
+    if (h.dtype == VSPMM_F32_F64) {
+        a.vals32 = reinterpret_cast<const float *>(a.vals);
+        a.vals = nullptr;
+    }
+    return a;
+}
+
 // Dispatches one aligned walk to its kernel family.
 template <typename T>
 void launch_aligned(bool vcs, const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
@@ -372,9 +384,13 @@ Plan scatter_plan(int64_t nnz, int64_t w, int64_t no, size_t elt, int n_cu, int 
 template <typename T>
 void launch_scatter_any(bool vcs, const Plan &pl, const vspmm_matrix_s &h, const void *B,
                         void *out, int w, int64_t no, hipStream_t s) {
-    const ScatterArgs<T> a{int(h.n_major()), int(h.n_groups), int(h.nnz), h.sptr, h.vptr,
-                           static_cast<const T *>(h.vals), h.idx, static_cast<const T *>(B),
-                           static_cast<T *>(out), w, int(no)};
+    ScatterArgs<T> a{int(h.n_major()), int(h.n_groups), int(h.nnz), h.sptr, h.vptr,
+                     static_cast<const T *>(h.vals), h.idx, static_cast<const T *>(B),
+                     static_cast<T *>(out), w, int(no)};
+    if (h.dtype == VSPMM_F32_F64) {  // float32 values summed in float64
+        a.vals32 = static_cast<const float *>(h.vals);
+        a.vals = nullptr;
+    }
     if constexpr (sizeof(T) == 4) {
         if (vcs) return launch_scatter<true, T>(pl, a, s);
     }
@@ -426,7 +442,7 @@ OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base, int64_t n_bins = 
     const bool vcs = h.layout != VSPMM_CSR;
     const bool tiled = partial_elems > 0;
     w.t_ptr = b.take<int32_t>(nb + 1);
-    w.t_vals = b.take<char>(nnz * h.elt());
+    w.t_vals = b.take<char>(nnz * h.val_elt());
     if (vcs) {
         w.t_vptr = b.take<int32_t>(nnz + 1);
         w.t_ngroups = b.take<int32_t>(1);
@@ -525,7 +541,7 @@ void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_pt
     hipLaunchKernelGGL(k_index_keys, dim3(grid), dim3(256), 0, s, int(h.nnz), h.idx, ka, pa);
     radix_sort(&ka, &pa, &kb, &pb, h.nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
     bin_starts(ka, h.nnz, h.n_minor(), t_ptr, n_cu, s);
-    if (h.dtype == VSPMM_F64)
+    if (h.val_elt() == 8)
         hipLaunchKernelGGL(k_transpose_emit<double>, dim3(grid), dim3(256), 0, s, int(h.nnz), pa,
                            w.slice_of, (const double *)h.vals, t_idx, (double *)t_val);
     else
@@ -838,9 +854,10 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         const int64_t ni = h.n_minor();
         const Plan pl = make_plan(h.n_major(), h.nnz, w, h.elt(), split_matrix, h.force_group,
                                   B, out, n_cu, ni, vcs);
-        if (h.dtype == VSPMM_F64)
-            launch_csr_or_vcs<double>(h, vcs, pl, walk_args<double>(h.n_major(), h.sptr, h.vptr,
-                                                                   h.vals, h.idx, B, out, w, ni),
+        if (h.dtype != VSPMM_F32)
+            launch_csr_or_vcs<double>(h, vcs, pl, values_of(h, walk_args<double>(
+                                                              h.n_major(), h.sptr, h.vptr,
+                                                              h.vals, h.idx, B, out, w, ni)),
                                       n_cu, s);
         else
             launch_csr_or_vcs<float>(h, vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr,
@@ -851,7 +868,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     if (mode == VSPMM_ATOMIC) {
         const Plan pl = scatter_plan(h.nnz, w, no, h.elt(), n_cu, h.force_group);
         launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
-        if (h.dtype == VSPMM_F64) launch_scatter_any<double>(vcs, pl, h, B, out, w, no, s);
+        if (h.dtype != VSPMM_F32) launch_scatter_any<double>(vcs, pl, h, B, out, w, no, s);
         else launch_scatter_any<float>(vcs, pl, h, B, out, w, no, s);
         return hip_status();
     }
@@ -875,9 +892,10 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     const int64_t nmaj = h.n_major();
     const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, B, out,
                               n_cu, nmaj, vcs);
-    if (h.dtype == VSPMM_F64)
-        launch_aligned<double>(false, pl, walk_args<double>(nmin, wl.t_ptr, nullptr, wl.t_vals,
-                                                            wl.t_idx, B, out, w, nmaj), s);
+    if (h.dtype != VSPMM_F32)
+        launch_aligned<double>(false, pl, values_of(h, walk_args<double>(nmin, wl.t_ptr, nullptr,
+                                                                         wl.t_vals, wl.t_idx, B,
+                                                                         out, w, nmaj)), s);
     else
         launch_aligned<float>(vcs, pl, walk_args<float>(nmin, wl.t_ptr, wl.t_vptr, wl.t_vals,
                                                         wl.t_idx, B, out, w, nmaj), s);
@@ -893,7 +911,8 @@ int csr_parts(int n_cu) { return 16 * std::max(n_cu, 1); }
 // than one round of the short walk (64 * 24 entries for float32, 64 * 12 for
 // float64). With entry-balanced row ranges a wave then walks about its share.
 int csr_long_len(int dtype, int64_t nnz, int n_parts) {
-    const int64_t round = dtype == VSPMM_F64 ? 64 * 12 : 64 * 24;
+    // (the walk's round holds 12 windows when the sums run in float64)
+    const int64_t round = dtype != VSPMM_F32 ? 64 * 12 : 64 * 24;
     const int64_t share = nnz / std::max(n_parts, 1);
     return int(std::min(round, std::max<int64_t>(64, share)));
 }
@@ -1037,7 +1056,7 @@ vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, i
                               vspmm_dtype dtype, uint32_t flags, int32_t force_group,
                               hipStream_t stream) {
     if (!h) return VSPMM_ERR_NULL;
-    if (dtype != VSPMM_F32 && dtype != VSPMM_F64) return VSPMM_ERR_ENUM;
+    if (dtype != VSPMM_F32 && dtype != VSPMM_F64 && dtype != VSPMM_F32_F64) return VSPMM_ERR_ENUM;
     if (flags & ~uint32_t(VSPMM_SPLIT_WIDTH | VSPMM_SPLIT_MATRIX | VSPMM_VALIDATE))
         return VSPMM_ERR_ENUM;
     if ((flags & VSPMM_SPLIT_WIDTH) && (flags & VSPMM_SPLIT_MATRIX)) return VSPMM_ERR_ENUM;
@@ -1202,7 +1221,7 @@ vspmm_status vspmm_expand_vcs(vspmm_matrix h, vspmm_format format, int32_t sort_
 
 vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_bytes) {
     if (vspmm_status st = check_handle(h)) return st;
-    const size_t nmaj = size_t(h->n_major()), nnz = size_t(h->nnz), e = h->elt();
+    const size_t nmaj = size_t(h->n_major()), nnz = size_t(h->nnz), e = h->val_elt();
     size_t own;
     if (h->layout == VSPMM_CSR)
         own = 4 * (nmaj + 1) + (4 + e) * nnz;

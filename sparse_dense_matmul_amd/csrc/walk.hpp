@@ -15,6 +15,8 @@
 
 namespace vspmm {
 
+
+
 template <typename T, int N>
 struct vec_of {
     typedef T type __attribute__((ext_vector_type(N)));
@@ -178,10 +180,9 @@ __device__ __forceinline__ void slot_reduce_sub(T (&acc)[VEC], int log_ww, int l
 // wave-uniform group cursor with readlane; otherwise each lane keeps its own
 // cursor. Calls body(p, index, value) for the lane's entry p of each step
 // (p >= e1 marks an idle lane).
-template <bool VCS, bool UNIFORM, typename T, typename Body>
+template <bool VCS, bool UNIFORM, typename T, typename VP, typename Body>
 __device__ __forceinline__ void walk_slice(int lane, int slot, int G, int ka, int kb, int e0,
-                                           int e1, const int *__restrict__ vptr,
-                                           const T *__restrict__ vals,
+                                           int e1, const int *__restrict__ vptr, VP vals,
                                            const int *__restrict__ idx, Body &&body) {
     if constexpr (!VCS) {
         // the next step's index and value are loaded (clamped to the slice)
@@ -253,10 +254,10 @@ __device__ __forceinline__ void walk_slice(int lane, int slot, int G, int ka, in
 //   sptr: CSR row pointers or VCS major_ptr; vptr: VCS value_ptr (unused for
 //   CSR); vals: CSR values or VCS group values; idx: minor indices;
 //   B: n_minor x w; out: n_slices x w.
-template <bool VCS, typename T, int VEC, bool UNIFORM>
+template <bool VCS, typename T, int VEC, bool UNIFORM, typename VP = const T *>
 __global__ void __launch_bounds__(256)
 k_aligned(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
-          const T *__restrict__ vals, const int *__restrict__ idx,
+          VP vals, const int *__restrict__ idx,
           const T *__restrict__ B, T *__restrict__ out, int w, Split sp, int long_len) {
     const int lane = threadIdx.x & 63;
     const int waves = blockDim.x >> 6;

@@ -155,10 +155,9 @@ struct Batch {
     T vv[NS];
 };
 
-template <bool VCS, typename T, int NS>
+template <bool VCS, typename T, int NS, typename VP>
 __device__ __forceinline__ void batch_load(Batch<T, NS> &b, int c, int e1, int G, int slot,
-                                           const T *__restrict__ vals,
-                                           const int *__restrict__ idx) {
+                                           VP vals, const int *__restrict__ idx) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int p = c + j * G + slot;
@@ -175,11 +174,11 @@ struct Pending {
     T b[NS][VEC];
 };
 
-template <bool VCS, typename T, int VEC, int NS>
+template <bool VCS, typename T, int VEC, int NS, typename VP>
 __device__ __forceinline__ void batch_issue(Pending<T, VEC, NS> &pd, const Batch<T, NS> &b, int c,
                                             int e1, int G, int slot, int col, bool act,
                                             Groups<T> &g, int lane, const int *__restrict__ vptr,
-                                            const T *__restrict__ vals, const T *Bs, int w) {
+                                            VP vals, const T *Bs, int w) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int q = c + j * G;
@@ -217,11 +216,10 @@ __device__ __forceinline__ void xor_reduce(T (&acc)[VEC], int from, int to) {
 // loading each next batch while the current one's gathers are in flight.
 // stride must be NS * G (a contiguous run), so the group cursor g, which must
 // sit at or before entry c, only moves forward.
-template <bool VCS, typename T, int VEC, int NS>
+template <bool VCS, typename T, int VEC, int NS, typename VP>
 __device__ __forceinline__ void run_batches(int c, int e1, int stride, int G, int slot, int col,
                                             bool act, Groups<T> &g, int lane,
-                                            const int *__restrict__ vptr,
-                                            const T *__restrict__ vals,
+                                            const int *__restrict__ vptr, VP vals,
                                             const int *__restrict__ idx, const T *Bs, int w,
                                             T (&acc)[VEC]) {
     if (c >= e1) return;
@@ -295,11 +293,10 @@ __device__ __forceinline__ void round_plan(Round &r, int sa, int s_end, int n_sl
     r.K1 = readlane(r.hp, last > 0 ? last : 1);
 }
 
-template <bool VCS, typename T, int NWR, int GWR>
+template <bool VCS, typename T, int NWR, int GWR, typename VP>
 __device__ __forceinline__ void round_load(const Round &r, int (&W)[NWR], T (&V)[NWR],
                                            int (&GS)[GWR], T (&GV)[GWR], int lane,
-                                           const int *__restrict__ vptr,
-                                           const T *__restrict__ vals,
+                                           const int *__restrict__ vptr, VP vals,
                                            const int *__restrict__ idx) {
 #pragma unroll
     for (int k = 0; k < NWR; ++k) {
@@ -476,11 +473,11 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
 
 // A slice too big for a round: walked alone, window by window, with the
 // plain per-step group cursor.
-template <bool VCS, typename T, int VEC, int SB>
+template <bool VCS, typename T, int VEC, int SB, typename VP>
 __device__ __forceinline__ void big_slice(int s, int lane, int slot, int cl, const Split &sp,
                                           const int *__restrict__ sptr,
                                           const int *__restrict__ vptr,
-                                          const T *__restrict__ vals, const int *__restrict__ idx,
+                                          VP vals, const int *__restrict__ idx,
                                           const T *Bs, T *__restrict__ out, int w) {
     const int G = 1 << sp.log_g;
     const int chunk = VEC << sp.log_ww;
@@ -548,11 +545,11 @@ __device__ __forceinline__ void big_slice(int s, int lane, int slot, int cl, con
 
 constexpr int kLongWaves = 8;  // waves walking one long slice (see long_walk)
 
-template <bool VCS, typename T, int VEC, int NC, int SBN, int NWR>
+template <bool VCS, typename T, int VEC, int NC, int SBN, int NWR, typename VP>
 __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
                                           const int *__restrict__ list, int group, int wave,
                                           T *part, const int *__restrict__ sptr,
-                                          const int *__restrict__ vptr, const T *__restrict__ vals,
+                                          const int *__restrict__ vptr, VP vals,
                                           const int *__restrict__ idx, const T *__restrict__ B,
                                           T *__restrict__ out, int w, Split sp);
 
@@ -563,10 +560,10 @@ __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
 // with skip_big, left to k_long over the list of such slices. NC width chunks
 // are walked together (1, 2 or 4, so that NC chunks cover the width or come
 // closest to it).
-template <bool VCS, typename T, int VEC, bool LDS_B, int NC>
+template <bool VCS, typename T, int VEC, bool LDS_B, int NC, typename VP = const T *>
 __global__ void __launch_bounds__(1024)
 k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
-        const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
+        VP vals, const int *__restrict__ idx, const T *__restrict__ B,
         T *__restrict__ out, int w, int n_in, Split sp, int skip_big, int long_len,
         const int *__restrict__ parts, int n_parts, const int *__restrict__ long_list,
         int n_long, int long_blocks) {
@@ -665,11 +662,11 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 // SBN steps have their gathers in flight together, and a pass loads NWR
 // windows; both set registers, not the arithmetic: a pass holds a multiple of
 // G entries, so each lane gets the same entries in the same order either way.
-template <bool VCS, typename T, int VEC, int NC, int SBN, int NWR>
+template <bool VCS, typename T, int VEC, int NC, int SBN, int NWR, typename VP>
 __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
                                           const int *__restrict__ list, int group, int wave,
                                           T *part, const int *__restrict__ sptr,
-                                          const int *__restrict__ vptr, const T *__restrict__ vals,
+                                          const int *__restrict__ vptr, VP vals,
                                           const int *__restrict__ idx, const T *__restrict__ B,
                                           T *__restrict__ out, int w, Split sp) {
     constexpr int PW = NC * 64 * VEC;  // part elements per wave
@@ -798,10 +795,10 @@ __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
 // k_long: one group (a block of kLongWaves waves) per slice, grid-stride over
 // the slices, or over the slices in `list` when it is given; requires
 // G * WW == 64.
-template <bool VCS, typename T, int VEC, int NC>
+template <bool VCS, typename T, int VEC, int NC, typename VP = const T *>
 __global__ void __launch_bounds__(64 * kLongWaves)
 k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
-       const T *__restrict__ vals, const int *__restrict__ idx, const T *__restrict__ B,
+       VP vals, const int *__restrict__ idx, const T *__restrict__ B,
        T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
     __shared__ T part[kLongWaves * NC * 64 * VEC];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

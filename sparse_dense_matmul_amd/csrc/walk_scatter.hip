@@ -102,9 +102,9 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, Rs...>, F 
     (f(std::integral_constant<int, Rs>{}), ...);
 }
 
-template <bool VCS, typename T, int LOG_WW, bool PRIV>
+template <bool VCS, typename T, int LOG_WW, bool PRIV, typename VP = const T *>
 __global__ void __launch_bounds__(1024)
-k_scatter(ScatterArgs<T> a) {
+k_scatter(ScatterArgs<T> a, VP vals) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     T *priv = reinterpret_cast<T *>(smem);
     const size_t n_el = size_t(a.n_out) * size_t(a.w);
@@ -136,9 +136,9 @@ k_scatter(ScatterArgs<T> a) {
         auto load = [&](int q_, int g0_, int s0_, int &gs_, T &gv_, int &ss_, int &ix_) {
             if constexpr (VCS) {
                 gs_ = a.vptr[lane < a.n_groups - g0_ ? g0_ + lane : a.n_groups];
-                gv_ = a.vals[lane < a.n_groups - g0_ ? g0_ + lane : a.n_groups - 1];
+                gv_ = vals[lane < a.n_groups - g0_ ? g0_ + lane : a.n_groups - 1];
             } else {
-                gv_ = a.vals[lane < nnz - q_ ? q_ + lane : nnz - 1];
+                gv_ = vals[lane < nnz - q_ ? q_ + lane : nnz - 1];
             }
             ss_ = a.sptr[lane < a.n_slices - s0_ ? s0_ + lane : a.n_slices];
             ix_ = a.idx[lane < nnz - q_ ? q_ + lane : nnz - 1];
@@ -283,14 +283,17 @@ void launch_scatter(const Plan &pl, const ScatterArgs<T> &a, hipStream_t s) {
     const dim3 g(pl.grid), b(pl.block);
 #define VSPMM_SCATTER(L, P)                                                                   \
     do {                                                                                      \
-        if (P) allow_lds(reinterpret_cast<const void *>(&k_scatter<VCS, T, L, P>));          \
-        hipLaunchKernelGGL((k_scatter<VCS, T, L, P>), g, b, P ? pl.lds_bytes : 0, s, a);     \
+        if (P) allow_lds(reinterpret_cast<const void *>(&k_scatter<VCS, T, L, P, VP>));      \
+        hipLaunchKernelGGL((k_scatter<VCS, T, L, P, VP>), g, b, P ? pl.lds_bytes : 0, s, a,  \
+                           vals);                                                             \
     } while (0)
 #define VSPMM_SCATTER_L(L)                                                                    \
     case L:                                                                                   \
         if (pl.lds) VSPMM_SCATTER(L, true);                                                   \
         else VSPMM_SCATTER(L, false);                                                         \
         break
+    with_vals<T>(a, [&](auto vals) {
+    using VP = decltype(vals);
     switch (pl.sp.log_ww) {
         VSPMM_SCATTER_L(0);
         VSPMM_SCATTER_L(1);
@@ -300,6 +303,7 @@ void launch_scatter(const Plan &pl, const ScatterArgs<T> &a, hipStream_t s) {
         VSPMM_SCATTER_L(5);
         default: VSPMM_SCATTER_L(6);
     }
+    });
 #undef VSPMM_SCATTER_L
 #undef VSPMM_SCATTER
 }

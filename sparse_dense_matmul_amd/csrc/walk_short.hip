@@ -22,18 +22,21 @@ void launch_short_nc(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     if (a.long_blocks > 0)
         lds = std::max(lds, size_t(pl.block / (64 * kLongWaves)) * kLongWaves * NC * 64 * VEC *
                                 sizeof(T));
-    if (pl.lds) {
-        allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true, NC>));
-        hipLaunchKernelGGL((k_short<false, T, VEC, true, NC>), g, b, lds, s, a.n_slices,
-                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
-                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
-                           a.n_long, a.long_blocks);
-    } else {
-        hipLaunchKernelGGL((k_short<false, T, VEC, false, NC>), g, b, lds, s, a.n_slices,
-                           a.sptr, a.vptr, a.vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
-                           a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
-                           a.n_long, a.long_blocks);
-    }
+    with_vals<T>(a, [&](auto vals) {
+        using VP = decltype(vals);
+        if (pl.lds) {
+            allow_lds(reinterpret_cast<const void *>(&k_short<false, T, VEC, true, NC, VP>));
+            hipLaunchKernelGGL((k_short<false, T, VEC, true, NC, VP>), g, b, lds, s, a.n_slices,
+                               a.sptr, a.vptr, vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
+                               a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
+                               a.n_long, a.long_blocks);
+        } else {
+            hipLaunchKernelGGL((k_short<false, T, VEC, false, NC, VP>), g, b, lds, s, a.n_slices,
+                               a.sptr, a.vptr, vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
+                               a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
+                               a.n_long, a.long_blocks);
+        }
+    });
 }
 
 // Width chunks walked together: the power of two (at most 4) that comes

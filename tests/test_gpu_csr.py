@@ -263,3 +263,44 @@ def test_row_ranges_and_long_rows(orc, dtype, case):
     batch = A.spmm(Bb, "AB")
     for c in (0, 13, 31):
         assert torch.equal(batch[:, c], A.spmm(Bb[:, c:c + 1].contiguous(), "AB")[:, 0]), (case, c)
+
+
+@pytest.mark.parametrize("width", [1, 8, 32])
+def test_float32_values_summed_in_float64(orc, regrid32, width):
+    """float32 values with float64 operands and sums (regridding page, section
+    "Why not cuSPARSE"): every value widens exactly, so each product equals,
+    bit for bit, the float64 handle over the widened values (the same walks),
+    and both match the oracle to float64 rounding. A@x, x@A atomic and
+    deterministic; batch columns equal solo products; the transpose keeps
+    float32 values."""
+    dev = need_gpu()
+    C = regrid32
+    m, n = C.shape
+    A = csr_handle(C, dev, dtype=torch.float64)
+    assert A.dtype == torch.float64 and A.val.dtype == torch.float32
+    C64 = W.Csr(C.shape, C.row_ptr, C.col, C.val.astype(np.float64))
+    A64 = csr_handle(C64, dev)
+    for direction in ("AB", "BA"):
+        rows = n if direction == "AB" else m
+        B = W.dense_normal(np.random.default_rng(width), rows, width, dtype=np.float64)
+        Bd = to_dev(B, dev)
+        modes = ["atomic"] if direction == "AB" else ["atomic", "deterministic"]
+        for mode in modes:
+            ws = A.workspace(direction, mode) if mode == "deterministic" else None
+            ws64 = A64.workspace(direction, mode) if mode == "deterministic" else None
+            out = A.spmm(Bd, direction, mode=mode, workspace=ws)
+            assert out.dtype == torch.float64
+            check_close(orc, C, direction, B, out, tol=1e-12, where=f"mixed {direction} {mode}")
+            if direction == "AB" or mode == "deterministic":
+                ref = A64.spmm(Bd, direction, mode=mode, workspace=ws64)
+                assert torch.equal(out, ref), (direction, mode, width)
+    if width == 32:
+        Bb = to_dev(W.dense_normal(np.random.default_rng(5), n, 32, dtype=np.float64), dev)
+        batch = A.spmm(Bb, "AB")
+        for c in (0, 9, 31):
+            assert torch.equal(batch[:, c], A.spmm(Bb[:, c:c + 1].contiguous(), "AB")[:, 0])
+        T = A.transpose()
+        assert T.val.dtype == torch.float32 and T.dtype == torch.float64
+        want = orc.transpose_csr(n, C.row_ptr, C.col, C.val)
+        assert np.array_equal(T.row_ptr.cpu().numpy(), want[0])
+        assert np.array_equal(T.val.cpu().numpy().view(np.uint32), want[2].view(np.uint32))
