@@ -255,6 +255,169 @@ k_expand_emit(int nnz, const int *__restrict__ pay, const int *__restrict__ src,
     }
 }
 
+// A VCS expanded with each slice's entries sorted by index (stable), one
+// block of BLOCK threads per slice (grid-stride). A slice of at most CAP
+// entries is sorted in LDS: keys (index << 32 | position in the slice) are
+// unique, so a bitonic sort gives the stable order; each entry's value comes
+// from its group through a per-thread cursor. A longer slice is sorted by the
+// block alone with a stable LSD radix sort on the index (8 bits per pass,
+// `bits` bits) through the workspace arrays ka/pa and kb/pb over the slice's
+// own range, its values staged in vb; then emitted.
+template <int BLOCK, int CAP>
+__global__ void __launch_bounds__(BLOCK)
+k_expand_sorted(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
+                const float *__restrict__ values, const int *__restrict__ idx, int bits,
+                uint32_t *__restrict__ ka, int *__restrict__ pa, uint32_t *__restrict__ kb,
+                int *__restrict__ pb, float *__restrict__ vb, int *__restrict__ idx_out,
+                float *__restrict__ val_out) {
+    constexpr int WAVES = BLOCK / 64;
+    __shared__ unsigned long long key[CAP];
+    __shared__ float val[CAP];
+    __shared__ int run[256];
+    __shared__ int wc[WAVES][256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int s = blockIdx.x; s < n_slices; s += gridDim.x) {
+        const int ka0 = sptr[s], kb0 = sptr[s + 1];
+        const int e0 = kb0 > ka0 ? vptr[ka0] : 0, e1 = kb0 > ka0 ? vptr[kb0] : 0;
+        const int n = e1 - e0;
+        if (n <= 0) continue;  // uniform in the block
+        if (n <= CAP) {
+            int N = 1;
+            while (N < n) N <<= 1;
+            int kc = ka0, kend = vptr[ka0 + 1];
+            for (int i = tid; i < N; i += BLOCK) {
+                if (i < n) {
+                    while (e0 + i >= kend) {
+                        ++kc;
+                        kend = vptr[kc + 1];
+                    }
+                    key[i] = ((unsigned long long)(uint32_t)idx[e0 + i] << 32) | (uint32_t)i;
+                    val[i] = values[kc];
+                } else {
+                    key[i] = ~0ull;
+                }
+            }
+            __syncthreads();
+            for (int k = 2; k <= N; k <<= 1) {
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    for (int i = tid; i < N; i += BLOCK) {
+                        const int ixj = i ^ j;
+                        if (ixj > i) {
+                            const unsigned long long a = key[i], b = key[ixj];
+                            if ((a > b) == ((i & k) == 0)) {
+                                key[i] = b;
+                                key[ixj] = a;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            for (int r = tid; r < n; r += BLOCK) {
+                const unsigned long long kk = key[r];
+                idx_out[e0 + r] = (int)(kk >> 32);
+                val_out[e0 + r] = val[(int)(kk & 0xffffffffu)];
+            }
+            __syncthreads();
+            continue;
+        }
+        // long slice: stage keys, positions and values, then radix passes
+        {
+            int kc = ka0, kend = vptr[ka0 + 1];
+            for (int i = tid; i < n; i += BLOCK) {
+                while (e0 + i >= kend) {
+                    ++kc;
+                    kend = vptr[kc + 1];
+                }
+                ka[e0 + i] = (uint32_t)idx[e0 + i];
+                pa[e0 + i] = i;
+                vb[e0 + i] = values[kc];
+            }
+        }
+        __syncthreads();
+        uint32_t *ks = ka, *kd = kb;
+        int *ps = pa, *pd = pb;
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        for (int shift = 0; shift < bits; shift += 8) {
+            for (int d = tid; d < 256; d += BLOCK) run[d] = 0;
+            __syncthreads();
+            for (int i = tid; i < n; i += BLOCK) atomicAdd(&run[(ks[e0 + i] >> shift) & 255u], 1);
+            __syncthreads();
+            {  // exclusive scan of the 256 digit counts: BPT per thread, then
+               // the threads' sums scanned across lanes and waves
+                constexpr int BPT = 256 / BLOCK;
+                int c[BPT], sum = 0;
+#pragma unroll
+                for (int q = 0; q < BPT; ++q) {
+                    c[q] = run[tid * BPT + q];
+                    sum += c[q];
+                }
+                int incl = sum;  // inclusive scan of sum over the wave's lanes
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
+                }
+                if (lane == 63) wc[0][wave] = incl;  // wave totals (wc is free here)
+                __syncthreads();
+                int before = incl - sum;
+                for (int w2 = 0; w2 < wave; ++w2) before += wc[0][w2];
+#pragma unroll
+                for (int q = 0; q < BPT; ++q) {
+                    run[tid * BPT + q] = before;
+                    before += c[q];
+                }
+            }
+            __syncthreads();
+            for (int d = tid; d < 256 * WAVES; d += BLOCK) wc[d / 256][d % 256] = 0;
+            __syncthreads();
+            for (int base = 0; base < n; base += BLOCK) {  // tiles in order: stable
+                const int i = base + tid;
+                const bool valid = i < n;
+                const uint32_t kk = valid ? ks[e0 + i] : 0u;
+                const int d = (int)((kk >> shift) & 255u);
+                uint64_t m = __ballot(valid);
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const bool bit = (d >> b) & 1;
+                    const uint64_t bb = __ballot(bit);
+                    m &= bit ? bb : ~bb;
+                }
+                const int wrank = __popcll(m & lt);
+                if (valid && wrank == 0) wc[wave][d] = __popcll(m);
+                __syncthreads();
+                if (valid) {
+                    int pos = run[d] + wrank;
+                    for (int w2 = 0; w2 < wave; ++w2) pos += wc[w2][d];
+                    kd[e0 + pos] = kk;
+                    pd[e0 + pos] = ps[e0 + i];
+                }
+                __syncthreads();
+                for (int dd = tid; dd < 256; dd += BLOCK) {
+                    int t = 0;
+                    for (int w2 = 0; w2 < WAVES; ++w2) {
+                        t += wc[w2][dd];
+                        wc[w2][dd] = 0;
+                    }
+                    run[dd] += t;
+                }
+                __syncthreads();
+            }
+            uint32_t *tk = ks;
+            ks = kd;
+            kd = tk;
+            int *tp = ps;
+            ps = pd;
+            pd = tp;
+        }
+        for (int r = tid; r < n; r += BLOCK) {
+            idx_out[e0 + r] = (int)ks[e0 + r];
+            val_out[e0 + r] = vb[e0 + ps[e0 + r]];
+        }
+        __syncthreads();
+    }
+}
+
 // Order key of a float32 bit pattern: ascending value, -0 before +0, NaNs
 // beyond the infinities by payload. Equal keys iff equal bits.
 __device__ __forceinline__ uint32_t value_order(uint32_t bits) {

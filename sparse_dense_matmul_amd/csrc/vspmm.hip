@@ -551,11 +551,11 @@ void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_pt
 
 // A VCS expanded to one value per entry (vsparse page, section "Benchmarks":
 // the expansion is index-sorted by default and takes a format). In the
-// layout's own format: stored order, or each slice sorted by index with two
-// stable radix sorts (by index, then by slice), so repeated indices keep their
-// stored order. In the other format: the exact transpose of the stored-order
-// expansion (a stable sort by index; each new slice lists its entries by
-// ascending old slice).
+// layout's own format: stored order, or each slice sorted by index (stable,
+// so repeated indices keep their stored order) by one block per slice. In the
+// other format: the exact transpose of the stored-order expansion (a global
+// stable sort by index; each new slice lists its entries by ascending old
+// slice).
 void build_expand(const vspmm_matrix_s &h, bool own, bool sorted, const OppositeWs &w,
                   int32_t *ptr, int32_t *idx_out, float *val_out, int n_cu, hipStream_t s) {
     const int64_t nmaj = h.n_major(), nnz = h.nnz;
@@ -571,6 +571,22 @@ void build_expand(const vspmm_matrix_s &h, bool own, bool sorted, const Opposite
                                values, h.idx, idx_out, val_out);
             return;
         }
+        // sorted: each slice by one block (in LDS, or a block radix sort
+        // through the workspace for a slice longer than the LDS holds)
+        const bool small = nnz / std::max<int64_t>(nmaj, 1) <= 128;
+        const int g = int(std::max<int64_t>(1, std::min<int64_t>(nmaj, int64_t(n_cu) *
+                                                                     (small ? 32 : 8))));
+        const int bits = key_bits(h.n_minor());
+        float *vb = reinterpret_cast<float *>(w.group_of);
+        if (small)
+            hipLaunchKernelGGL((k_expand_sorted<64, 512>), dim3(g), dim3(64), 0, s, int(nmaj),
+                               h.sptr, h.vptr, values, h.idx, bits, w.keys_a, w.pay_a, w.keys_b,
+                               w.pay_b, vb, idx_out, val_out);
+        else
+            hipLaunchKernelGGL((k_expand_sorted<256, 2048>), dim3(g), dim3(256), 0, s, int(nmaj),
+                               h.sptr, h.vptr, values, h.idx, bits, w.keys_a, w.pay_a, w.keys_b,
+                               w.pay_b, vb, idx_out, val_out);
+        return;
     } else if (nnz <= 0) {
         bin_starts(nullptr, 0, h.n_minor(), ptr, n_cu, s);
         return;
@@ -580,17 +596,9 @@ void build_expand(const vspmm_matrix_s &h, bool own, bool sorted, const Opposite
     int32_t *pa = w.pay_a, *pb = w.pay_b;
     hipLaunchKernelGGL(k_index_keys, dim3(grid), dim3(256), 0, s, int(nnz), h.idx, ka, pa);
     radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
-    if (own) {
-        hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
-                           ka);
-        radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(nmaj), w.hist, w.bsums, s);
-        hipLaunchKernelGGL(k_expand_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, h.idx,
-                           w.group_of, values, idx_out, val_out);
-    } else {
-        bin_starts(ka, nnz, h.n_minor(), ptr, n_cu, s);
-        hipLaunchKernelGGL(k_expand_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
-                           w.group_of, values, idx_out, val_out);
-    }
+    bin_starts(ka, nnz, h.n_minor(), ptr, n_cu, s);
+    hipLaunchKernelGGL(k_expand_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
+                       w.group_of, values, idx_out, val_out);
 }
 
 // The VCS regrouped by the other axis into (t_major_ptr, t_values,

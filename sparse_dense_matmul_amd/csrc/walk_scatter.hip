@@ -293,16 +293,16 @@ void launch_scatter(const Plan &pl, const ScatterArgs<T> &a, hipStream_t s) {
         else VSPMM_SCATTER(L, false);                                                         \
         break
     with_vals<T>(a, [&](auto vals) {
-    using VP = decltype(vals);
-    switch (pl.sp.log_ww) {
-        VSPMM_SCATTER_L(0);
-        VSPMM_SCATTER_L(1);
-        VSPMM_SCATTER_L(2);
-        VSPMM_SCATTER_L(3);
-        VSPMM_SCATTER_L(4);
-        VSPMM_SCATTER_L(5);
-        default: VSPMM_SCATTER_L(6);
-    }
+        using VP = decltype(vals);
+        switch (pl.sp.log_ww) {
+            VSPMM_SCATTER_L(0);
+            VSPMM_SCATTER_L(1);
+            VSPMM_SCATTER_L(2);
+            VSPMM_SCATTER_L(3);
+            VSPMM_SCATTER_L(4);
+            VSPMM_SCATTER_L(5);
+            default: VSPMM_SCATTER_L(6);
+        }
     });
 #undef VSPMM_SCATTER_L
 #undef VSPMM_SCATTER

@@ -86,3 +86,28 @@ def test_expand_overwrites_a_built_schedule(orc, count60k):
     check(orc, L, A, "csr", True, ws=ws)
     again = A.spmm(B, "BA", mode="deterministic", workspace=ws)
     assert torch.equal(again, first)
+
+
+def _vcs_from_lengths(lengths, n, layout, seed):
+    rng = np.random.default_rng(seed)
+    rows, cols = W.sample_columns(rng, np.asarray(lengths), n)
+    vals = rng.integers(1, 10, size=rows.size).astype(np.float32)
+    return W.build_vcs(W.Triplets((len(lengths), n), rows, cols, vals), layout)
+
+
+@pytest.mark.parametrize("case", ["long_mean", "short_mean_with_long"])
+def test_expand_sorted_every_slice_path(orc, case):
+    """The sorted expansion sorts a slice in LDS when it fits (up to 512 entries
+    with 64-thread blocks, chosen when the mean slice holds at most 128, else
+    up to 2,048 with 256 threads) and by a block radix sort otherwise: rows of
+    0 to 3,000 entries (mean ~1,500), and Poisson(40) rows with 20 rows of 600
+    to 2,000 entries, cover all four."""
+    dev = need_gpu()
+    rng = np.random.default_rng(5)
+    if case == "long_mean":
+        lengths = rng.integers(0, 3_001, size=300)
+    else:
+        lengths = rng.poisson(40, size=3_000)
+        lengths[rng.choice(3_000, 20, replace=False)] = rng.integers(600, 2_001, size=20)
+    L = _vcs_from_lengths(lengths, 4_000, "vcsr", seed=len(lengths))
+    check(orc, L, vcs_handle(L, dev), "csr", True)
