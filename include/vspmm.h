@@ -144,6 +144,41 @@ vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, i
                               vspmm_dtype dtype, uint32_t flags, int32_t force_group,
                               hipStream_t stream);
 
+/* Create a handle over a CSR with int64 row pointers and int32 column
+ * indices, for matrices of more than 2^31 - 1 entries (regridding page,
+ * section "Why not cuSPARSE": row pointers must be int64 past 2^31 entries,
+ * while the column indices can stay int32).
+ *  row_ptr device int64[n_rows + 1]; col device int32[nnz]; val device
+ *  float[nnz] or double[nnz] as for vspmm_create_csr. nnz may exceed int32;
+ *  n_rows and n_cols may not.
+ *  block_nnz   0, or 1 .. 2^30: entries per row block (0 = 2^30).
+ * The rows are cut into blocks of whole rows, each of at most block_nnz
+ * entries (a single longer row forms a block of its own, up to 2^30 entries),
+ * and each block becomes an int32 CSR handle over the same col and val arrays
+ * from its first entry on (rebased row pointers in device memory the handle
+ * owns). Creation copies row_ptr to the host (one wait on `stream`), checks
+ * that it starts at 0, does not decrease and ends at nnz, and creates the
+ * blocks as vspmm_create_csr does (flags and force_group apply to each).
+ * Products:
+ *  - A @ B: each block writes its own rows of out; rows repeat bit for bit and
+ *    equal the int32 handle's over the same rows when the blocks cut nothing.
+ *  - B @ A, atomic: out is zeroed once and every block scatters into it.
+ *  - B @ A, deterministic: block 0's product is written to out and each later
+ *    block's product (into the workspace) is added to it in block order, so
+ *    the result repeats bit for bit. The workspace holds 256 bytes, each
+ *    block's exact transpose and, with two or more non-empty blocks, an
+ *    n_cols x width buffer: vspmm_workspace_size_width gives the whole;
+ *    vspmm_workspace_size gives it without the buffer (enough for one
+ *    non-empty block).
+ * vspmm_validate checks every block; vspmm_plan_info reports block 0's plan;
+ * vspmm_transpose_csr returns VSPMM_ERR_UNSUPPORTED (its row pointers are
+ * int32). Errors: as vspmm_create_csr, plus _STRUCTURE (row_ptr as above) and
+ * _UNSUPPORTED (a row of more than 2^30 entries). */
+vspmm_status vspmm_create_csr64(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                                const int64_t *row_ptr, const int32_t *col, const void *val,
+                                vspmm_dtype dtype, uint32_t flags, int32_t force_group,
+                                int64_t block_nnz, hipStream_t stream);
+
 /* Release the handle: its host metadata and, for CSR, the device arrays it
  * owns (row ranges and long-row list). The borrowed arrays are untouched. */
 vspmm_status vspmm_destroy(vspmm_matrix h);

@@ -39,6 +39,8 @@ EXPORTS = {
                           _i32, _vp], ctypes.c_int),
     "vspmm_create_csr": ([_P(_vp), _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_int, _u32, _i32, _vp],
                          ctypes.c_int),
+    "vspmm_create_csr64": ([_P(_vp), _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_int, _u32, _i32,
+                            _i64, _vp], ctypes.c_int),
     "vspmm_destroy": ([_vp], ctypes.c_int),
     "vspmm_spmm": ([_vp, _vp, _vp, _i64, ctypes.c_int, _vp], ctypes.c_int),
     "vspmm_workspace_size": ([_vp, ctypes.c_int, ctypes.c_int, _P(_sz)], ctypes.c_int),
@@ -348,11 +350,13 @@ class VcsMatrix(SparseMatrix):
 class CsrMatrix(SparseMatrix):
     """CSR over device arrays: float32 or float64 values; the dense operands
     and the sums follow the values' type, or ``dtype=torch.float64`` with
-    float32 values sums them in float64 (``VSPMM_F32_F64``)."""
+    float32 values sums them in float64 (``VSPMM_F32_F64``). ``ptr64=True`` (implied
+    past 2^31 - 1 entries) keeps int64 row pointers: the rows are cut into blocks
+    of at most ``block_nnz`` entries (0: 2^30), each walked as an int32 CSR."""
 
     @classmethod
     def from_arrays(cls, shape, row_ptr, col, val, flags=0, force_group=0, validate=False,
-                    dtype=None):
+                    dtype=None, ptr64=False, block_nnz=0):
         dev = torch.as_tensor(row_ptr).device
         val = torch.as_tensor(val)
         if val.dtype not in (torch.float32, torch.float64):
@@ -364,16 +368,23 @@ class CsrMatrix(SparseMatrix):
             code = 2  # float32 values, float64 operands and sums
         else:
             raise TypeError(f"{val.dtype} values cannot be summed in {dtype}")
-        row_ptr = _dev_tensor(row_ptr, torch.int32, dev, "row_ptr")
+        ptr64 = ptr64 or torch.as_tensor(col).numel() > 2**31 - 1
+        row_ptr = _dev_tensor(row_ptr, torch.int64 if ptr64 else torch.int32, dev, "row_ptr")
         col = _dev_tensor(col, torch.int32, dev, "col")
         val = _dev_tensor(val, val.dtype, dev, "val")
         m, n = (int(x) for x in shape)
         flags = flags | (VALIDATE if validate else 0)
         h = _vp()
         with torch.cuda.device(dev):
-            st = lib.vspmm_create_csr(ctypes.byref(h), m, n, col.numel(), _ptr(row_ptr),
-                                      _ptr(col), _ptr(val), code, flags, force_group, _stream(dev))
-        _check(st, "vspmm_create_csr")
+            if ptr64:
+                st = lib.vspmm_create_csr64(ctypes.byref(h), m, n, col.numel(), _ptr(row_ptr),
+                                            _ptr(col), _ptr(val), code, flags, force_group,
+                                            block_nnz, _stream(dev))
+            else:
+                st = lib.vspmm_create_csr(ctypes.byref(h), m, n, col.numel(), _ptr(row_ptr),
+                                          _ptr(col), _ptr(val), code, flags, force_group,
+                                          _stream(dev))
+        _check(st, "vspmm_create_csr64" if ptr64 else "vspmm_create_csr")
         return cls(h, (row_ptr, col, val), (m, n), "csr", dtype, dev, flags, force_group)
 
     @property

@@ -653,6 +653,15 @@ __global__ void __launch_bounds__(256) k_zero(uint32_t *__restrict__ p, size_t n
     if (t < n_words - tail0) p[tail0 + t] = 0;
 }
 
+// out[i] += src[i] for i < n (the fixed-order sum of row-block products).
+template <typename T>
+__global__ void __launch_bounds__(256) k_accumulate(T *__restrict__ out, const T *__restrict__ src,
+                                                    size_t n) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        out[i] += src[i];
+}
+
 // Structure checks: flag bit 1 = pointer array does not start at 0, bit 2 =
 // decreasing, bit 4 = last pointer differs from count, bit 8 = index out of
 // range.

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <new>
 #include <unordered_map>
+#include <vector>
 
 #include "vspmm.h"
 #include "launch.hpp"
@@ -41,6 +42,14 @@ struct vspmm_matrix_s {
     // grid (16 waves per CU), device array of n_parts + 1 (owned)
     int32_t *parts = nullptr;
     int n_parts = 0;
+    // CSR created with int64 row pointers: the rows are cut into blocks of at
+    // most 2^30 entries, each an int32 CSR handle (owned) over the same col
+    // and val arrays from its first entry on; block_row0 holds each block's
+    // first row and then n_rows, block_ptr the blocks' rebased row pointers
+    bool ptr64 = false;
+    std::vector<vspmm_matrix_s *> blocks;
+    std::vector<int64_t> block_row0;
+    int32_t *block_ptr = nullptr;
     int64_t n_major() const { return layout == VSPMM_VCSC ? n_cols : n_rows; }
     int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
     // bytes of a dense element (the type the sums run in) and of a stored value
@@ -129,6 +138,10 @@ int key_bits(int64_t n_keys) {  // bits holding every key in [0, n_keys)
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Entries per row block of an int64 CSR at most (int32 offsets inside a
+// block keep clear of overflow, e.g. a position plus a round of windows).
+constexpr int64_t kBlockMaxNnz = int64_t(1) << 30;
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -836,8 +849,14 @@ vspmm_status check_product(const vspmm_matrix_s &h, const void *B, void *out, in
     return VSPMM_OK;
 }
 
+vspmm_status run_blocked(const vspmm_matrix_s &h, const void *B, void *out, int w, int dir,
+                         int mode, void *ws, size_t ws_bytes, hipStream_t s);
+
+// One product. With `accumulate`, a misaligned atomic product adds into out
+// instead of overwriting it (used for the row blocks of an int64 CSR).
 vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int64_t width,
-                         int dir, int mode, void *ws, size_t ws_bytes, hipStream_t s) {
+                         int dir, int mode, void *ws, size_t ws_bytes, hipStream_t s,
+                         bool accumulate = false) {
     vspmm_status st = check_product(h, B, out, width, dir);
     if (st) return st;
     if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
@@ -850,9 +869,10 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
                               (!vcs && !(h.flags & VSPMM_SPLIT_WIDTH));
     const int w = int(width);
     if (h.nnz == 0) {
-        launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
+        if (!accumulate) launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
         return hip_status();
     }
+    if (h.ptr64) return run_blocked(h, B, out, w, dir, mode, ws, ws_bytes, s);
     if (mode == VSPMM_DETERMINISTIC && ws && aligned(ws, 256)) {
         const TilePlan tp = tile_plan(h, dir, w, n_cu, split_matrix, B, ws);
         if (tp.ok && ws_bytes >= tiled_ws_bytes(h, tp, w))
@@ -875,7 +895,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     }
     if (mode == VSPMM_ATOMIC) {
         const Plan pl = scatter_plan(h.nnz, w, no, h.elt(), n_cu, h.force_group);
-        launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
+        if (!accumulate) launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
         if (h.dtype != VSPMM_F32) launch_scatter_any<double>(vcs, pl, h, B, out, w, no, s);
         else launch_scatter_any<float>(vcs, pl, h, B, out, w, no, s);
         return hip_status();
@@ -907,6 +927,104 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     else
         launch_aligned<float>(vcs, pl, walk_args<float>(nmin, wl.t_ptr, wl.t_vptr, wl.t_vals,
                                                         wl.t_idx, B, out, w, nmaj), s);
+    return hip_status();
+}
+
+// Workspace of a deterministic B @ A over an int64 CSR: 256 bytes, one
+// region per row block for its exact transpose, then (with more than one non-empty block)
+// the n_cols x width buffer each later block's product lands in before it is
+// added to out.
+struct BlockedWs {
+    std::vector<void *> sub;
+    std::vector<size_t> sub_bytes;
+    void *sum = nullptr;
+    size_t bytes = 0;
+};
+
+BlockedWs carve_blocked(const vspmm_matrix_s &h, void *base, int64_t width) {
+    BlockedWs L;
+    // the first 256 bytes stay unused: the workspace cache tags base itself
+    // with this handle, and block 0's region with block 0
+    size_t off = 256;
+    int live = 0;
+    for (const vspmm_matrix_s *b : h.blocks) {
+        const size_t nb = b->nnz > 0 ? align256(carve_opposite(*b, nullptr).bytes) : 0;
+        L.sub.push_back(base ? static_cast<char *>(base) + off : nullptr);
+        L.sub_bytes.push_back(nb);
+        off += nb;
+        live += b->nnz > 0;
+    }
+    if (live > 1 && width > 0) {
+        L.sum = base ? static_cast<char *>(base) + off : nullptr;
+        off += align256(size_t(h.n_cols) * size_t(width) * h.elt());
+    }
+    L.bytes = off;
+    return L;
+}
+
+// A product over an int64 CSR, block by block. A @ B: each block writes its
+// own rows of out. B @ A: each block meets its rows of B and adds into all of
+// out, with atomics (out zeroed once), or, deterministically, block 0's
+// product written to out and each later block's added to it in block order,
+// so the sum repeats bit for bit.
+vspmm_status run_blocked(const vspmm_matrix_s &h, const void *B, void *out, int w, int dir,
+                         int mode, void *ws, size_t ws_bytes, hipStream_t s) {
+    const size_t e = h.elt();
+    const size_t nb = h.blocks.size();
+    if (dir == VSPMM_AB) {
+        for (size_t b = 0; b < nb; ++b) {
+            void *o = static_cast<char *>(out) + size_t(h.block_row0[b]) * size_t(w) * e;
+            if (vspmm_status st = run_product(*h.blocks[b], B, o, w, dir, mode, nullptr, 0, s))
+                return st;
+        }
+        return VSPMM_OK;
+    }
+    const size_t n_el = size_t(h.n_cols) * size_t(w);
+    auto b_rows = [&](size_t b) {
+        return static_cast<const char *>(B) + size_t(h.block_row0[b]) * size_t(w) * e;
+    };
+    if (mode == VSPMM_ATOMIC) {
+        launch_zero(out, n_el * e, s);
+        for (size_t b = 0; b < nb; ++b) {
+            if (h.blocks[b]->nnz == 0) continue;
+            if (vspmm_status st = run_product(*h.blocks[b], b_rows(b), out, w, dir, mode, nullptr,
+                                              0, s, true))
+                return st;
+        }
+        return hip_status();
+    }
+    const BlockedWs need = carve_blocked(h, nullptr, w);
+    if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+    const BlockedWs L = carve_blocked(h, ws, w);
+    // a workspace that does not hold this handle's transposes makes every
+    // block build its own again
+    if (!ws_claim(ws, WsKey{h.id, dir, 0}))
+        for (size_t b = 0; b < nb; ++b)
+            if (L.sub_bytes[b]) ws_drop(L.sub[b]);
+    const DeviceInfo di = device_info(h.device);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    bool first = true;
+    for (size_t b = 0; b < nb; ++b) {
+        if (h.blocks[b]->nnz == 0) continue;
+        void *dst = first ? out : L.sum;
+        if (vspmm_status st = run_product(*h.blocks[b], b_rows(b), dst, w, dir, mode, L.sub[b],
+                                          L.sub_bytes[b], s)) {
+            ws_drop(ws);
+            return st;
+        }
+        if (!first) {
+            const unsigned g = (unsigned)std::min<size_t>((n_el + 255) / 256, size_t(n_cu) * 8);
+            if (e == 8)
+                hipLaunchKernelGGL(k_accumulate<double>, dim3(g), dim3(256), 0, s,
+                                   static_cast<double *>(out), static_cast<const double *>(L.sum),
+                                   n_el);
+            else
+                hipLaunchKernelGGL(k_accumulate<float>, dim3(g), dim3(256), 0, s,
+                                   static_cast<float *>(out), static_cast<const float *>(L.sum),
+                                   n_el);
+        }
+        first = false;
+    }
     return hip_status();
 }
 
@@ -975,6 +1093,8 @@ vspmm_status list_long_rows(vspmm_matrix_s *m, hipStream_t s) {
 void free_handle(vspmm_matrix_s *m) {
     if (m->long_rows) (void)hipFree(m->long_rows);
     if (m->parts) (void)hipFree(m->parts);
+    for (vspmm_matrix_s *b : m->blocks) vspmm_destroy(b);
+    if (m->block_ptr) (void)hipFree(m->block_ptr);
     delete m;
 }
 
@@ -1092,6 +1212,111 @@ vspmm_status vspmm_create_csr(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, i
     return finish_create(m, h, stream);
 }
 
+vspmm_status vspmm_create_csr64(vspmm_matrix *h, int64_t n_rows, int64_t n_cols, int64_t nnz,
+                                const int64_t *row_ptr, const int32_t *col, const void *val,
+                                vspmm_dtype dtype, uint32_t flags, int32_t force_group,
+                                int64_t block_nnz, hipStream_t stream) {
+    if (!h) return VSPMM_ERR_NULL;
+    if (dtype != VSPMM_F32 && dtype != VSPMM_F64 && dtype != VSPMM_F32_F64) return VSPMM_ERR_ENUM;
+    if (flags & ~uint32_t(VSPMM_SPLIT_WIDTH | VSPMM_SPLIT_MATRIX | VSPMM_VALIDATE))
+        return VSPMM_ERR_ENUM;
+    if ((flags & VSPMM_SPLIT_WIDTH) && (flags & VSPMM_SPLIT_MATRIX)) return VSPMM_ERR_ENUM;
+    if (!fits_i32(n_rows) || !fits_i32(n_cols) || n_rows + 1 > kI32Max || n_cols + 1 > kI32Max ||
+        nnz < 0)
+        return VSPMM_ERR_DIM;
+    if (block_nnz == 0) block_nnz = kBlockMaxNnz;
+    if (block_nnz < 1 || block_nnz > kBlockMaxNnz) return VSPMM_ERR_DIM;
+    if (force_group < 0 || force_group > 64 || (force_group & (force_group - 1)))
+        return VSPMM_ERR_DIM;
+    if (!row_ptr) return VSPMM_ERR_NULL;
+    if (nnz > 0 && (!col || !val)) return VSPMM_ERR_NULL;
+    // the row pointers on the host: their checks and the block cuts
+    std::vector<int64_t> rp;
+    try {
+        rp.resize(size_t(n_rows) + 1);
+    } catch (...) {
+        return VSPMM_ERR_ALLOC;
+    }
+    if (hipMemcpyAsync(rp.data(), row_ptr, rp.size() * sizeof(int64_t), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return VSPMM_ERR_HIP;
+    if (rp[0] != 0 || rp[size_t(n_rows)] != nnz) return VSPMM_ERR_STRUCTURE;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rp[size_t(r) + 1] < rp[size_t(r)]) return VSPMM_ERR_STRUCTURE;
+    auto *m = new (std::nothrow) vspmm_matrix_s{};
+    if (!m) return VSPMM_ERR_ALLOC;
+    m->layout = VSPMM_CSR;
+    m->n_rows = n_rows;
+    m->n_cols = n_cols;
+    m->nnz = nnz;
+    m->sptr = nullptr;
+    m->vals = val;
+    m->idx = col;
+    m->dtype = dtype;
+    m->flags = flags;
+    m->force_group = force_group;
+    m->ptr64 = true;
+    if (hipGetDevice(&m->device) != hipSuccess) {
+        delete m;
+        return VSPMM_ERR_HIP;
+    }
+    m->id = g_next_id.fetch_add(1);
+    // blocks of whole rows, each of at most block_nnz entries unless one row
+    // alone holds more (then at most 2^30)
+    std::vector<int32_t> ptr32;
+    try {
+        for (int64_t r0 = 0; r0 < n_rows;) {
+            int64_t r1 = r0 + 1;
+            while (r1 < n_rows && rp[size_t(r1) + 1] - rp[size_t(r0)] <= block_nnz) ++r1;
+            if (rp[size_t(r1)] - rp[size_t(r0)] > kBlockMaxNnz) {
+                free_handle(m);
+                return VSPMM_ERR_UNSUPPORTED;
+            }
+            m->block_row0.push_back(r0);
+            for (int64_t r = r0; r <= r1; ++r)
+                ptr32.push_back(int32_t(rp[size_t(r)] - rp[size_t(r0)]));
+            r0 = r1;
+        }
+        m->block_row0.push_back(n_rows);
+    } catch (...) {
+        free_handle(m);
+        return VSPMM_ERR_ALLOC;
+    }
+    if (!ptr32.empty()) {
+        if (hipMalloc(&m->block_ptr, ptr32.size() * sizeof(int32_t)) != hipSuccess) {
+            m->block_ptr = nullptr;
+            free_handle(m);
+            return VSPMM_ERR_HIP;
+        }
+        if (hipMemcpyAsync(m->block_ptr, ptr32.data(), ptr32.size() * sizeof(int32_t),
+                           hipMemcpyHostToDevice, stream) != hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess) {
+            free_handle(m);
+            return VSPMM_ERR_HIP;
+        }
+    }
+    const size_t ve = m->val_elt();
+    size_t off = 0;
+    for (size_t b = 0; b + 1 < m->block_row0.size(); ++b) {
+        const int64_t r0 = m->block_row0[b], r1 = m->block_row0[b + 1];
+        const int64_t e0 = rp[size_t(r0)], nb = rp[size_t(r1)] - e0;
+        vspmm_matrix sub = nullptr;
+        const vspmm_status st = vspmm_create_csr(
+            &sub, r1 - r0, n_cols, nb, m->block_ptr + off, nb > 0 ? col + e0 : nullptr,
+            nb > 0 ? static_cast<const char *>(val) + size_t(e0) * ve : nullptr, dtype, flags,
+            force_group, stream);
+        if (st) {
+            free_handle(m);
+            return st;
+        }
+        m->blocks.push_back(sub);
+        off += size_t(r1 - r0) + 1;
+    }
+    *h = m;
+    return VSPMM_OK;
+}
+
 vspmm_status vspmm_destroy(vspmm_matrix h) {
     if (!h) return VSPMM_ERR_NULL;
     {
@@ -1117,6 +1342,11 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
     if (!bytes) return VSPMM_ERR_NULL;
     if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
     if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
+    if (h->ptr64) {
+        *bytes = mode == VSPMM_DETERMINISTIC && dir == VSPMM_BA ? carve_blocked(*h, nullptr, 0).bytes
+                                                                : 0;
+        return VSPMM_OK;
+    }
     *bytes = (mode == VSPMM_DETERMINISTIC && !is_aligned(*h, dir))
                  ? carve_opposite(*h, nullptr).bytes
                  : 0;
@@ -1140,6 +1370,10 @@ vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vsp
     if (vspmm_status st = vspmm_workspace_size(h, dir, mode, bytes)) return st;
     if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
     if (mode != VSPMM_DETERMINISTIC) return VSPMM_OK;
+    if (h->ptr64) {
+        if (dir == VSPMM_BA) *bytes = carve_blocked(*h, nullptr, width).bytes;
+        return VSPMM_OK;
+    }
     const DeviceInfo di = device_info(h->device);
     const bool split_matrix = (h->flags & VSPMM_SPLIT_MATRIX) != 0;
     alignas(256) static const float probe[64] = {};
@@ -1150,6 +1384,13 @@ vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vsp
 
 vspmm_status vspmm_validate(vspmm_matrix h, hipStream_t stream) {
     if (vspmm_status st = check_handle(h)) return st;
+    if (h->ptr64) {
+        // the int64 row pointers were checked at creation; each block checks
+        // its indices (and its rebased pointers)
+        for (vspmm_matrix_s *b : h->blocks)
+            if (vspmm_status st = vspmm_validate(b, stream)) return st;
+        return VSPMM_OK;
+    }
     const DeviceInfo di = device_info(h->device);
     const int n_cu = di.ok ? di.n_cu : 256;
     int *flag = nullptr;
@@ -1180,6 +1421,7 @@ vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_
                                  void *t_val, void *ws, size_t ws_bytes, hipStream_t stream) {
     if (vspmm_status st = check_handle(h)) return st;
     if (h->layout != VSPMM_CSR) return VSPMM_ERR_ENUM;
+    if (h->ptr64) return VSPMM_ERR_UNSUPPORTED;
     if (!t_row_ptr || (h->nnz > 0 && (!t_col || !t_val))) return VSPMM_ERR_NULL;
     const OppositeWs need = carve_opposite(*h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
@@ -1230,13 +1472,14 @@ vspmm_status vspmm_expand_vcs(vspmm_matrix h, vspmm_format format, int32_t sort_
 vspmm_status vspmm_footprint(vspmm_matrix h, size_t *bytes, size_t *expanded_bytes) {
     if (vspmm_status st = check_handle(h)) return st;
     const size_t nmaj = size_t(h->n_major()), nnz = size_t(h->nnz), e = h->val_elt();
+    const size_t pe = h->ptr64 ? 8 : 4;  // bytes of a row pointer
     size_t own;
     if (h->layout == VSPMM_CSR)
-        own = 4 * (nmaj + 1) + (4 + e) * nnz;
+        own = pe * (nmaj + 1) + (4 + e) * nnz;
     else
         own = 4 * (nmaj + 1) + 4 * size_t(h->n_groups) + 4 * (size_t(h->n_groups) + 1) + 4 * nnz;
     if (bytes) *bytes = own;
-    if (expanded_bytes) *expanded_bytes = 4 * (nmaj + 1) + (4 + e) * nnz;
+    if (expanded_bytes) *expanded_bytes = pe * (nmaj + 1) + (4 + e) * nnz;
     return VSPMM_OK;
 }
 
@@ -1248,6 +1491,12 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
     if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
     if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
+    if (h->ptr64) {
+        if (h->blocks.empty()) return VSPMM_ERR_UNSUPPORTED;
+        if (tiles) *tiles = 0;
+        return vspmm_plan_info(h->blocks[0], width, dir, mode, entry_lanes, width_lanes, vec,
+                               slices_per_wave, lds_staged, kernel, nullptr);
+    }
     const bool vcs = h->layout != VSPMM_CSR;
     const bool split_matrix = (h->flags & VSPMM_SPLIT_MATRIX) ||
                               (!vcs && !(h->flags & VSPMM_SPLIT_WIDTH));

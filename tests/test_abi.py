@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_symbols():
     text = open(os.path.join(ROOT, "include", "vspmm.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vspmm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(vspmm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -57,6 +57,19 @@ def test_host_argument_checks_without_device():
                               None) == 2
     assert L.vspmm_create_csr(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 0, 0, 3, None) == 2
     assert L.vspmm_create_csr(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 0, 0, 128, None) == 2
+    # int64 row pointers: nnz may pass int32 (here it reaches the null checks),
+    # the extents may not; the block size is 0 or 1 .. 2^30
+    C64 = L.vspmm_create_csr64
+    assert C64(None, 2, 2, 1, dummy, dummy, dummy, 0, 0, 0, 0, None) == 1
+    assert C64(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 5, 0, 0, 0, None) == 3
+    assert C64(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 0, 3, 0, 0, None) == 3
+    assert C64(ctypes.byref(h), 2**31, 2, 1, dummy, dummy, dummy, 0, 0, 0, 0, None) == 2
+    assert C64(ctypes.byref(h), 2, 2, -1, dummy, dummy, dummy, 0, 0, 0, 0, None) == 2
+    assert C64(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 0, 0, 0, -1, None) == 2
+    assert C64(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 0, 0, 0, 2**30 + 1, None) == 2
+    assert C64(ctypes.byref(h), 2, 2, 1, dummy, dummy, dummy, 0, 0, 3, 0, None) == 2
+    assert C64(ctypes.byref(h), 2, 2, 2**33, None, dummy, dummy, 0, 0, 0, 0, None) == 1
+    assert C64(ctypes.byref(h), 2, 2, 2**33, dummy, None, dummy, 0, 0, 0, 0, None) == 1
     # missing arrays
     assert L.vspmm_create_vcs(ctypes.byref(h), 1, 2, 2, 1, 1, None, dummy, dummy, dummy, 0, 0,
                               None) == 1
