@@ -159,6 +159,69 @@ def cpu_baseline(layouts, width, budget_s):
                       f"width {width}, float64, single-threaded C ({total_s:.1f} s)"}
 
 
+def csr64_products(dev, steps):
+    """A CSR past 2^31 entries (int64 row pointers, int32 column indices),
+    reported beside the headline: 2^21 rows of 1,025 entries (2,149,580,800)
+    over 4,096 columns, indices uniform and values U(0,1) drawn on the device
+    (seeded). A @ x and x @ A (atomic, and deterministic with the blocks'
+    transposes built) at width 1, float32 sums and float32 values summed in
+    float64. The matrix (17.2 GB) is far larger than every cache, so each
+    product reads it from HBM. Algorithmic bytes: 8(m+1) + 8 nnz + s (n_in +
+    n_out), s = 4 or 8."""
+    import torch
+
+    import sparse_dense_matmul_amd as sdm
+
+    n_rows, L, n_cols = 2**21, 1025, 4096
+    nnz = n_rows * L
+    g = torch.Generator(device=dev)
+    g.manual_seed(20261202)
+    col = torch.empty(nnz, dtype=torch.int32, device=dev)
+    val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    chunk = 2**28
+    for s0 in range(0, nnz, chunk):
+        e0 = min(nnz, s0 + chunk)
+        col[s0:e0] = torch.randint(0, n_cols, (e0 - s0,), generator=g, device=dev,
+                                   dtype=torch.int32)
+        val[s0:e0] = torch.rand(e0 - s0, generator=g, device=dev)
+    row_ptr = torch.arange(n_rows + 1, dtype=torch.int64, device=dev) * L
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    steps = max(2, min(steps, 10))
+    for tdt, tname in ((torch.float32, "f32"), (torch.float64, "f32 values, f64 sums")):
+        A = sdm.CsrMatrix.from_arrays((n_rows, n_cols), row_ptr, col, val, dtype=tdt)
+        s = 4 if tdt == torch.float32 else 8
+        for direction in ("AB", "BA"):
+            n_in, n_out = (n_cols, n_rows) if direction == "AB" else (n_rows, n_cols)
+            B = torch.rand(n_in, 1, generator=g, device=dev, dtype=tdt)
+            O = torch.empty(n_out, 1, dtype=tdt, device=dev)
+            for mode in (["atomic"] if direction == "AB" else ["atomic", "deterministic"]):
+                ws = A.workspace(direction, mode, 1) if mode == "deterministic" else None
+                t0 = time.perf_counter()
+                A.spmm(B, direction, mode=mode, out=O, workspace=ws)  # builds the transposes
+                torch.cuda.synchronize()
+                first_ms = 1e3 * (time.perf_counter() - t0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(steps):
+                    A.spmm(B, direction, mode=mode, out=O, workspace=ws)
+                b.record(stream)
+                torch.cuda.synchronize()
+                us = 1e3 * a.elapsed_time(b) / steps
+                nbytes = 8 * (n_rows + 1) + 8 * nnz + s * (n_in + n_out)
+                key = f"{tname} w=1 {'A@x' if direction == 'AB' else 'x@A'}" + \
+                      ("" if direction == "AB" else f" {mode}")
+                out[key] = {"us": round(us, 1), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+                if mode == "deterministic":
+                    out[key]["first_call_ms"] = round(first_ms, 1)
+                del ws
+        del A
+    del col, val, row_ptr
+    torch.cuda.empty_cache()
+    return {"workload": f"CSR {n_rows} x {n_cols}, {nnz} entries (int64 row pointers, "
+                        "3 row blocks), width 1", "products": out}
+
+
 def csr_products(dev, steps, copies=8):
     """The CSR rows of the path, reported beside the headline (not in it): the
     regridding-shaped operator (20,000 x ~373,500, ~1.1M weights) in float32
@@ -352,6 +415,8 @@ def main():
     ap.add_argument("--no-csr", action="store_true", help="skip the CSR operator timings")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-expand", action="store_true", help="skip the VCS expansion timings")
+    ap.add_argument("--no-csr64", action="store_true",
+                    help="skip the timings of the CSR past 2^31 entries")
     ap.add_argument("--other-widths", default="1,8,32,64",
                     help="widths also timed beside the headline (comma list, empty for none)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -569,6 +634,9 @@ def main():
     if not args.no_csr:
         log("timing the CSR operator (reported beside the headline)")
         result["csr"] = csr_products(dev, args.steps)
+    if not args.no_csr64:
+        log("timing the CSR past 2^31 entries (reported beside the headline)")
+        result["csr64"] = csr64_products(dev, args.steps)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(layouts, w, args.cpu_budget)
