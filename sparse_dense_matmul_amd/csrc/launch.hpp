@@ -16,6 +16,11 @@ struct Split {
 
 enum Kind { kPlain = 0, kShort = 1, kLong = 2 };
 
+constexpr int kRing = 128;              // k_short: ring positions per wave (two windows)
+// k_short with 64 entry lanes, where a step is a whole window: a ring of eight
+// windows, filled four at a time, so four steps' gathers go out together
+constexpr int kRingDeep = 512;
+
 // How one walk is launched: the lane split, the kernel family and its grid.
 struct Plan {
     Split sp{0, 0};
@@ -27,10 +32,10 @@ struct Plan {
     int grid = 0;
     int block = 256;
     int wps = 8;         // k_vcs_long: waves per slice
+    int ring = kRing;    // k_short (CSR): ring positions per wave
 };
 
 constexpr size_t kLdsMax = 160 * 1024;  // LDS per CU on gfx950
-constexpr int kRing = 128;              // k_short: ring positions per wave (two windows)
 // k_vcs_rows: entry windows and group windows per round (two rounds are held
 // in registers at once), and the per-wave LDS they need (a mark byte per round
 // position, a float per round group)

@@ -155,7 +155,13 @@ int64_t n_out(const vspmm_matrix_s &h, int dir) { return dir == VSPMM_AB ? h.n_r
 
 // ------------------------------------------------------------------- plan
 
-constexpr int64_t kLongMean = 1024;        // mean entries per slice for k_long
+constexpr int64_t kLongMean = 1024;        // mean entries per slice for k_vcs_long
+
+// Entries in one round of the short CSR walk (64 times its windows per round:
+// 24 when the sums run in float32, 12 in float64). A CSR whose mean row is at
+// least this long is walked by k_long (a group of waves per row); shorter rows
+// fit a round of the short walk.
+constexpr int64_t csr_round_entries(size_t elt) { return elt == 8 ? 64 * 12 : 64 * 24; }
 
 // The lane split of one walk over a matrix with n_slices slices and nnz
 // entries, at width w. Entry lanes G and width lanes WW are powers of two with
@@ -198,7 +204,7 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
     // the VCS walks address B with 32-bit byte offsets and 24-bit row numbers
     const bool small_b = b_bytes < (size_t(1) << 32) && n_in < (int64_t(1) << 24);
     if (pl.R == 1 && (!vcs || small_b)) {
-        if (mean >= kLongMean) {
+        if (mean >= (vcs ? kLongMean : csr_round_entries(elt))) {
             pl.kind = kLong;
             pl.block = 512;
             if (vcs) {
@@ -223,8 +229,15 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
         // dynamic LDS: the staged B (16-byte aligned) and per wave either a
         // ring of (index, value) pairs (CSR) or the round's group marks and
         // values (VCS)
-        const size_t ring = vcs ? size_t(kRowsWaveLds) : size_t(kRing) * (elt == 8 ? 16 : 8);
+        // CSR with 64 entry lanes takes the deep ring when B is staged in LDS
+        // beside it (with B gathered from L2 it measured no better)
+        const size_t ring_el = elt == 8 ? 16 : 8;  // bytes of a ring entry
+        auto ring_of = [&](int n) { return vcs ? size_t(kRowsWaveLds) : size_t(n) * ring_el; };
         const size_t b_al = (b_bytes + 15) & ~size_t(15);
+        if (!vcs && log_g == 6 && b_bytes > 0 && aligned(B, 16) &&
+            b_al + 16 * ring_of(kRingDeep) <= kLdsMax)
+            pl.ring = kRingDeep;
+        const size_t ring = ring_of(pl.ring);
         // VCS: the block's slice-header table (two int arrays) and a counter
         auto extra = [&](int64_t grid) -> size_t {
             if (!vcs) return 0;
@@ -1037,8 +1050,7 @@ int csr_parts(int n_cu) { return 16 * std::max(n_cu, 1); }
 // than one round of the short walk (64 * 24 entries for float32, 64 * 12 for
 // float64). With entry-balanced row ranges a wave then walks about its share.
 int csr_long_len(int dtype, int64_t nnz, int n_parts) {
-    // (the walk's round holds 12 windows when the sums run in float64)
-    const int64_t round = dtype != VSPMM_F32 ? 64 * 12 : 64 * 24;
+    const int64_t round = csr_round_entries(dtype != VSPMM_F32 ? 8 : 4);
     const int64_t share = nnz / std::max(n_parts, 1);
     return int(std::min(round, std::max<int64_t>(64, share)));
 }

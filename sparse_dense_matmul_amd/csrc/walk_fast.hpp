@@ -358,7 +358,8 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
                                               const T (&V)[NWR], const int (&GS)[GWR],
                                               const T (&GV)[GWR], int c0, int lane, int slot,
                                               int cl, const Split &sp, const T *Bs,
-                                              RingEntry<T> *ring, T *__restrict__ out, int w) {
+                                              RingEntry<T> *ring, int ring_n, T *__restrict__ out,
+                                              int w) {
     // steps whose gathers are in flight together (float64 keeps two at any
     // NC; float32 at NC = 4 has no registers left for a second)
     constexpr int SBN = sizeof(T) == 8 ? 2 : (SB / NC > 0 ? SB / NC : 1);
@@ -408,7 +409,10 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
         } else {
             vk = V[k];
         }
-        ring[(64 * k + lane) & (kRing - 1)] = RingEntry<T>{W[k], vk};
+        ring[(64 * k + lane) & (ring_n - 1)] = RingEntry<T>{W[k], vk};
+        // a deep ring is walked once four windows are in it (or the round's
+        // last), so window-wide steps come four to a batch
+        if (ring_n > kRing && (k & 3) != 3 && wbase + 64 < r.E1) continue;
         const int ready = min(wbase + 64, r.E1);
         for (;;) {
             while (q >= e1) {  // slice i is complete
@@ -434,7 +438,7 @@ __device__ __forceinline__ void round_compute(const Round &r, const int (&W)[NWR
             // never -0, so the result is the same bit for bit.
             RingEntry<T> re[SBN];
 #pragma unroll
-            for (int t = 0; t < SBN; ++t) re[t] = ring[(q + t * G + slot - r.E0) & (kRing - 1)];
+            for (int t = 0; t < SBN; ++t) re[t] = ring[(q + t * G + slot - r.E0) & (ring_n - 1)];
             T bv[SBN][NC][VEC];
             bool live[SBN];
 #pragma unroll
@@ -566,7 +570,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
         VP vals, const int *__restrict__ idx, const T *__restrict__ B,
         T *__restrict__ out, int w, int n_in, Split sp, int skip_big, int long_len,
         const int *__restrict__ parts, int n_parts, const int *__restrict__ long_list,
-        int n_long, int long_blocks) {
+        int n_long, int long_blocks, int ring_n) {
     constexpr int NWR = sizeof(T) == 8 ? 12 : 24;
     constexpr int GWR = 4;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
@@ -592,7 +596,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
     }
     // dynamic LDS: [B staged (LDS_B), 16-byte aligned][one ring per wave]
     const size_t b_bytes = LDS_B ? (((size_t)n_in * w * sizeof(T) + 15) & ~size_t(15)) : 0;
-    RingEntry<T> *ring = reinterpret_cast<RingEntry<T> *>(smem + b_bytes) + wave * kRing;
+    RingEntry<T> *ring = reinterpret_cast<RingEntry<T> *>(smem + b_bytes) + wave * ring_n;
     const long long tw = (long long)(gridDim.x - long_blocks) * waves;
     const long long gw = (long long)(blockIdx.x - long_blocks) * waves + wave;
     int s_beg = (int)(gw * n_slices / tw);
@@ -636,7 +640,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
         } else {
             for (int c0 = 0; c0 < w; c0 += NC * chunk)
                 round_compute<VCS, T, VEC, NWR, GWR, SB, NC>(r, W, V, GS, GV, c0, lane, slot, cl,
-                                                             sp, Bs, ring, out, w);
+                                                             sp, Bs, ring, ring_n, out, w);
             sa += r.nsl;
         }
         if (sa < s_end) {

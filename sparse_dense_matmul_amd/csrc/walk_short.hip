@@ -29,12 +29,12 @@ void launch_short_nc(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
             hipLaunchKernelGGL((k_short<false, T, VEC, true, NC, VP>), g, b, lds, s, a.n_slices,
                                a.sptr, a.vptr, vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
                                a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
-                               a.n_long, a.long_blocks);
+                               a.n_long, a.long_blocks, pl.ring);
         } else {
             hipLaunchKernelGGL((k_short<false, T, VEC, false, NC, VP>), g, b, lds, s, a.n_slices,
                                a.sptr, a.vptr, vals, a.idx, a.B, a.out, a.w, a.n_in, pl.sp,
                                a.long_list ? 1 : 0, a.long_len, a.parts, a.n_parts, a.long_list,
-                               a.n_long, a.long_blocks);
+                               a.n_long, a.long_blocks, pl.ring);
         }
     });
 }
