@@ -31,7 +31,7 @@ struct Plan {
     size_t lds_bytes = 0;
     int grid = 0;
     int block = 256;
-    int wps = 8;         // k_vcs_long: waves per slice
+    int wps = 8;         // k_vcs_long, k_long: waves per slice
     int ring = kRing;    // k_short (CSR): ring positions per wave
 };
 

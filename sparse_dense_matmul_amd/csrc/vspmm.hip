@@ -221,7 +221,16 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
                 const int64_t blocks = (n_slices + spb - 1) / spb;
                 pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(blocks, int64_t(n_cu) * 8)));
             } else {
-                pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(n_slices, int64_t(n_cu) * 16)));
+                // k_long: as many waves per row as the mean row fills passes of
+                // the walk's windows, at most 8 (rows of ~1,000 entries get one
+                // wave each); it follows the matrix, not the width
+                const int64_t pass = csr_round_entries(elt);
+                int wps = 1;
+                while (wps < 8 && mean >= pass * wps * 2) wps *= 2;
+                pl.wps = wps;
+                const int64_t spb = 8 / wps;
+                const int64_t blocks = (n_slices + spb - 1) / spb;
+                pl.grid = int(std::max<int64_t>(1, std::min<int64_t>(blocks, int64_t(n_cu) * 16)));
             }
             return pl;
         }

@@ -555,7 +555,7 @@ __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
                                           T *part, const int *__restrict__ sptr,
                                           const int *__restrict__ vptr, VP vals,
                                           const int *__restrict__ idx, const T *__restrict__ B,
-                                          T *__restrict__ out, int w, Split sp);
+                                          T *__restrict__ out, int w, Split sp, int waves);
 
 // Short slices; requires G * WW == 64. Each wave walks a contiguous block of
 // slices in rounds. LDS_B stages B (n_in x w) in dynamic LDS first (one
@@ -591,7 +591,7 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
         constexpr int LSBN = SB / NC > 0 ? SB / NC : 1;
         long_walk<VCS, T, VEC, NC, LSBN, 8>(blockIdx.x * groups, long_blocks * groups, n_long, long_list,
                                    group, wave - group * kLongWaves, part, sptr, vptr, vals, idx,
-                                   B, out, w, sp);
+                                   B, out, w, sp, kLongWaves);
         return;
     }
     // dynamic LDS: [B staged (LDS_B), 16-byte aligned][one ring per wave]
@@ -659,10 +659,13 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 // rows are added in wave order. The split depends only on the slice, so a
 // column's arithmetic is the same in every launch that walks it.
 //
-// long_walk: the block's `groups` groups take the slices li = first + group,
-// then li + stride, ... (li < n_walk; the slice is list[li], or li without a
-// list); every wave of the block runs the same iterations (the barriers are
-// block-wide). part: LDS for the group, kLongWaves x NC*64*VEC elements.
+// long_walk: the block's `groups` groups of `waves` waves (kLongWaves for the
+// handle's long-row list; for a matrix walked by k_long alone, as many as its
+// mean row fills passes, at most kLongWaves) take the slices li = first +
+// group, then li + stride, ... (li < n_walk; the slice is list[li], or li
+// without a list); every wave of the block runs the same iterations (the
+// barriers are block-wide). part: LDS for the group, waves x NC*64*VEC
+// elements.
 // SBN steps have their gathers in flight together, and a pass loads NWR
 // windows; both set registers, not the arithmetic: a pass holds a multiple of
 // G entries, so each lane gets the same entries in the same order either way.
@@ -672,10 +675,9 @@ __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
                                           T *part, const int *__restrict__ sptr,
                                           const int *__restrict__ vptr, VP vals,
                                           const int *__restrict__ idx, const T *__restrict__ B,
-                                          T *__restrict__ out, int w, Split sp) {
+                                          T *__restrict__ out, int w, Split sp, int waves) {
     constexpr int PW = NC * 64 * VEC;  // part elements per wave
     const int lane = threadIdx.x & 63;
-    const int waves = kLongWaves;
     const int G = 1 << sp.log_g;
     const int slot = lane >> sp.log_ww;
     const int cl = lane & ((1 << sp.log_ww) - 1);
@@ -796,19 +798,23 @@ __device__ __forceinline__ void long_walk(int first, int stride, int n_walk,
 }
 
 
-// k_long: one group (a block of kLongWaves waves) per slice, grid-stride over
-// the slices, or over the slices in `list` when it is given; requires
-// G * WW == 64.
+// k_long: a group of wps waves (1, 2, 4 or 8; kLongWaves / wps groups per
+// block) per slice, grid-stride over the slices, or over the slices in `list`
+// when it is given; requires G * WW == 64.
 template <bool VCS, typename T, int VEC, int NC, typename VP = const T *>
 __global__ void __launch_bounds__(64 * kLongWaves)
 k_long(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr,
        VP vals, const int *__restrict__ idx, const T *__restrict__ B,
-       T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list) {
-    __shared__ T part[kLongWaves * NC * 64 * VEC];
+       T *__restrict__ out, int w, Split sp, const int *__restrict__ list, int n_list, int wps) {
+    constexpr int PW = NC * 64 * VEC;
+    __shared__ T part[kLongWaves * PW];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int groups = kLongWaves / wps;
+    const int group = wave / wps;
     constexpr int SB = sizeof(T) == 8 ? 2 : 4;
-    long_walk<VCS, T, VEC, NC, SB, sizeof(T) == 8 ? 12 : 24>(blockIdx.x, gridDim.x, list ? n_list : n_slices, list, 0, wave,
-                                   part, sptr, vptr, vals, idx, B, out, w, sp);
+    long_walk<VCS, T, VEC, NC, SB, sizeof(T) == 8 ? 12 : 24>(
+        blockIdx.x * groups, gridDim.x * groups, list ? n_list : n_slices, list, group,
+        wave - group * wps, part + group * wps * PW, sptr, vptr, vals, idx, B, out, w, sp, wps);
 }
 
 }  // namespace vspmm

@@ -13,7 +13,7 @@ void launch_long_v(const Plan &pl, const WalkArgs<T> &a, hipStream_t s) {
     const int n_chunks = (a.w + chunk - 1) / chunk;
 #define VSPMM_LONG(NC)                                                                           \
     hipLaunchKernelGGL((k_long<VCS, T, VEC, NC, decltype(vals)>), g, b, 0, s, a.n_slices, a.sptr, \
-                       a.vptr, vals, a.idx, a.B, a.out, a.w, pl.sp, a.long_list, a.n_long)
+                       a.vptr, vals, a.idx, a.B, a.out, a.w, pl.sp, a.long_list, a.n_long, pl.wps)
     with_vals<T>(a, [&](auto vals) {
         if (n_chunks >= 4) VSPMM_LONG(4);
         else if (n_chunks >= 2) VSPMM_LONG(2);

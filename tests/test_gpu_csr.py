@@ -304,3 +304,35 @@ def test_float32_values_summed_in_float64(orc, regrid32, width):
         want = orc.transpose_csr(n, C.row_ptr, C.col, C.val)
         assert np.array_equal(T.row_ptr.cpu().numpy(), want[0])
         assert np.array_equal(T.val.cpu().numpy().view(np.uint32), want[2].view(np.uint32))
+
+
+@pytest.mark.parametrize("mean", [800, 1700, 3300, 7000, 13000])
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_long_walk_waves_follow_mean_row(orc, mean, dtype):
+    """Matrices whose mean row fills a round of the short walk go to the long
+    walk with 1, 2, 4 or 8 waves per row (as many as the mean row fills passes
+    of 1,536 / 768 entries): against the oracle at widths 1, 8 and 33 in both
+    directions, with rows from a tenth to twice the mean and a few empty rows,
+    and each batch column equal, bit for bit, to its solo product."""
+    dev = need_gpu()
+    rng = np.random.default_rng(mean)
+    m, n = 96, 5000
+    np_t = np.float32 if dtype == "f32" else np.float64
+    lengths = rng.integers(mean // 10, 2 * mean, m)
+    lengths[rng.choice(m, 5, replace=False)] = 0
+    rows = np.repeat(np.arange(m), lengths)
+    cols = rng.integers(0, n, rows.size).astype(np.int32)
+    vals = rng.uniform(-1, 1, rows.size).astype(np_t)
+    C = W.Csr((m, n), np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), cols, vals)
+    A = csr_handle(C, dev)
+    tol = 1e-5 if dtype == "f32" else 1e-13
+    for direction in ("AB", "BA"):
+        rows_in, _ = dims(C, direction)
+        for width in (1, 8, 33):
+            B = W.dense_normal(np.random.default_rng(width), rows_in, width, dtype=np_t)
+            check_close(orc, C, direction, B, A.spmm(to_dev(B, dev), direction), tol=tol,
+                        where=f"mean {mean} {dtype} {direction} w={width}")
+    Bb = to_dev(W.dense_normal(np.random.default_rng(2), n, 8, dtype=np_t), dev)
+    batch = A.spmm(Bb, "AB")
+    for c in (0, 5):
+        assert torch.equal(batch[:, c], A.spmm(Bb[:, c:c + 1].contiguous(), "AB")[:, 0])
