@@ -211,7 +211,10 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * 2 MB, a multiple of 8 of them, each fitting one XCD's L2: the blocks of a
  * tile, all on one XCD and as many as the XCD holds at once, gather it from
  * global memory. A smaller B with rows of up to 64 bytes is cut into tiles
- * that fit in LDS, and each block stages its tile there. The
+ * that fit in LDS, and each block stages its tile there; where the fewest such
+ * tiles would leave (tile, output row) parts of 1,024 entries or more on
+ * average, the tile count rises to a multiple of 8 until the mean is at most
+ * 512. The
  * product writes one partial row per (tile, output row) into ws and adds them
  * in a fixed order; it repeats bit for bit. The copy is reused like the
  * opposite layout (it also depends on the tile size, which follows the

@@ -764,7 +764,16 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     // so a tile of B is fetched into one XCD's L2 instead of all eight
     if (tiles >= 4) tiles = (tiles + 7) / 8 * 8;
     tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);  // balanced tiles
-    tiles = (ni + tr - 1) / tr;                           // (rounding tr may drop one)
+    // virtual slices too long for the short walk (a narrow B makes few,
+    // large tiles): more tiles, a multiple of 8, until their mean is at most
+    // 512 entries
+    if (h.nnz / std::max<int64_t>(tiles * no, 1) >= kLongMean) {
+        tiles = std::max<int64_t>(tiles, (h.nnz + no * 512 - 1) / (no * 512));
+        tiles = (tiles + 7) / 8 * 8;
+        tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);
+        if (tr < 64) return tp;
+    }
+    tiles = (ni + tr - 1) / tr;  // (rounding tr may drop one)
     const int64_t nv = tiles * no;
     if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
     const int64_t mean = h.nnz / nv;

@@ -5,9 +5,9 @@ to 64 bytes (staged there), and one XCD's L2 for wider rows (gathered from
 global memory, the blocks of a tile on one XCD). Checked on the 60,000 x 2,000
 count matrix in both directions whose dense input (60,000 rows) is too large
 for LDS, at widths where LDS tiles apply (4, 8, 16), where L2 tiles apply (32,
-64) and where neither does (1: too few, too long virtual slices; the untiled
-path runs instead); on a matrix whose last tile is short and holds runs of
-empty groups; across workspaces and widths sharing one workspace; and against
+64), and at width 1, where the fewest tiles would leave virtual slices too long
+for the short walk and the tile count rises; on a matrix whose last tile is
+short and holds runs of empty groups; across workspaces and widths sharing one workspace; and against
 the float64 oracle, exactly on integer data."""
 
 import numpy as np
@@ -88,15 +88,20 @@ def test_l2_tiled_parity(orc, count60k, layout, direction, width):
 
 @pytest.mark.parametrize("width", [1])
 @pytest.mark.parametrize("layout,direction", LONG)
-def test_untiled_widths(orc, count60k, layout, direction, width):
-    """Width 1 (two tiles would leave too few, too long virtual slices): no
-    tiled schedule; the workspace asked for serves the plain path."""
+def test_width1_tiles_follow_slice_length(orc, count60k, layout, direction, width):
+    """Width 1: B (240 KB) would fit two tiles, leaving virtual slices of
+    ~1,500 entries, beyond the short walk; the tile count rises to a multiple
+    of 8 until the mean is at most 512 (8 tiles, ~375 entries). Parity and a
+    bit-for-bit repeat."""
     dev = need_gpu()
     L = count60k[layout]
     A = vcs_handle(L, dev)
-    assert A.plan_info(width, direction, "deterministic")["tiles"] == 0
-    B, out, _ = run_det(A, L, direction, width)
-    check_close(orc, L, direction, B, out, where=f"untiled {layout} {direction} w={width}")
+    info = A.plan_info(width, direction, "deterministic")
+    assert info["tiles"] == 8 and info["kernel_name"] == "k_vcs_rows" and info["lds_staged"] == 1
+    B, out, ws = run_det(A, L, direction, width)
+    check_close(orc, L, direction, B, out, where=f"width 1 {layout} {direction}")
+    again = A.spmm(to_dev(B, dev), direction, mode="deterministic", workspace=ws)
+    assert torch.equal(again.view(torch.int32), out.view(torch.int32))
 
 
 @pytest.mark.parametrize("name,direction", [("vcsr", "BA"), ("vcsc", "BA"), ("vcsc_empty", "BA")])
