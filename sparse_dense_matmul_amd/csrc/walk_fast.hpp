@@ -13,9 +13,11 @@
 //    CU), so gathers use the LDS pipe. Slices longer than long_len are left to
 //    the long walk; with long blocks, the first blocks of the same launch run
 //    it beside the short slices.
-//  - long_walk (k_long, and the long blocks of k_short): kLongWaves waves walk
-//    one slice, wave k taking the k-th of kLongWaves contiguous pieces of its
-//    entries; the pieces' partial sums are added in wave order.
+//  - long_walk (k_long, and the long blocks of k_short): a group of waves
+//    walks one slice (kLongWaves for a handle's long-row list; for a matrix
+//    walked by k_long alone, as many as its mean row fills passes), wave k
+//    taking the k-th of the group's contiguous pieces of its entries; the
+//    pieces' partial sums are added in wave order.
 //
 // Gathers are issued by every lane without branches (an idle lane reads a
 // valid row), so a step's loads go out together; only the FMAs are masked.
@@ -652,12 +654,13 @@ k_short(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vptr
 
 // ------------------------------------------------------------------- long
 
-// Long slices: each is walked by a group of kLongWaves waves; wave k of the
-// group takes the k-th of kLongWaves contiguous pieces of the slice's
-// entries; a piece (up to 64*NWR entries per pass) and the slice's group
-// window are loaded at once, then walked from registers. The waves' partial
-// rows are added in wave order. The split depends only on the slice, so a
-// column's arithmetic is the same in every launch that walks it.
+// Long slices: each is walked by a group of waves; wave k of the group takes
+// the k-th of the group's contiguous pieces of the slice's entries; a piece
+// (up to 64*NWR entries per pass) and the slice's group window are loaded at
+// once, then walked from registers. The waves' partial rows are added in wave
+// order. The group size depends only on the matrix (and on whether the slice
+// is on a long-row list), so a column's arithmetic is the same at every
+// width.
 //
 // long_walk: the block's `groups` groups of `waves` waves (kLongWaves for the
 // handle's long-row list; for a matrix walked by k_long alone, as many as its
