@@ -336,3 +336,41 @@ def test_long_walk_waves_follow_mean_row(orc, mean, dtype):
     batch = A.spmm(Bb, "AB")
     for c in (0, 5):
         assert torch.equal(batch[:, c], A.spmm(Bb[:, c:c + 1].contiguous(), "AB")[:, 0])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_deep_ring_rows_of_a_thousand(orc, dtype):
+    """Rows of 500 to 1,500 entries over 1,000 columns: 64 entry lanes, a
+    window per step, and B small enough to sit in LDS beside the eight-window
+    ring at widths 1 to 16 (float32; float64 up to width 4, beyond which the
+    two-window ring keeps B in LDS). Against the oracle in both directions and
+    modes, repeats, and batch columns equal to solo products bit for bit."""
+    dev = need_gpu()
+    rng = np.random.default_rng(1000)
+    m, n = 700, 1000
+    np_t = np.float32 if dtype == "f32" else np.float64
+    lengths = rng.integers(500, 1500, m)
+    lengths[[3, 350]] = 0
+    rows = np.repeat(np.arange(m), lengths)
+    cols = rng.integers(0, n, rows.size).astype(np.int32)
+    vals = rng.uniform(-1, 1, rows.size).astype(np_t)
+    C = W.Csr((m, n), np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), cols, vals)
+    A = csr_handle(C, dev)
+    assert A.plan_info(1, "AB")["entry_lanes"] == 64
+    tol = 1e-5 if dtype == "f32" else 1e-13
+    for width in (1, 4, 8, 16):
+        for direction in ("AB", "BA"):
+            rows_in, _ = dims(C, direction)
+            B = W.dense_normal(np.random.default_rng(width), rows_in, width, dtype=np_t)
+            Bd = to_dev(B, dev)
+            for mode in (["atomic"] if direction == "AB" else ["atomic", "deterministic"]):
+                ws = A.workspace(direction, mode) if mode == "deterministic" else None
+                out = A.spmm(Bd, direction, mode=mode, workspace=ws)
+                check_close(orc, C, direction, B, out, tol=tol,
+                            where=f"{dtype} {direction} {mode} w={width}")
+                if direction == "AB" or mode == "deterministic":
+                    assert torch.equal(out, A.spmm(Bd, direction, mode=mode, workspace=ws))
+    Bb = to_dev(W.dense_normal(np.random.default_rng(9), n, 16, dtype=np_t), dev)
+    batch = A.spmm(Bb, "AB")
+    for c in (0, 7, 15):
+        assert torch.equal(batch[:, c], A.spmm(Bb[:, c:c + 1].contiguous(), "AB")[:, 0])
