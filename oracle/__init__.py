@@ -38,9 +38,10 @@ STATUS = {0: "ok", 1: "pointer array does not start at 0", 2: "pointer array dec
 
 
 def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile the oracle with gcc (plain C11, -O2, no fast-math)."""
+    """Compile the oracle with gcc (plain C11, -O2, no fast-math; OpenMP for
+    the threaded timing mode)."""
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-ffp-contract=off", "-o", out, src]
+           "-ffp-contract=off", "-fopenmp", "-o", out, src]
     subprocess.run(cmd, check=True)
     return out
 
@@ -69,6 +70,12 @@ def load(path: str | None = None):
     lib.orc_spmm_vcs.restype = None
     lib.orc_spmm_csr.argtypes = [ctypes.c_int, i64, i32p, i32p, dp, dp, i64, dp, vp]
     lib.orc_spmm_csr.restype = None
+    lib.orc_spmm_vcs_threaded.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i32p, dp, i32p,
+                                          i32p, dp, i64, dp, ctypes.c_int]
+    lib.orc_spmm_vcs_threaded.restype = ctypes.c_int
+    lib.orc_spmm_csr_threaded.argtypes = [ctypes.c_int, i64, i64, i32p, i32p, dp, dp, i64, dp,
+                                          ctypes.c_int]
+    lib.orc_spmm_csr_threaded.restype = ctypes.c_int
     lib.orc_expand_vcs.argtypes = [i64, i32p, vp, i32p, i32p, i32p, i32p, vp]
     lib.orc_expand_vcs.restype = None
     lib.orc_transpose_csr.argtypes = [i64, i64, i32p, i32p, vp, ctypes.c_int, i32p, i32p, vp]
@@ -172,6 +179,36 @@ def spmm(A, direction, B, want=None, lib=None) -> np.ndarray:
         return spmm_vcs(A.layout, direction, A.shape, A.major_ptr, A.values, A.value_ptr,
                         A.indices, B, want=want, lib=lib)
     return spmm_csr(direction, A.shape, A.row_ptr, A.col, A.val, B, want=want, lib=lib)
+
+
+def spmm_threaded(A, direction, B, threads, lib=None) -> np.ndarray:
+    """The same product as :func:`spmm` on ``threads`` host threads (the timed
+    CPU baseline): slices split over the threads, private float64 outputs
+    summed in thread order where the output rows are not the slices. Equal
+    to :func:`spmm` bit for bit where the output rows are the slices; else
+    up to the regrouped additions' rounding."""
+    lib = lib or load()
+    m, n = A.shape
+    B = _f64(B)
+    w = B.shape[1] if B.ndim == 2 else 1
+    n_in, n_out = (n, m) if direction == "AB" else (m, n)
+    if B.shape[0] != n_in:
+        raise ValueError(f"dense operand has {B.shape[0]} rows, expected {n_in}")
+    out = np.zeros((n_out, w), dtype=np.float64)
+    if hasattr(A, "major_ptr"):
+        major_ptr, value_ptr, indices = _i32(A.major_ptr), _i32(A.value_ptr), _i32(A.indices)
+        vals = _f64(A.values)
+        n_major = m if A.layout == "vcsr" else n
+        st = lib.orc_spmm_vcs_threaded(LAYOUTS[A.layout], DIRS[direction], n_major, n_out,
+                                       _p(major_ptr), _p(vals), _p(value_ptr), _p(indices),
+                                       _p(B), w, _p(out), int(threads))
+    else:
+        row_ptr, col, v = _i32(A.row_ptr), _i32(A.col), _f64(A.val)
+        st = lib.orc_spmm_csr_threaded(DIRS[direction], m, n_out, _p(row_ptr), _p(col), _p(v),
+                                       _p(B), w, _p(out), int(threads))
+    if st != 0:
+        raise MemoryError("the threaded oracle could not allocate its private outputs")
+    return out
 
 
 def abs_scale(A, direction, B, want=None, lib=None) -> np.ndarray:

@@ -32,10 +32,17 @@
  * is exact, so every single product v * b is exact and only the additions
  * round.
  *
+ * The threaded mode (orc_spmm_*_threaded) is the timed CPU baseline: the
+ * same loops with the slices split over host threads, private float64
+ * outputs where the output rows are not the slices (vsparse, "The kernels").
+ * The parity checks use the sequential functions.
+ *
  * Parity pins: see the tests that exercise this file (brute-force dense
  * products, scipy.sparse, the all-ones closed forms, the dot-product identity,
- * the transpose involution, page 1's footprint ratios).
+ * the transpose involution, page 1's footprint ratios; the threaded mode
+ * against the sequential one).
  */
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -122,6 +129,88 @@ void orc_spmm_csr(int dir, int64_t n_rows, const int32_t *row_ptr, const int32_t
     for (int64_t r = 0; r < n_rows; ++r)
         for (int64_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p)
             entry(dir, r, col[p], val[p], B, w, out, want);
+}
+
+/* ------------------------------------------------- products, threaded mode */
+
+/* The timed mode of the same products, on n_threads host threads (OpenMP).
+ * It follows the host product of vsparse, section "The kernels": the major
+ * slices are split over the threads, and in a direction whose output rows
+ * are not the slices each thread adds into an accumulator of its own.
+ *  - Output rows are the slices (VCSR or CSR times B, B times VCSC): thread t
+ *    walks the t-th of n_threads contiguous ranges of slices and writes their
+ *    rows. Every row is summed by one thread in the order of the sequential
+ *    functions above, so the result equals theirs bit for bit.
+ *  - Otherwise: thread t walks its range of slices into a private zeroed
+ *    n_out x w float64 copy of out; then every output element is the sum of
+ *    the copies taken in thread order. The additions are regrouped by thread,
+ *    so the result may differ from the sequential one in the last bits
+ *    (exactly equal when every partial sum is exact, e.g. integer data).
+ * out must be zeroed by the caller. Returns 0, or 1 if the private copies
+ * could not be allocated. */
+
+static void slice_vcs(int layout, int dir, int64_t s, const int32_t *major_ptr,
+                      const double *values, const int32_t *value_ptr, const int32_t *indices,
+                      const double *B, int64_t w, double *out) {
+    for (int64_t k = major_ptr[s]; k < major_ptr[s + 1]; ++k)
+        for (int64_t p = value_ptr[k]; p < value_ptr[k + 1]; ++p) {
+            int64_t r = layout == 1 ? s : indices[p];
+            int64_t c = layout == 1 ? indices[p] : s;
+            entry(dir, r, c, values[k], B, w, out, NULL);
+        }
+}
+
+static void slice_csr(int dir, int64_t r, const int32_t *row_ptr, const int32_t *col,
+                      const double *val, const double *B, int64_t w, double *out) {
+    for (int64_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p)
+        entry(dir, r, col[p], val[p], B, w, out, NULL);
+}
+
+/* kind 0 = CSR (rows are slices), 1 = VCSR, 2 = VCSC. */
+static int spmm_threaded(int kind, int dir, int64_t n_major, int64_t n_out,
+                         const int32_t *sptr, const double *vals, const int32_t *vptr,
+                         const int32_t *idx, const double *B, int64_t w, double *out,
+                         int n_threads) {
+    const int rows_are_slices = (kind != 2) == (dir == 0);
+    const int64_t n_el = n_out * w;
+    double *priv = NULL;
+    if (n_threads < 1) n_threads = 1;
+    if (!rows_are_slices) {
+        priv = (double *)calloc((size_t)n_threads * (size_t)(n_el > 0 ? n_el : 1), sizeof(double));
+        if (!priv) return 1;
+    }
+#pragma omp parallel num_threads(n_threads)
+    {
+        const int64_t t = omp_get_thread_num(), nt = omp_get_num_threads();
+        const int64_t s0 = n_major * t / nt, s1 = n_major * (t + 1) / nt;
+        double *dst = rows_are_slices ? out : priv + t * n_el;
+        for (int64_t s = s0; s < s1; ++s) {
+            if (kind == 0) slice_csr(dir, s, sptr, idx, vals, B, w, dst);
+            else slice_vcs(kind, dir, s, sptr, vals, vptr, idx, B, w, dst);
+        }
+        if (!rows_are_slices) {
+#pragma omp barrier
+            const int64_t e0 = n_el * t / nt, e1 = n_el * (t + 1) / nt;
+            for (int64_t e = e0; e < e1; ++e)
+                for (int64_t u = 0; u < nt; ++u) out[e] += priv[u * n_el + e];
+        }
+    }
+    free(priv);
+    return 0;
+}
+
+int orc_spmm_vcs_threaded(int layout, int dir, int64_t n_major, int64_t n_out,
+                          const int32_t *major_ptr, const double *values,
+                          const int32_t *value_ptr, const int32_t *indices, const double *B,
+                          int64_t w, double *out, int n_threads) {
+    return spmm_threaded(layout, dir, n_major, n_out, major_ptr, values, value_ptr, indices, B,
+                         w, out, n_threads);
+}
+
+int orc_spmm_csr_threaded(int dir, int64_t n_rows, int64_t n_out, const int32_t *row_ptr,
+                          const int32_t *col, const double *val, const double *B, int64_t w,
+                          double *out, int n_threads) {
+    return spmm_threaded(0, dir, n_rows, n_out, row_ptr, val, NULL, col, B, w, out, n_threads);
 }
 
 /* ---------------------------------------------------------------- expansion */

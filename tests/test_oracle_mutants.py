@@ -33,6 +33,13 @@ MUTANTS = [
     ("expand_ptr", "ptr[s] = value_ptr[major_ptr[s]];", "ptr[s] = major_ptr[s];"),
     ("validate_monotone", "if (ptr[i + 1] < ptr[i]) return ORC_BAD_MONOTONE;",
      "if (ptr[i + 1] < ptr[i] - 1) return ORC_BAD_MONOTONE;"),
+    # the threaded timing mode
+    ("threaded_skips_first_slice", "for (int64_t s = s0; s < s1; ++s) {",
+     "for (int64_t s = s0 + 1; s < s1; ++s) {"),
+    ("threaded_drops_last_copy", "for (int64_t u = 0; u < nt; ++u) out[e] += priv[u * n_el + e];",
+     "for (int64_t u = 0; u + 1 < nt; ++u) out[e] += priv[u * n_el + e];"),
+    ("threaded_shared_copy", "double *dst = rows_are_slices ? out : priv + t * n_el;",
+     "double *dst = rows_are_slices ? out : priv;"),
 ]
 
 
@@ -57,6 +64,16 @@ PY_MUTANTS = [
     ("expand_sort_descending", "np.lexsort((idx, slice_of))", "np.lexsort((-idx, slice_of))"),
     ("expand_other_format_untransposed", "    return transpose_csr(n_minor, ptr, idx, val, lib=lib)\n\n\ndef transpose_csr",
      "    return ptr, idx, val\n\n\ndef transpose_csr"),
+    # the float comparator behind every parity check, and its scale
+    ("comparator_mean", "rel = float((err[pos] / scale[pos]).max())",
+     "rel = float((err[pos] / scale[pos]).mean())"),
+    ("comparator_mask_inverted", "    pos = scale > 0\n", "    pos = ~(scale > 0)\n"),
+    ("comparator_zeros_forced", "zeros_ok = bool(np.all(got[~pos] == 0))", "zeros_ok = True"),
+    ("abs_scale_signed_b_vcs", "A.indices, np.abs(_f64(B))", "A.indices, _f64(B)"),
+    ("abs_scale_signed_b_csr", "np.abs(_f64(A.val)),\n                    np.abs(_f64(B))",
+     "np.abs(_f64(A.val)),\n                    _f64(B)"),
+    ("abs_scale_signed_values", "np.abs(_f64(A.values))", "_f64(A.values)"),
+    ("abs_scale_signed_csr_values", "np.abs(_f64(A.val))", "_f64(A.val)"),
 ]
 
 

@@ -394,3 +394,106 @@ def test_expand_sorted_repeated_indices(orc):
                                           "csc", True)
     assert ptr.tolist() == [0, 1, 3, 3, 3, 4, 5]
     assert idx.tolist() == [1, 0, 0, 1, 0] and val.tolist() == [7, 2, 3, 7, 2]
+
+
+# ------------------------------------------------------------ the comparator
+
+def test_max_rel_error_hand_computed(orc):
+    """The float parity criterion on arrays worked by hand: the largest
+    |got - ref| / S over outputs with S > 0 (errors 0, 0.5, 1.0 over scales
+    1, 1, 4 give 0, 0.5, 0.25: the maximum is 0.5, the mean would be 0.25)."""
+    got = np.array([1.0, 2.0, 3.0])
+    ref = np.array([1.0, 2.5, 2.0])
+    scale = np.array([1.0, 1.0, 4.0])
+    rel, zeros_ok = orc.max_rel_error(got, ref, scale)
+    assert rel == 0.5 and zeros_ok
+
+
+def test_max_rel_error_cancellation(orc):
+    """A cancelled output (reference 0, |A||B| = 2) judged against S, not
+    against |ref|: an error of 1e-7 is 5e-8 relative, not infinite."""
+    rel, zeros_ok = orc.max_rel_error(np.array([1e-7, 3.0]), np.array([0.0, 3.0]),
+                                      np.array([2.0, 3.0]))
+    assert rel == pytest.approx(5e-8, rel=1e-12) and zeros_ok
+
+
+def test_max_rel_error_zero_scale(orc):
+    """Outputs whose |A||B| is 0 must be exactly 0: any nonzero value there
+    fails, however small, and does not enter the relative error (which comes
+    from the S > 0 outputs alone)."""
+    scale = np.array([0.0, 2.0, 0.0])
+    ref = np.array([0.0, 1.0, 0.0])
+    rel, zeros_ok = orc.max_rel_error(np.array([0.0, 3.0, 0.0]), ref, scale)
+    assert rel == 1.0 and zeros_ok
+    rel, zeros_ok = orc.max_rel_error(np.array([1e-30, 1.0, 0.0]), ref, scale)
+    assert rel == 0.0 and not zeros_ok
+    rel, zeros_ok = orc.max_rel_error(np.array([0.0, 1.0, -0.0]), ref, scale)
+    assert rel == 0.0 and zeros_ok  # -0 equals 0
+    rel, zeros_ok = orc.max_rel_error(np.zeros(3), np.zeros(3), np.zeros(3))
+    assert rel == 0.0 and zeros_ok
+
+
+def _signed_hand_matrix():
+    """A = [[1, 2], [1, -2]] as triplets, B = [[1, 3], [-1, 1]] (hand-picked
+    so that |A||B|, |A|B and A|B| all differ): A B = [[-1, 5], [3, 1]],
+    |A||B| = [[3, 5], [3, 5]]; for B A (B given transposed as Bt = [[1, -1],
+    [3, 1]] over the rows of A): (B A)^T = [[4, 0], [-4, -4]] and
+    |A|^T |Bt| = [[4, 2], [8, 4]]."""
+    t = W.Triplets((2, 2), np.array([0, 0, 1, 1]), np.array([0, 1, 0, 1]),
+                   np.array([1.0, 2.0, 1.0, -2.0], dtype=np.float32))
+    B = np.array([[1.0, 3.0], [-1.0, 1.0]])
+    Bt = np.array([[1.0, -1.0], [3.0, 1.0]])
+    return t, B, Bt
+
+
+@pytest.mark.parametrize("kind", ["vcsr", "vcsc", "csr"])
+def test_abs_scale_hand_computed(orc, kind):
+    """S = |A| |B| in the output's layout, worked by hand (a dropped absolute
+    value on A or on B changes some entry)."""
+    t, B, Bt = _signed_hand_matrix()
+    L = layouts_of(t)[kind]
+    assert np.array_equal(orc.spmm(L, "AB", B), [[-1.0, 5.0], [3.0, 1.0]])
+    assert np.array_equal(orc.abs_scale(L, "AB", B), [[3.0, 5.0], [3.0, 5.0]])
+    assert np.array_equal(orc.spmm(L, "BA", Bt), [[4.0, 0.0], [-4.0, -4.0]])
+    assert np.array_equal(orc.abs_scale(L, "BA", Bt), [[4.0, 2.0], [8.0, 4.0]])
+
+
+# ---------------------------------------------------------- threaded mode
+
+@pytest.mark.parametrize("threads", [1, 3, 8])
+def test_threaded_integer_exact(orc, threads):
+    """The timed mode on integer data: every partial sum is exact, so each
+    layout and direction equals the triple loop exactly at any thread count
+    (more threads than slices included)."""
+    for seed in range(4):
+        rng = np.random.default_rng(3000 + seed)
+        m, n = (int(x) for x in rng.integers(1, 30, size=2))
+        t = W.tiny_count(m, n, rng.uniform(0.1, 0.9), 64, rng)
+        A = dense_of(t)
+        for direction, rows in (("AB", n), ("BA", m)):
+            B = W.dense_int(rng, rows, 3, dtype=np.float64)
+            want = brute(A, direction, B)
+            for name, L in layouts_of(t).items():
+                got = orc.spmm_threaded(L, direction, B, threads)
+                assert np.array_equal(got, want), (name, direction, threads)
+
+
+@pytest.mark.parametrize("threads", [2, 7])
+def test_threaded_real_data(orc, threads):
+    """Real data: where the output rows are the slices each row is summed by
+    one thread in the sequential order (bitwise equal); elsewhere the private
+    outputs regroup the additions, within 1e-13 of |A||B|."""
+    rng = W.rng_for(96)
+    t = W.count_matrix(1500, 300, 20.0, 64, rng)
+    t = W.Triplets(t.shape, t.rows, t.cols, (t.vals * 0.37).astype(np.float32))
+    for name, L in layouts_of(t).items():
+        for direction, rows in (("AB", 300), ("BA", 1500)):
+            B = rng.standard_normal((rows, 5))
+            seq = orc.spmm(L, direction, B)
+            got = orc.spmm_threaded(L, direction, B, threads)
+            rows_are_slices = (name != "vcsc") == (direction == "AB")
+            if rows_are_slices:
+                assert np.array_equal(got, seq), (name, direction)
+            else:
+                rel, zeros_ok = orc.max_rel_error(got, seq, orc.abs_scale(L, direction, B))
+                assert rel <= 1e-13 and zeros_ok, (name, direction, rel)
