@@ -136,27 +136,128 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
 
 
+def ceilings(reps=20):
+    """Measured ceilings of the resources the walks use besides HBM (the
+    probe kernels of libvspmm_probe.so, shaped like the aligned walk's inner
+    loop): 64-byte row gathers from LDS and from global memory (L2), global
+    float atomics as a width-16 scatter issues them, and back-to-back empty
+    launches. Rates are per chip; 'us_per_6M' is the time 6,000,000 such
+    rows (or 6M entries' adds at width 16) take at that rate."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_dense_matmul_amd", "libvspmm_probe.so"))
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.vspmm_probe.argtypes = [ci, ci, vp, ci, vp, ci, ci, ci, vp, vp, ci, vp,
+                                ctypes.POINTER(ctypes.c_float)]
+    lib.vspmm_probe.restype = ci
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    clk_ghz = 2.4
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    rng = np.random.default_rng(5)
+    grid = n_cu
+    n_win = 4096
+    sink = torch.empty(grid * 1024, dtype=torch.float32, device=dev)
+
+    def run(kind, mode, n_rows, iters, table=None, out=None, g=grid):
+        idx = torch.from_numpy(rng.integers(0, n_rows, size=n_win * 64).astype(np.int32)).to(dev)
+        ms = ctypes.c_float(0)
+        st = lib.vspmm_probe(kind, mode, vp(table.data_ptr()) if table is not None else None,
+                             n_rows, vp(idx.data_ptr()), n_win, iters, g, vp(sink.data_ptr()),
+                             vp(out.data_ptr()) if out is not None else None, reps, stream,
+                             ctypes.byref(ms))
+        if st != 0:
+            raise RuntimeError(f"vspmm_probe(kind={kind}, mode={mode}) failed: {st}")
+        return ms.value / reps  # ms per launch
+
+    res = {}
+    iters = 512
+    rows_per_launch = grid * 16 * iters * 4 * 16  # 16 rows per step per wave
+    table = torch.randn(2000 * 16, device=dev)
+    for mode, name in ((0, "lds_gather_b128_random_rows"), (1, "lds_gather_b128_conflict_free"),
+                       (2, "lds_gather_2xb64_random_rows")):
+        ms = run(0, mode, 2000, iters, table=table)
+        rate = rows_per_launch / (ms * 1e-3)
+        res[name] = {"G_rows_per_s": round(rate / 1e9, 2),
+                     "bytes_per_clk_per_CU": round(rate * 64 / (clk_ghz * 1e9 * n_cu), 1),
+                     "us_per_6M": round(6e6 / rate * 1e6, 2)}
+    for n_rows, name in ((2000, "l2_gather_128KB_table"), (60000, "l2_gather_3.84MB_table")):
+        tab = torch.randn(n_rows * 16, device=dev)
+        ms = run(1, 0, n_rows, iters // 4, table=tab)
+        rate = rows_per_launch / 4 / (ms * 1e-3)
+        res[name] = {"G_rows_per_s": round(rate / 1e9, 2), "us_per_6M": round(6e6 / rate * 1e6, 2)}
+    for n_rows, name in ((2000, "atomic_f32_w16_128KB_out"), (60000, "atomic_f32_w16_3.84MB_out")):
+        out = torch.zeros(n_rows * 16, device=dev)
+        it_a = 16
+        ms = run(2, 0, n_rows, it_a, out=out)
+        entries = grid * 16 * it_a * 64  # 64 entries (rows of 16 adds) per window
+        rate = entries / (ms * 1e-3)
+        res[name] = {"G_entries_per_s": round(rate / 1e9, 3),
+                     "G_instr_per_s": round(rate / 4 / 1e9, 3),
+                     "us_per_6M": round(6e6 / rate * 1e6, 1)}
+    res["empty_launch_us"] = round(1e3 * run(3, 0, 1, 0, g=1024), 2)
+    return {"device_cus": n_cu, "clock_ghz_assumed": clk_ghz, "grid": grid,
+            "threads_per_block": 1024, "reps": reps, "ceilings": res}
+
+
+def cpu_threads():
+    """Host threads for the oracle's timed mode: OMP_NUM_THREADS when set (the
+    share of the host's cores a job is given), else every core the process
+    may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(layouts, width, budget_s):
-    """The float64 oracle, as it is, on the host: the four directions over the
-    full matrix, repeated until about budget_s seconds have passed."""
+    """The float64 oracle, as it is, on the host: its threaded mode (slices
+    split over the host threads, private float64 outputs where the output rows
+    are not the slices) over the four directions of the full matrix. One
+    warm-up pass, then passes until about budget_s seconds (at least 5); the
+    value is the bytes of a pass over the median pass time. A single-threaded
+    pass of the sequential oracle is timed too."""
     import oracle
 
     rng = np.random.default_rng(1)
-    total_bytes, total_s, passes = 0, 0.0, 0
-    while total_s < budget_s or passes == 0:
-        for name, layout, direction, _ in DIRECTIONS:
-            L = layouts[layout]
-            m, n = L.shape
-            B = rng.standard_normal((n if direction == "AB" else m, width)).astype(np.float32)
-            t0 = time.perf_counter()
-            oracle.spmm(L, direction, B)
-            total_s += time.perf_counter() - t0
-            total_bytes += L.nbytes() + dense_bytes(L.shape, direction, width)
-        passes += 1
-    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+    threads = cpu_threads()
+    ops = []
+    for name, layout, direction, _ in DIRECTIONS:
+        L = layouts[layout]
+        m, n = L.shape
+        B = rng.standard_normal((n if direction == "AB" else m, width)).astype(np.float32)
+        ops.append((L, direction, B.astype(np.float64)))
+    pass_bytes = sum(L.nbytes() + dense_bytes(L.shape, d, width) for L, d, _ in ops)
+
+    def one_pass(fn):
+        t0 = time.perf_counter()
+        for L, d, B in ops:
+            fn(L, d, B)
+        return time.perf_counter() - t0
+
+    threaded = lambda L, d, B: oracle.spmm_threaded(L, d, B, threads)
+    one_pass(threaded)  # warm-up
+    times, spent = [], 0.0
+    while len(times) < 5 or spent < budget_s:
+        times.append(one_pass(threaded))
+        spent += times[-1]
+        if len(times) >= 200:
+            break
+    med = float(np.median(times))
+    single = one_pass(lambda L, d, B: oracle.spmm(L, d, B))
+    return {"value": round(pass_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{passes} pass(es) of the four directions over the full 60k x 2k matrix at "
-                      f"width {width}, float64, single-threaded C ({total_s:.1f} s)"}
+            "host_cpu_count": os.cpu_count(),
+            "single_thread_GBps": round(pass_bytes / single / 1e9, 4),
+            "sample": f"median of {len(times)} passes (after one warm-up) of the four directions "
+                      f"over the full 60k x 2k matrix at width {width}, float64 C oracle, threaded "
+                      f"mode on {threads} threads (host reports {os.cpu_count()} CPUs); "
+                      f"{spent:.1f} s timed; one sequential pass took {single:.2f} s"}
 
 
 def csr64_products(dev, steps):
@@ -419,6 +520,8 @@ def main():
                     help="skip the timings of the CSR past 2^31 entries")
     ap.add_argument("--other-widths", default="1,8,32,64",
                     help="widths also timed beside the headline (comma list, empty for none)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the secondary ceilings (LDS/L2 gathers, atomics, launches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter scale)")
     args = ap.parse_args()
@@ -429,6 +532,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.ceilings:
+        print(json.dumps(ceilings()), flush=True)
         return
 
     import torch
