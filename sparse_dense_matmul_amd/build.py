@@ -21,6 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvspmm.so")
+# the benchmark's ceiling probes (not part of the product library)
+PROBE_LIB = os.path.join(HERE, "libvspmm_probe.so")
+PROBE_SRC = "probe.hip"
 OBJDIR = os.path.join(HERE, "_build")
 # (source, extra defines, object name)
 UNITS = [
@@ -56,8 +59,25 @@ def flags() -> list[str]:
     ]
 
 
+def _up_to_date(obj: str, dep: str, cmd: list[str]) -> bool:
+    """True when obj was built by the same command and is newer than every
+    file its dependency list names."""
+    try:
+        t = os.path.getmtime(obj)
+        text = open(dep).read()
+        if open(obj + ".cmd").read() != " ".join(cmd):
+            return False
+    except OSError:
+        return False
+    files = text.replace("\\\n", " ").split(":", 1)[1].split()
+    return all(os.path.exists(f) and os.path.getmtime(f) <= t for f in files)
+
+
 def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = True,
-          jobs: int | None = None) -> str:
+          jobs: int | None = None, incremental: bool = False) -> str:
+    """Compile every unit and link. With incremental, a unit whose object is
+    newer than the sources and headers it was built from is not compiled
+    again (a development shortcut; the default always compiles)."""
     os.makedirs(OBJDIR, exist_ok=True)
     cc = hipcc()
     base = flags() + (extra or [])
@@ -65,7 +85,13 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = True,
     def compile_unit(unit):
         src, defs, name = unit
         obj = os.path.join(OBJDIR, name + ".o")
+        dep = os.path.join(OBJDIR, name + ".d")
         cmd = [cc] + base + defs + ["-c", "-o", obj, os.path.join(CSRC, src)]
+        if incremental and _up_to_date(obj, dep, cmd):
+            return obj
+        with open(obj + ".cmd", "w") as fh:
+            fh.write(" ".join(cmd))
+        cmd = cmd + ["-MD", "-MF", dep]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
@@ -73,15 +99,25 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = True,
 
     jobs = jobs or min(len(UNITS), max(1, os.cpu_count() or 1), 16)
     with ThreadPoolExecutor(max_workers=jobs) as pool:
+        probe = pool.submit(compile_unit, (PROBE_SRC, [], "probe"))
         objs = list(pool.map(compile_unit, UNITS))
+        probe_obj = probe.result()
     tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIB)
     return out
 
 
 if __name__ == "__main__":
-    build(extra=sys.argv[1:])
+    args = sys.argv[1:]
+    inc = "--incremental" in args
+    build(extra=[a for a in args if a != "--incremental"], incremental=inc)
