@@ -53,6 +53,36 @@ constexpr int kPieceNWR = 16;
 constexpr int kPieceGWR = 4;
 constexpr int kPieceWaveLds = 64 * kPieceNWR + 256 * kPieceGWR;
 
+// k_vcs_seg: where one wave of a launch starts. Its run is the slices
+// [s_a, s_b), entries [E_a, E_b) and groups [K_a, K_b), with K_a the group
+// holding entry E_a (past any empty groups starting there). Built once per
+// layout and launch shape by k_seg_plan.
+struct SegDesc {
+    int s_a, s_b, E_a, E_b, K_a, K_b, pad0, pad1;
+};
+
+// The slices [bb, be) that block blk of a k_vcs_rows / k_vcs_seg launch of
+// `grid` blocks owns, and its tile: the slices are `tiles` runs of
+// n_slices / tiles (one per tile of B), each cut into grid / tiles parts;
+// with a multiple of 8 tiles, the blocks of a tile share an XCD (blocks go
+// to the 8 XCDs round robin, block b to XCD b % 8), so a tile of B is
+// fetched into one L2.
+__host__ __device__ inline void seg_block_range(int blk, int grid, int tiles, int n_slices,
+                                                int &bb, int &be, int &tile) {
+    const int bpt = grid / tiles;  // blocks per tile
+    int part;
+    tile = blk / bpt;
+    part = blk - tile * bpt;
+    if (tiles % 8 == 0) {
+        const int x = blk & 7, j = blk >> 3;
+        tile = x * (tiles >> 3) + j / bpt;
+        part = j - (j / bpt) * bpt;
+    }
+    const int n_run = n_slices / tiles;
+    bb = tile * n_run + (int)((long long)part * n_run / bpt);
+    be = tile * n_run + (int)((long long)(part + 1) * n_run / bpt);
+}
+
 // The operands of one aligned walk (slices of the walked layout = rows of out).
 template <typename T>
 struct WalkArgs {
@@ -85,6 +115,13 @@ struct WalkArgs {
     // float32 CSR values with T = double: the sums run in float64 over the
     // widened values (vals unused)
     const float *vals32 = nullptr;
+    // VCS short walks: each slice's first entry (n_slices + 1) and the
+    // per-wave starts of a k_vcs_seg launch of seg_grid blocks of seg_wpb
+    // waves (null: walk with k_vcs_rows)
+    const int *he = nullptr;
+    const SegDesc *seg = nullptr;
+    int seg_grid = 0;
+    int seg_wpb = 0;
 };
 
 // Values of one type read as another (float32 CSR values summed in float64):

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace vspmm {
 
 constexpr int kSortThreads = 256;
@@ -636,6 +638,65 @@ k_tile_sum(const float *__restrict__ part, float *__restrict__ out, int tiles, s
 // ----------------------------------------------------------- utilities
 
 // Fill n bytes (a multiple of 4) at p with zeros; p is 4-byte aligned.
+// he[s] = value_ptr[major_ptr[s]] for s = 0 .. n_slices: the first entry of
+// each VCS slice (and the entry count at the end). Group numbers are clamped
+// to [0, n_groups], so a malformed structure reads nothing out of bounds.
+__global__ void __launch_bounds__(256)
+k_slice_starts(int n_slices, int n_groups, const int *__restrict__ sptr,
+               const int *__restrict__ vptr, int *__restrict__ he) {
+    for (int s = blockIdx.x * blockDim.x + threadIdx.x; s <= n_slices; s += gridDim.x * blockDim.x)
+        he[s] = vptr[min(max(sptr[s], 0), n_groups)];
+}
+
+// The starts of the waves of a k_vcs_seg launch of `grid` blocks of `wpb`
+// waves over a VCS of n_slices slices (as `tiles` runs): block b owns the
+// slices seg_block_range gives it; its waves cut the block's entries into
+// wpb equal shares, and wave k takes the slices that start in its share (the
+// last wave also every empty slice at the end). One thread per wave. Reads
+// stay in bounds for any structure (group numbers clamped to [0, n_groups]);
+// a malformed one gets a meaningless plan, as its products are undefined.
+__global__ void __launch_bounds__(256)
+k_seg_plan(int n_slices, int n_groups, const int *__restrict__ sptr,
+           const int *__restrict__ vptr, const int *__restrict__ he, int tiles, int grid, int wpb,
+           SegDesc *__restrict__ desc) {
+    const int gw = blockIdx.x * blockDim.x + threadIdx.x;
+    if (gw >= grid * wpb) return;
+    const int b = gw / wpb, w = gw - b * wpb;
+    int bb, be, tile;
+    seg_block_range(b, grid, tiles, n_slices, bb, be, tile);
+    const int EB = he[bb], EE = he[be];
+    auto first_at = [&](int k) {  // the first slice in [bb, be] starting at or after cut k
+        if (k >= wpb) return be;
+        const int cut = EB + (int)((long long)(EE - EB) * k / wpb);
+        int lo = bb, hi = be;  // he[be] = EE >= cut
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (he[mid] >= cut) hi = mid;
+            else lo = mid + 1;
+        }
+        return lo;
+    };
+    SegDesc d;
+    d.s_a = first_at(w);
+    d.s_b = first_at(w + 1);
+    d.E_a = he[d.s_a];
+    d.E_b = he[d.s_b];
+    d.K_b = min(max(sptr[d.s_b], 0), n_groups);
+    // the last group of the run starting at or before E_a (groups before it
+    // are empty: slice s_a's first group starts at E_a)
+    int lo = min(max(sptr[d.s_a], 0), d.K_b), hi = d.K_b - 1;
+    if (d.E_a < d.E_b) {
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (vptr[mid] <= d.E_a) lo = mid;
+            else hi = mid - 1;
+        }
+    }
+    d.K_a = lo;
+    d.pad0 = d.pad1 = 0;
+    desc[gw] = d;
+}
+
 __global__ void __launch_bounds__(256) k_zero(uint32_t *__restrict__ p, size_t n_words) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -47,6 +47,12 @@ struct vspmm_matrix_s {
     // and val arrays from its first entry on; block_row0 holds each block's
     // first row and then n_rows, block_ptr the blocks' rebased row pointers
     bool ptr64 = false;
+    // VCS: each slice's first entry and the per-wave starts of the k_vcs_seg
+    // walk over the handle's own layout (device, owned; one block of
+    // kSegWaves waves per CU)
+    int32_t *seg_he = nullptr;
+    SegDesc *seg_desc = nullptr;
+    int seg_grid = 0;
     std::vector<vspmm_matrix_s *> blocks;
     std::vector<int64_t> block_row0;
     int32_t *block_ptr = nullptr;
@@ -118,6 +124,9 @@ DeviceInfo device_info(int dev) {
 }
 
 constexpr int64_t kI32Max = 2147483647;
+
+// Waves per block of the k_vcs_seg walks over a layout's own slices.
+constexpr int kSegWaves = 16;
 
 bool fits_i32(int64_t x) { return x >= 0 && x <= kI32Max; }
 
@@ -201,8 +210,10 @@ Plan make_plan(int64_t n_slices, int64_t nnz, int64_t w, size_t elt, bool split_
     pl.R = 64 >> (log_g + log_ww);
     const int64_t mean = n_slices > 0 ? nnz / n_slices : 0;
     const size_t b_bytes = size_t(n_in) * size_t(w) * elt;
-    // the VCS walks address B with 32-bit byte offsets and 24-bit row numbers
-    const bool small_b = b_bytes < (size_t(1) << 32) && n_in < (int64_t(1) << 24);
+    // the VCS walks address B with 32-bit byte offsets: a row number and the
+    // row stride (w * elt bytes) each multiply in 24 bits
+    const bool small_b = b_bytes < (size_t(1) << 32) && n_in < (int64_t(1) << 24) &&
+                         size_t(w) * elt < (size_t(1) << 24);
     if (pl.R == 1 && (!vcs || small_b)) {
         if (mean >= (vcs ? kLongMean : csr_round_entries(elt))) {
             pl.kind = kLong;
@@ -290,6 +301,28 @@ void launch_zero(void *p, size_t bytes, hipStream_t s) {
     if (!words) return;
     const size_t blocks = std::min<size_t>((words / 4 + 255) / 256 + 1, 4096);
     hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t *)p, words);
+}
+
+// Each slice's first entry (he) and the starts of the waves of a k_vcs_seg
+// launch of `grid` blocks of `wpb` waves over a VCS (as `tiles` runs).
+void seg_plan(int64_t n_slices, int64_t n_groups, const int32_t *sptr, const int32_t *vptr,
+              int tiles, int grid, int wpb, int32_t *he, SegDesc *desc, int n_cu, hipStream_t s) {
+    const int64_t n = n_slices + 1;
+    const int g1 = int(std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, int64_t(n_cu) * 16)));
+    hipLaunchKernelGGL(k_slice_starts, dim3(g1), dim3(256), 0, s, int(n_slices), int(n_groups),
+                       sptr, vptr, he);
+    const int nw = grid * wpb;
+    hipLaunchKernelGGL(k_seg_plan, dim3((nw + 255) / 256), dim3(256), 0, s, int(n_slices),
+                       int(n_groups), sptr, vptr, he, tiles, grid, wpb, desc);
+}
+
+// Attaches a k_vcs_seg plan to the walk's arguments.
+template <typename T>
+void with_seg(WalkArgs<T> &a, const int32_t *he, const SegDesc *desc, int grid, int wpb) {
+    a.he = he;
+    a.seg = desc;
+    a.seg_grid = grid;
+    a.seg_wpb = wpb;
 }
 
 template <typename T>
@@ -459,6 +492,8 @@ struct OppositeWs {
     int32_t *t_idx = nullptr;      // nnz
     int32_t *t_ngroups = nullptr;  // VCS: 1
     float *partial = nullptr;      // tiled: the product's partial rows (n_bins x width)
+    int32_t *t_he = nullptr;       // VCS: first entry of each new slice (n_bins + 1)
+    SegDesc *t_seg = nullptr;      // VCS: the k_vcs_seg plan over it (seg_waves)
     // scratch
     int32_t *slice_of = nullptr, *group_of = nullptr, *vkey = nullptr;
     uint32_t *keys_a = nullptr, *keys_b = nullptr;
@@ -469,7 +504,7 @@ struct OppositeWs {
 };
 
 OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base, int64_t n_bins = -1,
-                          int64_t partial_elems = 0) {
+                          int64_t partial_elems = 0, int64_t seg_waves = -1) {
     OppositeWs w;
     Bump b{static_cast<char *>(base)};
     const size_t nnz = size_t(h.nnz);
@@ -484,6 +519,14 @@ OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base, int64_t n_bins = 
     }
     w.t_idx = b.take<int32_t>(nnz);
     if (tiled) w.partial = b.take<float>(size_t(partial_elems));
+    if (vcs) {
+        if (seg_waves < 0) {
+            const DeviceInfo di = device_info(h.device);
+            seg_waves = int64_t(di.ok ? di.n_cu : 256) * kSegWaves;
+        }
+        w.t_he = b.take<int32_t>(nb + 1);
+        w.t_seg = b.take<SegDesc>(size_t(seg_waves));
+    }
     w.slice_of = b.take<int32_t>(nnz);
     if (vcs) w.group_of = b.take<int32_t>(nnz);
     if (tiled) w.vkey = b.take<int32_t>(nnz);
@@ -802,8 +845,11 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
 }
 
 // Workspace bytes of a tiled product at width w.
+// Waves of a tiled walk's launch (one k_vcs_seg start each).
+int64_t tiled_waves(const TilePlan &tp) { return int64_t(tp.pl.grid) * (tp.pl.block / 64); }
+
 size_t tiled_ws_bytes(const vspmm_matrix_s &h, const TilePlan &tp, int64_t w) {
-    return carve_opposite(h, nullptr, tp.n_bins(), tp.n_bins() * w).bytes;
+    return carve_opposite(h, nullptr, tp.n_bins(), tp.n_bins() * w, tiled_waves(tp)).bytes;
 }
 
 // Builds the tiled layout of a VCS handle into w: entries keyed by virtual
@@ -837,13 +883,16 @@ void build_tiled(const vspmm_matrix_s &h, const OppositeWs &w, const TilePlan &t
                        w.group_of, vals, w.flag, w.gid, (float *)w.t_vals, w.t_vptr, w.t_idx);
     hipLaunchKernelGGL(k_group_major_ptr, dim3(grid_for(nb + 1, n_cu)), dim3(256), 0, s, int(nb),
                        int(nnz), w.cnt, w.gid, n_groups, w.t_ptr, w.t_vptr, w.t_ngroups);
+    // (the tiled copy holds at most nnz groups; its pointers bound the reads)
+    seg_plan(nb, nnz, w.t_ptr, w.t_vptr, tp.tiles, tp.pl.grid, tp.pl.block / 64, w.t_he, w.t_seg,
+             n_cu, s);
 }
 
 // The tiled product: build (or reuse) the layout in ws, walk it, add the
 // tiles' partial rows into out.
 vspmm_status run_tiled(const vspmm_matrix_s &h, const TilePlan &tp, const void *B, void *out,
                        int w, int dir, void *ws, int n_cu, hipStream_t s) {
-    const OppositeWs wl = carve_opposite(h, ws, tp.n_bins(), tp.n_bins() * w);
+    const OppositeWs wl = carve_opposite(h, ws, tp.n_bins(), tp.n_bins() * w, tiled_waves(tp));
     if (!ws_claim(ws, WsKey{h.id, dir, tp.tr})) {
         build_tiled(h, wl, tp, is_aligned(h, dir), n_cu, s);
         if (vspmm_status st = hip_status()) {
@@ -855,6 +904,7 @@ vspmm_status run_tiled(const vspmm_matrix_s &h, const TilePlan &tp, const void *
                                          B, wl.partial, w, tp.tr);
     a.tiles = tp.tiles;
     a.n_b_rows = int(tp.n_in);
+    with_seg(a, wl.t_he, wl.t_seg, tp.pl.grid, tp.pl.block / 64);
     launch_aligned<float>(true, tp.pl, a, s);
     const size_t n = size_t(tp.n_out) * size_t(w);
     const int grid = int(std::min<size_t>((n + 63) / 64, size_t(n_cu) * 16));
@@ -918,10 +968,12 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
                                                               h.n_major(), h.sptr, h.vptr,
                                                               h.vals, h.idx, B, out, w, ni)),
                                       n_cu, s);
-        else
-            launch_csr_or_vcs<float>(h, vcs, pl, walk_args<float>(h.n_major(), h.sptr, h.vptr,
-                                                                 h.vals, h.idx, B, out, w, ni),
-                                     n_cu, s);
+        else {
+            WalkArgs<float> a = walk_args<float>(h.n_major(), h.sptr, h.vptr, h.vals, h.idx, B,
+                                                 out, w, ni);
+            if (vcs) with_seg(a, h.seg_he, h.seg_desc, h.seg_grid, kSegWaves);
+            launch_csr_or_vcs<float>(h, vcs, pl, a, n_cu, s);
+        }
         return hip_status();
     }
     if (mode == VSPMM_ATOMIC) {
@@ -936,10 +988,12 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
     const OppositeWs wl = carve_opposite(h, ws);
     if (!ws_claim(ws, WsKey{h.id, dir, 0})) {
-        if (vcs)
+        if (vcs) {
             build_regroup(h, wl, wl.t_ptr, (float *)wl.t_vals, wl.t_vptr, wl.t_idx, wl.t_ngroups,
                           n_cu, s);
-        else
+            seg_plan(h.n_minor(), h.nnz, wl.t_ptr, wl.t_vptr, 1, n_cu, kSegWaves, wl.t_he,
+                     wl.t_seg, n_cu, s);
+        } else
             build_transpose(h, wl, wl.t_ptr, wl.t_idx, wl.t_vals, n_cu, s);
         st = hip_status();
         if (st) {
@@ -955,9 +1009,12 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         launch_aligned<double>(false, pl, values_of(h, walk_args<double>(nmin, wl.t_ptr, nullptr,
                                                                          wl.t_vals, wl.t_idx, B,
                                                                          out, w, nmaj)), s);
-    else
-        launch_aligned<float>(vcs, pl, walk_args<float>(nmin, wl.t_ptr, wl.t_vptr, wl.t_vals,
-                                                        wl.t_idx, B, out, w, nmaj), s);
+    else {
+        WalkArgs<float> a = walk_args<float>(nmin, wl.t_ptr, wl.t_vptr, wl.t_vals, wl.t_idx, B,
+                                             out, w, nmaj);
+        if (vcs) with_seg(a, wl.t_he, wl.t_seg, n_cu, kSegWaves);
+        launch_aligned<float>(vcs, pl, a, s);
+    }
     return hip_status();
 }
 
@@ -1121,6 +1178,8 @@ vspmm_status list_long_rows(vspmm_matrix_s *m, hipStream_t s) {
 }
 
 void free_handle(vspmm_matrix_s *m) {
+    if (m->seg_he) (void)hipFree(m->seg_he);
+    if (m->seg_desc) (void)hipFree(m->seg_desc);
     if (m->long_rows) (void)hipFree(m->long_rows);
     if (m->parts) (void)hipFree(m->parts);
     for (vspmm_matrix_s *b : m->blocks) vspmm_destroy(b);
@@ -1138,6 +1197,25 @@ vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
         const vspmm_status st = vspmm_validate(m, s);
         if (st) {
             delete m;
+            return st;
+        }
+    }
+    if (m->layout != VSPMM_CSR) {
+        // the k_vcs_seg plan over the handle's own slices: n_cu blocks of
+        // kSegWaves waves
+        const DeviceInfo di = device_info(m->device);
+        const int n_cu = di.ok ? di.n_cu : 256;
+        const int64_t nmaj = m->n_major();
+        if (hipMalloc(&m->seg_he, size_t(nmaj + 1) * sizeof(int32_t)) != hipSuccess ||
+            hipMalloc(&m->seg_desc, size_t(n_cu) * kSegWaves * sizeof(SegDesc)) != hipSuccess) {
+            free_handle(m);
+            return VSPMM_ERR_HIP;
+        }
+        m->seg_grid = n_cu;
+        seg_plan(nmaj, m->n_groups, m->sptr, m->vptr, 1, n_cu, kSegWaves, m->seg_he, m->seg_desc,
+                 n_cu, s);
+        if (vspmm_status st = hip_status()) {
+            free_handle(m);
             return st;
         }
     }
