@@ -4,8 +4,9 @@ width 16, all four directions, on one MI355X.
 A step is one pass of the product path over that matrix in all four
 directions: VCSR @ B and B @ VCSC (aligned walks), B @ VCSR and VCSC @ B
 (misaligned). The headline runs each direction the fastest deterministic way
-the library offers, with every workspace sized for width 16 and its schedule
-already built (the one-time builds are timed and reported separately):
+the library offers, with each deterministic direction's schedule built for
+width 16 (vspmm_schedule_create; the one-time builds and the schedules'
+resident bytes are reported separately):
 VCSR @ B as the plain aligned walk (B fits in LDS), VCSC @ B as the walk over
 the regrouped layout, and B @ VCSR and B @ VCSC over the tiled copy of the
 matrix (B's 60,000 rows cut into tiles that fit in LDS). Atomic mode, whose
@@ -297,15 +298,20 @@ def csr64_products(dev, steps):
             B = torch.rand(n_in, 1, generator=g, device=dev, dtype=tdt)
             O = torch.empty(n_out, 1, dtype=tdt, device=dev)
             for mode in (["atomic"] if direction == "AB" else ["atomic", "deterministic"]):
-                ws = A.workspace(direction, mode, 1) if mode == "deterministic" else None
+                sc = None
                 t0 = time.perf_counter()
-                A.spmm(B, direction, mode=mode, out=O, workspace=ws)  # builds the transposes
+                if mode == "deterministic":
+                    sc = A.schedule(direction, 1)  # the blocks' transposes
+                    run = lambda: sc.spmm(B, out=O)
+                else:
+                    run = lambda: A.spmm(B, direction, mode=mode, out=O)
+                run()
                 torch.cuda.synchronize()
                 first_ms = 1e3 * (time.perf_counter() - t0)
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 for _ in range(steps):
-                    A.spmm(B, direction, mode=mode, out=O, workspace=ws)
+                    run()
                 b.record(stream)
                 torch.cuda.synchronize()
                 us = 1e3 * a.elapsed_time(b) / steps
@@ -314,8 +320,9 @@ def csr64_products(dev, steps):
                       ("" if direction == "AB" else f" {mode}")
                 out[key] = {"us": round(us, 1), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
                 if mode == "deterministic":
-                    out[key]["first_call_ms"] = round(first_ms, 1)
-                del ws
+                    out[key]["schedule_build_plus_first_ms"] = round(first_ms, 1)
+                    out[key]["schedule_bytes"] = sc.nbytes
+                del sc
         del A
     del col, val, row_ptr
     torch.cuda.empty_cache()
@@ -355,13 +362,15 @@ def csr_products(dev, steps, copies=8):
                 Os = [torch.empty((n_out, w), dtype=Bs[0].dtype, device=dev) for _ in range(copies)]
                 modes = ["atomic"] if direction == "AB" else ["atomic", "deterministic"]
                 for mode in modes:
-                    wss = [h.workspace(direction, mode) for h in hs] if mode != "atomic" else \
-                        [None] * copies
-                    run = lambda k: hs[k % copies].spmm(Bs[k % copies], direction, mode=mode,
-                                                        out=Os[k % copies],
-                                                        workspace=wss[k % copies])
+                    if mode == "deterministic":  # the transposes, built once
+                        scs = [h.schedule(direction, w) for h in hs]
+                        run = lambda k: scs[k % copies].spmm(Bs[k % copies], out=Os[k % copies])
+                    else:
+                        scs = None
+                        run = lambda k: hs[k % copies].spmm(Bs[k % copies], direction, mode=mode,
+                                                            out=Os[k % copies])
                     for k in range(copies):
-                        run(k)  # warm-up; builds the deterministic schedules
+                        run(k)  # warm-up
                     torch.cuda.synchronize()
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     a.record(stream)
@@ -375,7 +384,9 @@ def csr_products(dev, steps, copies=8):
                           ("" if direction == "AB" else f" {mode}")
                     out[key] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                                 "kernel": hs[0].plan_info(w, direction, mode)["kernel_name"]}
-                    del wss
+                    if scs:
+                        out[key]["schedule_bytes"] = scs[0].nbytes
+                    del scs
         # the exact transpose on the device (vspmm_transpose_csr), once per copy
         h0 = hs[0]
         ws = h0.workspace("BA")
@@ -475,13 +486,15 @@ def other_widths(layouts, dev, widths, steps, copies=8):
             L = layouts[lay]
             out = [torch.empty((m if direction == "AB" else n, w), device=dev) for _ in range(copies)]
             size = hs[0][lay].workspace_size(direction, "deterministic", w)
-            wss = [h[lay].workspace(direction, "deterministic", w) if size else None for h in hs]
             mode = "deterministic" if size else "atomic"
-            run = lambda k: hs[k % copies][lay].spmm(Bs[k % copies][direction], direction,
-                                                     mode=mode, workspace=wss[k % copies],
-                                                     out=out[k % copies])
+            scs = [h[lay].schedule(direction, w) for h in hs] if size else None
+            if scs:
+                run = lambda k: scs[k % copies].spmm(Bs[k % copies][direction], out=out[k % copies])
+            else:
+                run = lambda k: hs[k % copies][lay].spmm(Bs[k % copies][direction], direction,
+                                                         out=out[k % copies])
             for k in range(copies):
-                run(k)  # builds the schedules
+                run(k)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -496,9 +509,11 @@ def other_widths(layouts, dev, widths, steps, copies=8):
             info = hs[0][lay].plan_info(w, direction, mode)
             per[name] = {"us": round(us, 2), "kernel": info["kernel_name"] +
                          (f" (tiled, {info['tiles']} tiles) + k_tile_sum" if info["tiles"] else "")}
+            if scs:
+                per[name]["schedule_bytes"] = scs[0].nbytes
             tot_us += us
             tot_b += nb
-            del wss, out
+            del scs, out
         res[f"w={w}"] = {"GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1), "directions": per}
     return res
 
@@ -561,7 +576,7 @@ def main():
     log(f"placing {K} copies of each operand set on the device")
     copies = []
     for _ in range(K):
-        c = {"A": {}, "ws": {}}
+        c = {"A": {}, "sc": {}}
         for lay, L in layouts.items():
             c["A"][lay] = sdm.VcsMatrix.from_arrays(lay, L.shape, *[a.clone() for a in base[lay]])
         c["B"] = {d: x.clone() for d, x in dense_d.items()}
@@ -573,30 +588,34 @@ def main():
     def run(k, d, mode):
         name, lay, direction, _ = DIRECTIONS[d]
         c = copies[k % K]
-        ws = c["ws"].get((lay, direction)) if mode == "deterministic" else None
-        c["A"][lay].spmm(c["B"][direction], direction, mode=mode, workspace=ws,
-                         out=c["out"][(lay, direction)])
+        sc = c["sc"].get((lay, direction)) if mode == "deterministic" else None
+        if sc is not None:
+            sc.spmm(c["B"][direction], out=c["out"][(lay, direction)])
+        else:
+            c["A"][lay].spmm(c["B"][direction], direction, mode=mode,
+                             out=c["out"][(lay, direction)])
 
-    # one-time build of the deterministic schedules: the opposite layout of a
-    # misaligned direction, or the tiled copy of a direction whose dense input
-    # does not fit in LDS (workspaces sized for this width)
-    build_ms = {}
+    # one-time build of the deterministic schedules (vspmm_schedule_create):
+    # the opposite layout of a misaligned direction, or the tiled copy of a
+    # direction whose dense input does not fit in LDS, for this width
+    build_ms, sched_bytes = {}, {}
     stream = torch.cuda.current_stream(dev)
     for d, (name, lay, direction, walk) in enumerate(DIRECTIONS):
         if copies[0]["A"][lay].workspace_size(direction, "deterministic", w) == 0:
             continue
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         times = []
         for k in range(K):
             c = copies[k]
-            c["ws"][(lay, direction)] = c["A"][lay].workspace(direction, "deterministic", w)
-            e0.record(stream)
-            run(k, d, "deterministic")  # first call builds, then runs pass 2
-            e1.record(stream)
+            scratch = c["A"][lay].workspace(direction, "deterministic", w)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
+            t0 = time.perf_counter()
+            c["sc"][(lay, direction)] = c["A"][lay].schedule(direction, w, workspace=scratch)
+            times.append(1e3 * (time.perf_counter() - t0))  # (the build waits for its stream)
+            del scratch
         build_ms[name] = round(float(np.median(times)), 3)
-    log(f"deterministic schedules built: {build_ms} ms (build + first product)")
+        sched_bytes[name] = copies[0]["sc"][(lay, direction)].nbytes
+    torch.cuda.empty_cache()
+    log(f"deterministic schedules built: {build_ms} ms, resident bytes {sched_bytes}")
 
     def time_direction(d, mode):
         for k in range(args.warmup):
@@ -616,7 +635,7 @@ def main():
         L = layouts[lay]
         entry = {"walk": walk}
         A0 = copies[0]["A"][lay]
-        has_ws = (lay, direction) in copies[0]["ws"]
+        has_ws = (lay, direction) in copies[0]["sc"]
         info = A0.plan_info(w, direction, "deterministic" if has_ws else "atomic")
         kernel = info["kernel_name"] + (" (tiled) + k_tile_sum" if info["tiles"] else "")
         tiled = f", tiled schedule ({info['tiles']} tiles of B)" if info["tiles"] else ""
@@ -652,7 +671,7 @@ def main():
     # graph holds a step on every copy, each direction in its headline mode
     graph = None
     if not args.no_graph:
-        modes = ["deterministic" if (lay, direction) in copies[0]["ws"] else "atomic"
+        modes = ["deterministic" if (lay, direction) in copies[0]["sc"] else "atomic"
                  for _, lay, direction, _ in DIRECTIONS]
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(device=dev)
@@ -684,9 +703,9 @@ def main():
     c0 = copies[0]
     r1 = c0["A"]["vcsr"].spmm(c0["B"]["AB"], "AB").clone()
     r2 = c0["A"]["vcsr"].spmm(c0["B"]["AB"], "AB")
-    ws = c0["ws"][("vcsc", "AB")]
-    r3 = c0["A"]["vcsc"].spmm(c0["B"]["AB"], "AB", mode="deterministic", workspace=ws).clone()
-    r4 = c0["A"]["vcsc"].spmm(c0["B"]["AB"], "AB", mode="deterministic", workspace=ws)
+    sc = c0["sc"][("vcsc", "AB")]
+    r3 = sc.spmm(c0["B"]["AB"]).clone()
+    r4 = sc.spmm(c0["B"]["AB"])
     repeat_ok = bool(torch.equal(r1, r2) and torch.equal(r3, r4))
 
     traffic, traffic_src = traffic_record(per_dir[dom]["kernel"], dom, w)
@@ -717,7 +736,9 @@ def main():
         "atomic_mode": {"value": round(atomic_bytes / (atomic_us * 1e-6) / 1e9, 2) if not
                         args.no_atomic else None, "unit": "GB/s",
                         "ms_per_step": round(atomic_us / 1e3, 5) if not args.no_atomic else None},
-        "det_build_plus_first_product_ms": build_ms,
+        "det_schedule_build_ms": build_ms,
+        "det_schedule_bytes": sched_bytes,
+        "footprint_bytes": {lay: copies[0]["A"][lay].footprint()[0] for lay in layouts},
         "graph_replay": graph,
         "roofline": {"bound": "hbm", "kernel": f"{per_dir[dom]['kernel']} ({dom})",
                      "achieved": per_dir[dom]["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",

@@ -63,6 +63,7 @@ extern "C" {
 #endif
 
 typedef struct vspmm_matrix_s *vspmm_matrix; /* opaque handle */
+typedef struct vspmm_schedule_s *vspmm_schedule; /* opaque: a built pass-2 layout */
 
 typedef enum {
     VSPMM_OK = 0,
@@ -203,11 +204,11 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
                                   size_t *bytes);
 
 /* vspmm_spmm with a mode. VSPMM_DETERMINISTIC on a misaligned direction
- * builds, on the first call with a given workspace, the matrix in the opposite
- * layout (CSR: its exact transpose; VCSR/VCSC: the same matrix regrouped by
- * the other axis) inside ws, and runs the aligned walk over it. Later calls
- * with the same handle, direction and ws reuse what is there: the caller must
- * not write into ws between them, or must call vspmm_workspace_invalidate.
+ * builds the matrix in the opposite layout (CSR: its exact transpose;
+ * VCSR/VCSC: the same matrix regrouped by the other axis) inside ws, and runs
+ * the aligned walk over it. Every call builds it again: ws holds nothing from
+ * one call to the next. To build once and run many products, use a schedule
+ * (vspmm_schedule_create).
  *
  * Tiled schedule (VCSR/VCSC, float, either direction): when B's rows do not
  * fit in a CU's LDS and ws holds at least vspmm_workspace_size_width bytes
@@ -223,10 +224,8 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * average, the tile count rises to a multiple of 8 until the mean is at most
  * 512. The
  * product writes one partial row per (tile, output row) into ws and adds them
- * in a fixed order; it repeats bit for bit. The copy is reused like the
- * opposite layout (it also depends on the tile size, which follows the
- * width). A smaller ws falls back to the path above (aligned: the plain walk,
- * ws unused).
+ * in a fixed order; it repeats bit for bit. A smaller ws falls back to the
+ * path above (aligned: the plain walk, ws unused).
  *
  * ws: device, 256-byte aligned, at least vspmm_workspace_size bytes; unused
  * (may be NULL) when the size is 0. Errors: as vspmm_spmm, plus
@@ -242,9 +241,45 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
 vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
                                         int64_t width, size_t *bytes);
 
-/* Forget any schedule cached in the workspace at ws (call before reusing
- * that memory for anything else). */
-vspmm_status vspmm_workspace_invalidate(void *ws);
+/* Schedules: the two-pass deterministic product with its first pass done
+ * once. On the regridding page the exact transpose is kept once it has been
+ * built (section "API"), the build is a two-pass counting sort (section "How
+ * it is built") and every output row is summed in a fixed order (section
+ * "Why"). A schedule holds such a built layout for one (handle, direction,
+ * width): the opposite layout
+ * of a misaligned direction, or the tiled copy where vspmm_spmm_ex would
+ * take the tiled schedule, in device memory of its own sized to what the
+ * product reads (the realized group count, not the worst case). Products
+ * through it equal vspmm_spmm_ex's in deterministic mode bit for bit.
+ *
+ * vspmm_schedule_create builds it. scratch: device, 256-byte aligned, at
+ * least vspmm_workspace_size_width(h, dir, VSPMM_DETERMINISTIC, width) bytes,
+ * used only during the call; or NULL, and the call allocates and frees
+ * scratch of its own. Waits for `stream` (it reads back the group count).
+ * Errors: _NULL, _ENUM, _DIM, _WORKSPACE (scratch too small), _HIP, _ALLOC.
+ * For an aligned direction with no tiled copy (and for an empty matrix) the
+ * schedule holds nothing and its products are the plain walk.
+ *
+ * The schedule reads the handle's arrays: destroy it before the handle. */
+vspmm_status vspmm_schedule_create(vspmm_schedule *sc, vspmm_matrix h, vspmm_direction dir,
+                                   int64_t width, void *scratch, size_t scratch_bytes,
+                                   hipStream_t stream);
+
+/* out = A @ B or B @ A through schedule sc, in its direction; width must equal
+ * the schedule's. A tiled schedule keeps the product's partial rows in its
+ * own memory: products through one schedule must not overlap in time (issue
+ * them on one stream, or wait between them). Errors: as vspmm_spmm, plus _DIM
+ * for another width. */
+vspmm_status vspmm_schedule_spmm(vspmm_schedule sc, const void *B, void *out, int64_t width,
+                                 hipStream_t stream);
+
+/* Device bytes the schedule holds (vsparse page, section "Benchmarks": device
+ * bytes are reported against the expanded form). bytes: host. Errors: _NULL. */
+vspmm_status vspmm_schedule_bytes(vspmm_schedule sc, size_t *bytes);
+
+/* Frees the schedule's memory (after its products have finished on the
+ * device). Errors: _NULL. */
+vspmm_status vspmm_schedule_destroy(vspmm_schedule sc);
 
 /* Check the structure on the device: pointer arrays start at 0, do not
  * decrease and end at their array's length; every index is in range

@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["VcsMatrix", "CsrMatrix", "VspmmError", "lib", "LIB_PATH", "EXPORTS"]
+__all__ = ["VcsMatrix", "CsrMatrix", "Schedule", "VspmmError", "lib", "LIB_PATH", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvspmm.so")
@@ -46,7 +46,10 @@ EXPORTS = {
     "vspmm_workspace_size": ([_vp, ctypes.c_int, ctypes.c_int, _P(_sz)], ctypes.c_int),
     "vspmm_spmm_ex": ([_vp, _vp, _vp, _i64, ctypes.c_int, ctypes.c_int, _vp, _sz, _vp],
                       ctypes.c_int),
-    "vspmm_workspace_invalidate": ([_vp], ctypes.c_int),
+    "vspmm_schedule_create": ([_P(_vp), _vp, ctypes.c_int, _i64, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_schedule_spmm": ([_vp, _vp, _vp, _i64, _vp], ctypes.c_int),
+    "vspmm_schedule_bytes": ([_vp, _P(_sz)], ctypes.c_int),
+    "vspmm_schedule_destroy": ([_vp], ctypes.c_int),
     "vspmm_validate": ([_vp, _vp], ctypes.c_int),
     "vspmm_transpose_csr": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_regroup_vcs": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -159,13 +162,7 @@ class SparseMatrix:
             raise ValueError(f"{name} has shape {tuple(B.shape)}, expected ({rows}, width)")
         return B
 
-    def spmm(self, B: torch.Tensor, direction: str = "AB", mode: str = "atomic",
-             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-        """``A @ B`` for ``direction="AB"`` (B: n x w, returns m x w), or
-        ``(B @ A)`` transposed for ``direction="BA"`` (B given transposed,
-        m x w; returns n x w). ``mode="deterministic"`` makes the misaligned
-        directions repeat bit for bit (needs ``workspace``, see
-        :meth:`workspace_size`)."""
+    def _operands(self, B, direction, out):
         m, n = self.shape
         n_in, n_out = (n, m) if direction == "AB" else (m, n)
         B = self._dense_in(B, n_in)
@@ -174,6 +171,18 @@ class SparseMatrix:
             out = torch.empty((n_out, w), dtype=self.dtype, device=self.device)
         elif out.shape != (n_out, w) or not out.is_contiguous() or out.dtype != self.dtype:
             raise ValueError("out must be a contiguous (n_out, width) tensor of the matrix dtype")
+        return B, out
+
+    def spmm(self, B: torch.Tensor, direction: str = "AB", mode: str = "atomic",
+             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+        """``A @ B`` for ``direction="AB"`` (B: n x w, returns m x w), or
+        ``(B @ A)`` transposed for ``direction="BA"`` (B given transposed,
+        m x w; returns n x w). ``mode="deterministic"`` makes the misaligned
+        directions repeat bit for bit (needs ``workspace``, see
+        :meth:`workspace_size`); each such call builds its layout again, see
+        :meth:`schedule` to build it once."""
+        B, out = self._operands(B, direction, out)
+        w = B.shape[1]
         d, md = DIRECTIONS[direction], MODES[mode]
         if md == 0:
             st = lib.vspmm_spmm(self._h, _ptr(B), _ptr(out), w, d, _stream(self.device))
@@ -212,13 +221,25 @@ class SparseMatrix:
 
     def workspace(self, direction: str = "BA", mode: str = "deterministic",
                   width: int | None = None) -> torch.Tensor:
-        """A fresh device workspace of the required size (256-byte aligned). The
-        library caches a built layout by workspace address; a fresh tensor may
-        reuse the address of a freed one, so its cache tag is dropped here."""
+        """A device workspace of the required size (torch's allocations are
+        256-byte aligned)."""
         nbytes = self.workspace_size(direction, mode, width)
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
-        lib.vspmm_workspace_invalidate(_ptr(ws))
-        return ws
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+
+    def schedule(self, direction: str, width: int,
+                 workspace: torch.Tensor | None = None) -> "Schedule":
+        """The deterministic product's layout for ``direction`` at ``width``,
+        built once (``vspmm_schedule_create``); ``workspace`` is build scratch
+        (``workspace_size(direction, "deterministic", width)`` bytes), or
+        None for scratch the library allocates for the call."""
+        h = _vp()
+        nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        with torch.cuda.device(self.device):
+            st = lib.vspmm_schedule_create(ctypes.byref(h), self._h, DIRECTIONS[direction],
+                                           int(width), _ptr(workspace), nbytes,
+                                           _stream(self.device))
+        _check(st, "vspmm_schedule_create")
+        return Schedule(h, self, direction, int(width))
 
     def validate(self) -> bool:
         st = lib.vspmm_validate(self._h, _stream(self.device))
@@ -248,6 +269,38 @@ class SparseMatrix:
                                2: "k_vcs_long" if vcs else "k_long",
                                3: "k_scatter"}[info["kernel"]]
         return info
+
+
+class Schedule:
+    """A built deterministic product (see ``vspmm_schedule_create``). Keeps its
+    matrix alive; products through it must not overlap in time (one stream)."""
+
+    def __init__(self, handle, matrix: SparseMatrix, direction: str, width: int):
+        self._h = handle
+        self.matrix = matrix
+        self.direction = direction
+        self.width = width
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and lib is not None:
+            lib.vspmm_schedule_destroy(h)
+            self._h = None
+
+    @property
+    def nbytes(self) -> int:
+        n = _sz(0)
+        _check(lib.vspmm_schedule_bytes(self._h, ctypes.byref(n)), "vspmm_schedule_bytes")
+        return int(n.value)
+
+    def spmm(self, B: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """The product in the schedule's direction (operands as
+        :meth:`SparseMatrix.spmm`)."""
+        B, out = self.matrix._operands(B, self.direction, out)
+        st = lib.vspmm_schedule_spmm(self._h, _ptr(B), _ptr(out), B.shape[1],
+                                     _stream(self.matrix.device))
+        _check(st, "vspmm_schedule_spmm")
+        return out
 
 
 class VcsMatrix(SparseMatrix):

@@ -32,7 +32,6 @@ struct vspmm_matrix_s {
     uint32_t flags;
     int force_group;
     int device;
-    uint64_t id;
     // CSR: rows longer than long_len (device list, owned), walked by k_long
     // apart from the short walks so one long row does not hold up a wave
     int32_t *long_rows = nullptr;
@@ -74,34 +73,6 @@ void vspmm::allow_lds(const void *fn) {
 }
 
 namespace {
-
-std::atomic<uint64_t> g_next_id{1};
-
-// Workspaces holding a built layout: ws address -> what it holds (handle id,
-// direction, and the tile rows of a tiled layout, 0 for the opposite layout).
-struct WsKey {
-    uint64_t id;
-    int dir;
-    int tr;
-    bool operator==(const WsKey &o) const { return id == o.id && dir == o.dir && tr == o.tr; }
-};
-std::mutex g_ws_mutex;
-std::unordered_map<const void *, WsKey> g_ws_cache;
-
-// True when ws already holds `want`; otherwise records it as holding it (the
-// caller builds it next, and drops the record if that fails).
-bool ws_claim(void *ws, const WsKey &want) {
-    std::lock_guard<std::mutex> lk(g_ws_mutex);
-    auto it = g_ws_cache.find(ws);
-    if (it != g_ws_cache.end() && it->second == want) return true;
-    g_ws_cache[ws] = want;
-    return false;
-}
-
-void ws_drop(void *ws) {
-    std::lock_guard<std::mutex> lk(g_ws_mutex);
-    g_ws_cache.erase(ws);
-}
 
 struct DeviceInfo {
     int n_cu = 0;
@@ -498,7 +469,7 @@ struct OppositeWs {
     int32_t *slice_of = nullptr, *group_of = nullptr, *vkey = nullptr;
     uint32_t *keys_a = nullptr, *keys_b = nullptr;
     int32_t *pay_a = nullptr, *pay_b = nullptr;
-    int32_t *flag = nullptr, *gid = nullptr, *cnt = nullptr;
+    int32_t *cnt = nullptr;
     int32_t *hist = nullptr, *bsums = nullptr, *scalars = nullptr;
     size_t bytes = 0;
 };
@@ -534,10 +505,6 @@ OppositeWs carve_opposite(const vspmm_matrix_s &h, void *base, int64_t n_bins = 
     w.keys_b = b.take<uint32_t>(nnz);
     w.pay_a = b.take<int32_t>(nnz);
     w.pay_b = b.take<int32_t>(nnz);
-    if (vcs) {
-        w.flag = b.take<int32_t>(nnz);
-        w.gid = b.take<int32_t>(nnz);
-    }
     w.cnt = b.take<int32_t>(nb + 1);
     const size_t nblocks = (nnz + kSortTile - 1) / kSortTile;
     w.hist = b.take<int32_t>(256 * std::max<size_t>(nblocks, 1));
@@ -688,6 +655,7 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
     const int64_t nnz = h.nnz;
     const int grid = grid_for(std::max<int64_t>(nnz, 1), n_cu);
     int32_t *n_groups = w.scalars;
+    int32_t *gid = w.pay_b;  // (not read when nnz is 0)
     if (nnz > 0) {
         expand_slices(h, w, n_cu, s);
         uint32_t *ka = w.keys_a, *kb = w.keys_b;
@@ -698,11 +666,15 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
         hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, h.idx, ka);
         radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(h.n_minor()), w.hist, w.bsums, s);
         bin_starts(ka, nnz, h.n_minor(), tptr, n_cu, s);
+        // the sort's other key and payload arrays are free now: group flags
+        // and group numbers
+        int32_t *flag = reinterpret_cast<int32_t *>(kb);
+        gid = pb;
         hipLaunchKernelGGL(k_group_flags, dim3(grid), dim3(256), 0, s, int(nnz), pa, ka,
-                           w.group_of, (const float *)h.vals, w.flag);
-        scan_excl(w.flag, w.gid, nnz, w.bsums, n_groups, s);
+                           w.group_of, (const float *)h.vals, flag);
+        scan_excl(flag, gid, nnz, w.bsums, n_groups, s);
         hipLaunchKernelGGL(k_group_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
-                           w.group_of, (const float *)h.vals, w.flag, w.gid, t_values,
+                           w.group_of, (const float *)h.vals, flag, gid, t_values,
                            t_value_ptr, t_indices);
     } else {
         launch_zero(n_groups, 4, s);
@@ -710,7 +682,7 @@ void build_regroup(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_majo
     }
     const int g2 = grid_for(h.n_minor() + 1, n_cu);
     hipLaunchKernelGGL(k_group_major_ptr, dim3(g2), dim3(256), 0, s, int(h.n_minor()), int(nnz),
-                       tptr, w.gid, n_groups, t_major_ptr, t_value_ptr, t_n_groups);
+                       tptr, gid, n_groups, t_major_ptr, t_value_ptr, t_n_groups);
 }
 
 // ------------------------------------------------------------ tiled layout
@@ -876,40 +848,75 @@ void build_tiled(const vspmm_matrix_s &h, const OppositeWs &w, const TilePlan &t
     hipLaunchKernelGGL(k_gather_index, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.vkey, ka);
     radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(nb), w.hist, w.bsums, s);
     bin_starts(ka, nnz, nb, w.cnt, n_cu, s);
+    // group flags and numbers in the sort's free key and payload arrays
+    int32_t *flag = reinterpret_cast<int32_t *>(kb), *gid = pb;
     hipLaunchKernelGGL(k_group_flags, dim3(grid), dim3(256), 0, s, int(nnz), pa, ka, w.group_of,
-                       vals, w.flag);
-    scan_excl(w.flag, w.gid, nnz, w.bsums, n_groups, s);
+                       vals, flag);
+    scan_excl(flag, gid, nnz, w.bsums, n_groups, s);
     hipLaunchKernelGGL(k_group_emit, dim3(grid), dim3(256), 0, s, int(nnz), pa, w.slice_of,
-                       w.group_of, vals, w.flag, w.gid, (float *)w.t_vals, w.t_vptr, w.t_idx);
+                       w.group_of, vals, flag, gid, (float *)w.t_vals, w.t_vptr, w.t_idx);
     hipLaunchKernelGGL(k_group_major_ptr, dim3(grid_for(nb + 1, n_cu)), dim3(256), 0, s, int(nb),
-                       int(nnz), w.cnt, w.gid, n_groups, w.t_ptr, w.t_vptr, w.t_ngroups);
+                       int(nnz), w.cnt, gid, n_groups, w.t_ptr, w.t_vptr, w.t_ngroups);
     // (the tiled copy holds at most nnz groups; its pointers bound the reads)
     seg_plan(nb, nnz, w.t_ptr, w.t_vptr, tp.tiles, tp.pl.grid, tp.pl.block / 64, w.t_he, w.t_seg,
              n_cu, s);
 }
 
-// The tiled product: build (or reuse) the layout in ws, walk it, add the
-// tiles' partial rows into out.
-vspmm_status run_tiled(const vspmm_matrix_s &h, const TilePlan &tp, const void *B, void *out,
-                       int w, int dir, void *ws, int n_cu, hipStream_t s) {
-    const OppositeWs wl = carve_opposite(h, ws, tp.n_bins(), tp.n_bins() * w, tiled_waves(tp));
-    if (!ws_claim(ws, WsKey{h.id, dir, tp.tr})) {
-        build_tiled(h, wl, tp, is_aligned(h, dir), n_cu, s);
-        if (vspmm_status st = hip_status()) {
-            ws_drop(ws);
-            return st;
-        }
-    }
-    WalkArgs<float> a = walk_args<float>(tp.n_bins(), wl.t_ptr, wl.t_vptr, wl.t_vals, wl.t_idx,
-                                         B, wl.partial, w, tp.tr);
+// The tiled product over a built tiled copy L: the walk writes one partial
+// row per (tile, output row) into L.partial, then the tiles' partial rows are
+// added in tile order into out.
+vspmm_status walk_tiled(const TilePlan &tp, const OppositeWs &L, const void *B, void *out, int w,
+                        int n_cu, hipStream_t s) {
+    WalkArgs<float> a = walk_args<float>(tp.n_bins(), L.t_ptr, L.t_vptr, L.t_vals, L.t_idx, B,
+                                         L.partial, w, tp.tr);
     a.tiles = tp.tiles;
     a.n_b_rows = int(tp.n_in);
-    with_seg(a, wl.t_he, wl.t_seg, tp.pl.grid, tp.pl.block / 64);
+    with_seg(a, L.t_he, L.t_seg, tp.pl.grid, tp.pl.block / 64);
     launch_aligned<float>(true, tp.pl, a, s);
     const size_t n = size_t(tp.n_out) * size_t(w);
     const int grid = int(std::min<size_t>((n + 63) / 64, size_t(n_cu) * 16));
-    hipLaunchKernelGGL(k_tile_sum, dim3(grid), dim3(256), 0, s, wl.partial, (float *)out,
+    hipLaunchKernelGGL(k_tile_sum, dim3(grid), dim3(256), 0, s, L.partial, (float *)out,
                        tp.tiles, n);
+    return hip_status();
+}
+
+// Whether the walks split entry lanes by the matrix (a CSR's default) or by
+// the width (a VCS's default).
+bool split_of(const vspmm_matrix_s &h) {
+    return (h.flags & VSPMM_SPLIT_MATRIX) ||
+           (h.layout == VSPMM_CSR && !(h.flags & VSPMM_SPLIT_WIDTH));
+}
+
+// The opposite layout of h built into L: a CSR's exact transpose, or a VCS
+// regrouped by the other axis with the k_vcs_seg plan over its slices.
+void build_opposite(const vspmm_matrix_s &h, const OppositeWs &L, int n_cu, hipStream_t s) {
+    if (h.layout == VSPMM_CSR) {
+        build_transpose(h, L, L.t_ptr, L.t_idx, L.t_vals, n_cu, s);
+        return;
+    }
+    build_regroup(h, L, L.t_ptr, (float *)L.t_vals, L.t_vptr, L.t_idx, L.t_ngroups, n_cu, s);
+    // (the regrouped layout holds at most nnz groups; its pointers bound the reads)
+    seg_plan(h.n_minor(), h.nnz, L.t_ptr, L.t_vptr, 1, n_cu, kSegWaves, L.t_he, L.t_seg, n_cu, s);
+}
+
+// Pass 2 of a deterministic misaligned product: the aligned walk over the
+// opposite layout in L.
+vspmm_status walk_opposite(const vspmm_matrix_s &h, const OppositeWs &L, const void *B, void *out,
+                           int w, int n_cu, hipStream_t s) {
+    const bool vcs = h.layout != VSPMM_CSR;
+    const int64_t nmin = h.n_minor(), nmaj = h.n_major();
+    const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_of(h), h.force_group, B, out, n_cu,
+                              nmaj, vcs);
+    if (h.dtype != VSPMM_F32) {
+        launch_aligned<double>(false, pl, values_of(h, walk_args<double>(nmin, L.t_ptr, nullptr,
+                                                                         L.t_vals, L.t_idx, B,
+                                                                         out, w, nmaj)), s);
+    } else {
+        WalkArgs<float> a = walk_args<float>(nmin, L.t_ptr, L.t_vptr, L.t_vals, L.t_idx, B, out,
+                                             w, nmaj);
+        if (vcs) with_seg(a, L.t_he, L.t_seg, n_cu, kSegWaves);
+        launch_aligned<float>(vcs, pl, a, s);
+    }
     return hip_status();
 }
 
@@ -931,7 +938,8 @@ vspmm_status check_product(const vspmm_matrix_s &h, const void *B, void *out, in
 }
 
 vspmm_status run_blocked(const vspmm_matrix_s &h, const void *B, void *out, int w, int dir,
-                         int mode, void *ws, size_t ws_bytes, hipStream_t s);
+                         int mode, void *ws, size_t ws_bytes, hipStream_t s,
+                         const vspmm_schedule_s *sc = nullptr);
 
 // One product. With `accumulate`, a misaligned atomic product adds into out
 // instead of overwriting it (used for the row blocks of an int64 CSR).
@@ -946,8 +954,7 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     const DeviceInfo di = device_info(h.device);
     const int n_cu = di.ok ? di.n_cu : 256;
     const bool vcs = h.layout != VSPMM_CSR;
-    const bool split_matrix = (h.flags & VSPMM_SPLIT_MATRIX) ||
-                              (!vcs && !(h.flags & VSPMM_SPLIT_WIDTH));
+    const bool split_matrix = split_of(h);
     const int w = int(width);
     if (h.nnz == 0) {
         if (!accumulate) launch_zero(out, size_t(no) * size_t(w) * h.elt(), s);
@@ -956,8 +963,12 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
     if (h.ptr64) return run_blocked(h, B, out, w, dir, mode, ws, ws_bytes, s);
     if (mode == VSPMM_DETERMINISTIC && ws && aligned(ws, 256)) {
         const TilePlan tp = tile_plan(h, dir, w, n_cu, split_matrix, B, ws);
-        if (tp.ok && ws_bytes >= tiled_ws_bytes(h, tp, w))
-            return run_tiled(h, tp, B, out, w, dir, ws, n_cu, s);
+        if (tp.ok && ws_bytes >= tiled_ws_bytes(h, tp, w)) {
+            const OppositeWs L = carve_opposite(h, ws, tp.n_bins(), tp.n_bins() * w,
+                                                tiled_waves(tp));
+            build_tiled(h, L, tp, is_aligned(h, dir), n_cu, s);
+            return walk_tiled(tp, L, B, out, w, n_cu, s);
+        }
     }
     if (is_aligned(h, dir)) {
         const int64_t ni = h.n_minor();
@@ -983,65 +994,59 @@ vspmm_status run_product(const vspmm_matrix_s &h, const void *B, void *out, int6
         else launch_scatter_any<float>(vcs, pl, h, B, out, w, no, s);
         return hip_status();
     }
-    // deterministic: build (or reuse) the opposite layout, then walk it aligned
+    // deterministic: build the opposite layout in ws, then walk it aligned
     const OppositeWs need = carve_opposite(h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-    const OppositeWs wl = carve_opposite(h, ws);
-    if (!ws_claim(ws, WsKey{h.id, dir, 0})) {
-        if (vcs) {
-            build_regroup(h, wl, wl.t_ptr, (float *)wl.t_vals, wl.t_vptr, wl.t_idx, wl.t_ngroups,
-                          n_cu, s);
-            seg_plan(h.n_minor(), h.nnz, wl.t_ptr, wl.t_vptr, 1, n_cu, kSegWaves, wl.t_he,
-                     wl.t_seg, n_cu, s);
-        } else
-            build_transpose(h, wl, wl.t_ptr, wl.t_idx, wl.t_vals, n_cu, s);
-        st = hip_status();
-        if (st) {
-            ws_drop(ws);
-            return st;
-        }
-    }
-    const int64_t nmin = h.n_minor();
-    const int64_t nmaj = h.n_major();
-    const Plan pl = make_plan(nmin, h.nnz, w, h.elt(), split_matrix, h.force_group, B, out,
-                              n_cu, nmaj, vcs);
-    if (h.dtype != VSPMM_F32)
-        launch_aligned<double>(false, pl, values_of(h, walk_args<double>(nmin, wl.t_ptr, nullptr,
-                                                                         wl.t_vals, wl.t_idx, B,
-                                                                         out, w, nmaj)), s);
-    else {
-        WalkArgs<float> a = walk_args<float>(nmin, wl.t_ptr, wl.t_vptr, wl.t_vals, wl.t_idx, B,
-                                             out, w, nmaj);
-        if (vcs) with_seg(a, wl.t_he, wl.t_seg, n_cu, kSegWaves);
-        launch_aligned<float>(vcs, pl, a, s);
-    }
-    return hip_status();
+    const OppositeWs L = carve_opposite(h, ws);
+    build_opposite(h, L, n_cu, s);
+    if (vspmm_status st2 = hip_status()) return st2;
+    return walk_opposite(h, L, B, out, w, n_cu, s);
 }
 
-// Workspace of a deterministic B @ A over an int64 CSR: 256 bytes, one
-// region per row block for its exact transpose, then (with more than one non-empty block)
-// the n_cols x width buffer each later block's product lands in before it is
+}  // namespace
+
+// A deterministic product's pass-2 layout, built once and kept in device
+// memory the schedule owns, sized to what the walks read.
+struct vspmm_schedule_s {
+    const vspmm_matrix_s *h = nullptr;
+    int dir = 0;
+    int64_t width = 0;
+    int kind = 0;         // a SchedKind
+    TilePlan tp;          // kSchedTiled: the tile plan the copy was built for
+    OppositeWs L;         // the built arrays, inside mem
+    void *mem = nullptr;  // owned device memory
+    size_t bytes = 0;
+    // kSchedBlocked (int64 CSR, B @ A): one schedule per non-empty row block
+    // (null for empty ones), and, with more than one, the buffer each later
+    // block's product lands in before it is added to out (inside mem)
+    std::vector<vspmm_schedule_s *> subs;
+    void *sum = nullptr;
+};
+
+namespace {
+
+// Workspace of a deterministic B @ A over an int64 CSR: one region for a row
+// block's exact transpose (built again for each block, in stream order, so
+// one region serves them all), then, with more than one non-empty block, the
+// n_cols x width buffer each later block's product lands in before it is
 // added to out.
 struct BlockedWs {
-    std::vector<void *> sub;
-    std::vector<size_t> sub_bytes;
+    void *sub = nullptr;
+    size_t sub_bytes = 0;
     void *sum = nullptr;
     size_t bytes = 0;
 };
 
 BlockedWs carve_blocked(const vspmm_matrix_s &h, void *base, int64_t width) {
     BlockedWs L;
-    // the first 256 bytes stay unused: the workspace cache tags base itself
-    // with this handle, and block 0's region with block 0
-    size_t off = 256;
     int live = 0;
     for (const vspmm_matrix_s *b : h.blocks) {
-        const size_t nb = b->nnz > 0 ? align256(carve_opposite(*b, nullptr).bytes) : 0;
-        L.sub.push_back(base ? static_cast<char *>(base) + off : nullptr);
-        L.sub_bytes.push_back(nb);
-        off += nb;
-        live += b->nnz > 0;
+        if (b->nnz <= 0) continue;
+        L.sub_bytes = std::max(L.sub_bytes, align256(carve_opposite(*b, nullptr).bytes));
+        ++live;
     }
+    L.sub = base;
+    size_t off = L.sub_bytes;
     if (live > 1 && width > 0) {
         L.sum = base ? static_cast<char *>(base) + off : nullptr;
         off += align256(size_t(h.n_cols) * size_t(width) * h.elt());
@@ -1050,13 +1055,29 @@ BlockedWs carve_blocked(const vspmm_matrix_s &h, void *base, int64_t width) {
     return L;
 }
 
+void launch_accumulate(void *out, const void *sum, size_t n_el, size_t e, int n_cu,
+                       hipStream_t s) {
+    const unsigned g = (unsigned)std::min<size_t>((n_el + 255) / 256, size_t(n_cu) * 8);
+    if (e == 8)
+        hipLaunchKernelGGL(k_accumulate<double>, dim3(g), dim3(256), 0, s,
+                           static_cast<double *>(out), static_cast<const double *>(sum), n_el);
+    else
+        hipLaunchKernelGGL(k_accumulate<float>, dim3(g), dim3(256), 0, s,
+                           static_cast<float *>(out), static_cast<const float *>(sum), n_el);
+}
+
+vspmm_status schedule_product(const vspmm_schedule_s &sc, const void *B, void *out,
+                              hipStream_t s);
+
 // A product over an int64 CSR, block by block. A @ B: each block writes its
 // own rows of out. B @ A: each block meets its rows of B and adds into all of
 // out, with atomics (out zeroed once), or, deterministically, block 0's
 // product written to out and each later block's added to it in block order,
-// so the sum repeats bit for bit.
+// so the sum repeats bit for bit (each block's transpose built in ws, or taken
+// from the schedule sc).
 vspmm_status run_blocked(const vspmm_matrix_s &h, const void *B, void *out, int w, int dir,
-                         int mode, void *ws, size_t ws_bytes, hipStream_t s) {
+                         int mode, void *ws, size_t ws_bytes, hipStream_t s,
+                         const vspmm_schedule_s *sc) {
     const size_t e = h.elt();
     const size_t nb = h.blocks.size();
     if (dir == VSPMM_AB) {
@@ -1081,39 +1102,209 @@ vspmm_status run_blocked(const vspmm_matrix_s &h, const void *B, void *out, int 
         }
         return hip_status();
     }
-    const BlockedWs need = carve_blocked(h, nullptr, w);
-    if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-    const BlockedWs L = carve_blocked(h, ws, w);
-    // a workspace that does not hold this handle's transposes makes every
-    // block build its own again
-    if (!ws_claim(ws, WsKey{h.id, dir, 0}))
-        for (size_t b = 0; b < nb; ++b)
-            if (L.sub_bytes[b]) ws_drop(L.sub[b]);
+    BlockedWs L;
+    if (sc) {
+        L.sum = sc->sum;
+    } else {
+        const BlockedWs need = carve_blocked(h, nullptr, w);
+        if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+        L = carve_blocked(h, ws, w);
+    }
     const DeviceInfo di = device_info(h.device);
     const int n_cu = di.ok ? di.n_cu : 256;
     bool first = true;
     for (size_t b = 0; b < nb; ++b) {
         if (h.blocks[b]->nnz == 0) continue;
         void *dst = first ? out : L.sum;
-        if (vspmm_status st = run_product(*h.blocks[b], b_rows(b), dst, w, dir, mode, L.sub[b],
-                                          L.sub_bytes[b], s)) {
-            ws_drop(ws);
-            return st;
-        }
-        if (!first) {
-            const unsigned g = (unsigned)std::min<size_t>((n_el + 255) / 256, size_t(n_cu) * 8);
-            if (e == 8)
-                hipLaunchKernelGGL(k_accumulate<double>, dim3(g), dim3(256), 0, s,
-                                   static_cast<double *>(out), static_cast<const double *>(L.sum),
-                                   n_el);
-            else
-                hipLaunchKernelGGL(k_accumulate<float>, dim3(g), dim3(256), 0, s,
-                                   static_cast<float *>(out), static_cast<const float *>(L.sum),
-                                   n_el);
-        }
+        const vspmm_status st =
+            sc ? schedule_product(*sc->subs[b], b_rows(b), dst, s)
+               : run_product(*h.blocks[b], b_rows(b), dst, w, dir, mode, L.sub, L.sub_bytes, s);
+        if (st) return st;
+        if (!first) launch_accumulate(out, L.sum, n_el, e, n_cu, s);
         first = false;
     }
     return hip_status();
+}
+
+// ------------------------------------------------------------- schedules
+
+enum SchedKind { kSchedPlain = 0, kSchedOpposite = 1, kSchedTiled = 2, kSchedBlocked = 3 };
+
+void schedule_free(vspmm_schedule_s *sc) {
+    if (!sc) return;
+    for (vspmm_schedule_s *sub : sc->subs) schedule_free(sub);
+    if (sc->mem) (void)hipFree(sc->mem);
+    delete sc;
+}
+
+// The resident arrays of a built layout: the pointers, the group values and
+// pointers at the realized group count G (VCS), the indices, the k_vcs_seg
+// plan, and (tiled) the product's partial rows.
+OppositeWs carve_resident(const vspmm_matrix_s &h, void *base, int64_t n_bins, int64_t G,
+                          int64_t partial_elems, int64_t seg_waves) {
+    OppositeWs r;
+    Bump b{static_cast<char *>(base)};
+    const size_t nnz = size_t(h.nnz), nb = size_t(n_bins);
+    const bool vcs = h.layout != VSPMM_CSR;
+    r.t_ptr = b.take<int32_t>(nb + 1);
+    r.t_vals = b.take<char>((vcs ? size_t(G) : nnz) * h.val_elt());
+    if (vcs) r.t_vptr = b.take<int32_t>(size_t(G) + 1);
+    r.t_idx = b.take<int32_t>(nnz);
+    if (partial_elems > 0) r.partial = b.take<float>(size_t(partial_elems));
+    if (vcs) {
+        r.t_he = b.take<int32_t>(nb + 1);
+        r.t_seg = b.take<SegDesc>(size_t(seg_waves));
+    }
+    r.bytes = align256(b.off);
+    return r;
+}
+
+vspmm_status copy_d2d(void *dst, const void *src, size_t bytes, hipStream_t s) {
+    if (!bytes) return VSPMM_OK;
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess
+               ? VSPMM_OK
+               : VSPMM_ERR_HIP;
+}
+
+// Builds the layout of sc (kind, tp set) in scratch S, reads back its group
+// count, and keeps an exact-size copy in memory the schedule owns. Waits for
+// the stream.
+vspmm_status schedule_fill(vspmm_schedule_s *sc, const OppositeWs &S, int n_cu, hipStream_t s) {
+    const vspmm_matrix_s &h = *sc->h;
+    const bool vcs = h.layout != VSPMM_CSR;
+    const bool tiled = sc->kind == kSchedTiled;
+    const int64_t nb = tiled ? sc->tp.n_bins() : h.n_minor();
+    const int64_t seg_waves = tiled ? tiled_waves(sc->tp) : int64_t(n_cu) * kSegWaves;
+    if (tiled)
+        build_tiled(h, S, sc->tp, is_aligned(h, sc->dir), n_cu, s);
+    else
+        build_opposite(h, S, n_cu, s);
+    if (vspmm_status st = hip_status()) return st;
+    int32_t G = 0;
+    if (vcs && hipMemcpyAsync(&G, S.t_ngroups, sizeof(G), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return VSPMM_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return VSPMM_ERR_HIP;
+    if (G < 0 || G > h.nnz) return VSPMM_ERR_HIP;
+    const int64_t partial = tiled ? nb * sc->width : 0;
+    const OppositeWs need = carve_resident(h, nullptr, nb, G, partial, seg_waves);
+    if (hipMalloc(&sc->mem, need.bytes) != hipSuccess) {
+        sc->mem = nullptr;
+        return VSPMM_ERR_HIP;
+    }
+    sc->bytes = need.bytes;
+    OppositeWs &R = sc->L;
+    R = carve_resident(h, sc->mem, nb, G, partial, seg_waves);
+    const size_t nnz = size_t(h.nnz);
+    vspmm_status st = copy_d2d(R.t_ptr, S.t_ptr, size_t(nb + 1) * 4, s);
+    if (!st) st = copy_d2d(R.t_vals, S.t_vals, (vcs ? size_t(G) : nnz) * h.val_elt(), s);
+    if (!st && vcs) st = copy_d2d(R.t_vptr, S.t_vptr, (size_t(G) + 1) * 4, s);
+    if (!st) st = copy_d2d(R.t_idx, S.t_idx, nnz * 4, s);
+    if (!st && vcs) st = copy_d2d(R.t_he, S.t_he, size_t(nb + 1) * 4, s);
+    if (!st && vcs) st = copy_d2d(R.t_seg, S.t_seg, size_t(seg_waves) * sizeof(SegDesc), s);
+    if (!st && hipStreamSynchronize(s) != hipSuccess) st = VSPMM_ERR_HIP;
+    return st;
+}
+
+// Builds a schedule for (h, dir, width) with build scratch `scratch` of
+// scratch_bytes, or, when scratch is null, scratch of its own for the call.
+vspmm_status schedule_build(vspmm_schedule_s *sc, void *scratch, size_t scratch_bytes,
+                            hipStream_t s) {
+    const vspmm_matrix_s &h = *sc->h;
+    const DeviceInfo di = device_info(h.device);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    size_t need = 0;
+    if (h.ptr64) {
+        if (sc->dir != VSPMM_BA || h.nnz == 0 || sc->width == 0) return VSPMM_OK;
+        sc->kind = kSchedBlocked;
+        const BlockedWs bw = carve_blocked(h, nullptr, sc->width);
+        need = bw.sub_bytes;
+    } else if (h.nnz > 0 && sc->width > 0) {
+        alignas(256) static const float probe[64] = {};
+        const TilePlan tp = tile_plan(h, sc->dir, sc->width, n_cu, split_of(h), probe, probe);
+        if (tp.ok) {
+            sc->kind = kSchedTiled;
+            sc->tp = tp;
+            need = tiled_ws_bytes(h, tp, sc->width);
+        } else if (!is_aligned(h, sc->dir)) {
+            sc->kind = kSchedOpposite;
+            need = carve_opposite(h, nullptr).bytes;
+        }
+    }
+    if (sc->kind == kSchedPlain) return VSPMM_OK;
+    void *own = nullptr;
+    if (scratch) {
+        if (scratch_bytes < need || !aligned(scratch, 256)) return VSPMM_ERR_WORKSPACE;
+    } else {
+        if (hipMalloc(&own, std::max<size_t>(need, 256)) != hipSuccess) return VSPMM_ERR_HIP;
+        scratch = own;
+    }
+    vspmm_status st = VSPMM_OK;
+    if (sc->kind == kSchedBlocked) {
+        sc->subs.assign(h.blocks.size(), nullptr);
+        int live = 0;
+        for (size_t b = 0; b < h.blocks.size() && !st; ++b) {
+            if (h.blocks[b]->nnz == 0) continue;
+            ++live;
+            auto *sub = new (std::nothrow) vspmm_schedule_s{};
+            if (!sub) {
+                st = VSPMM_ERR_ALLOC;
+                break;
+            }
+            sc->subs[b] = sub;
+            sub->h = h.blocks[b];
+            sub->dir = sc->dir;
+            sub->width = sc->width;
+            sub->kind = kSchedOpposite;
+            st = schedule_fill(sub, carve_opposite(*sub->h, scratch), n_cu, s);
+        }
+        if (!st && live > 1) {
+            const size_t sum_bytes = size_t(h.n_cols) * size_t(sc->width) * h.elt();
+            if (hipMalloc(&sc->mem, sum_bytes) != hipSuccess) {
+                sc->mem = nullptr;
+                st = VSPMM_ERR_HIP;
+            } else {
+                sc->sum = sc->mem;
+                sc->bytes = sum_bytes;
+            }
+        }
+    } else {
+        const OppositeWs S =
+            sc->kind == kSchedTiled
+                ? carve_opposite(h, scratch, sc->tp.n_bins(), sc->tp.n_bins() * sc->width,
+                                 tiled_waves(sc->tp))
+                : carve_opposite(h, scratch);
+        st = schedule_fill(sc, S, n_cu, s);
+    }
+    if (own) {
+        if (hipStreamSynchronize(s) != hipSuccess && !st) st = VSPMM_ERR_HIP;
+        (void)hipFree(own);
+    }
+    return st;
+}
+
+// One product through a built schedule.
+vspmm_status schedule_product(const vspmm_schedule_s &sc, const void *B, void *out,
+                              hipStream_t s) {
+    const vspmm_matrix_s &h = *sc.h;
+    const int w = int(sc.width);
+    const DeviceInfo di = device_info(h.device);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    switch (sc.kind) {
+        case kSchedOpposite: return walk_opposite(h, sc.L, B, out, w, n_cu, s);
+        case kSchedTiled: {
+            // the launch's lane split follows B's alignment; the tiles, grid
+            // and so the built copy and its plan do not
+            const TilePlan tp = tile_plan(h, sc.dir, w, n_cu, split_of(h), B, sc.L.partial);
+            if (!tp.ok || tp.tr != sc.tp.tr || tp.tiles != sc.tp.tiles ||
+                tp.pl.grid != sc.tp.pl.grid || tp.pl.block != sc.tp.pl.block)
+                return VSPMM_ERR_UNSUPPORTED;
+            return walk_tiled(tp, sc.L, B, out, w, n_cu, s);
+        }
+        case kSchedBlocked:
+            return run_blocked(h, B, out, w, sc.dir, VSPMM_DETERMINISTIC, nullptr, 0, s, &sc);
+        default:
+            return run_product(h, B, out, w, sc.dir, VSPMM_DETERMINISTIC, nullptr, 0, s);
+    }
 }
 
 // Waves of the short CSR walk's grid (16 per CU), one entry-balanced row
@@ -1192,7 +1383,6 @@ vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
         delete m;
         return VSPMM_ERR_HIP;
     }
-    m->id = g_next_id.fetch_add(1);
     if (m->flags & VSPMM_VALIDATE) {
         const vspmm_status st = vspmm_validate(m, s);
         if (st) {
@@ -1369,7 +1559,6 @@ vspmm_status vspmm_create_csr64(vspmm_matrix *h, int64_t n_rows, int64_t n_cols,
         delete m;
         return VSPMM_ERR_HIP;
     }
-    m->id = g_next_id.fetch_add(1);
     // blocks of whole rows, each of at most block_nnz entries unless one row
     // alone holds more (then at most 2^30)
     std::vector<int32_t> ptr32;
@@ -1427,13 +1616,6 @@ vspmm_status vspmm_create_csr64(vspmm_matrix *h, int64_t n_rows, int64_t n_cols,
 
 vspmm_status vspmm_destroy(vspmm_matrix h) {
     if (!h) return VSPMM_ERR_NULL;
-    {
-        std::lock_guard<std::mutex> lk(g_ws_mutex);
-        for (auto it = g_ws_cache.begin(); it != g_ws_cache.end();) {
-            if (it->second.id == h->id) it = g_ws_cache.erase(it);
-            else ++it;
-        }
-    }
     free_handle(h);
     return VSPMM_OK;
 }
@@ -1468,8 +1650,54 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
     return run_product(*h, B, out, width, dir, mode, ws, ws_bytes, stream);
 }
 
-vspmm_status vspmm_workspace_invalidate(void *ws) {
-    ws_drop(ws);
+vspmm_status vspmm_schedule_create(vspmm_schedule *sc, vspmm_matrix h, vspmm_direction dir,
+                                   int64_t width, void *scratch, size_t scratch_bytes,
+                                   hipStream_t stream) {
+    if (!sc) return VSPMM_ERR_NULL;
+    *sc = nullptr;
+    if (vspmm_status st = check_handle(h)) return st;
+    if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
+    if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
+    auto *s = new (std::nothrow) vspmm_schedule_s{};
+    if (!s) return VSPMM_ERR_ALLOC;
+    s->h = h;
+    s->dir = dir;
+    s->width = width;
+    vspmm_status st;
+    try {
+        st = schedule_build(s, scratch, scratch_bytes, stream);
+    } catch (...) {
+        st = VSPMM_ERR_ALLOC;
+    }
+    if (st) {
+        schedule_free(s);
+        return st;
+    }
+    *sc = s;
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_schedule_spmm(vspmm_schedule sc, const void *B, void *out, int64_t width,
+                                 hipStream_t stream) {
+    if (!sc) return VSPMM_ERR_NULL;
+    if (vspmm_status st = check_product(*sc->h, B, out, width, sc->dir)) return st;
+    if (width != sc->width) return VSPMM_ERR_DIM;
+    if (width == 0 || n_out(*sc->h, sc->dir) == 0) return VSPMM_OK;
+    return schedule_product(*sc, B, out, stream);
+}
+
+vspmm_status vspmm_schedule_bytes(vspmm_schedule sc, size_t *bytes) {
+    if (!sc || !bytes) return VSPMM_ERR_NULL;
+    size_t n = sc->bytes;
+    for (const vspmm_schedule_s *sub : sc->subs)
+        if (sub) n += sub->bytes;
+    *bytes = n;
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_schedule_destroy(vspmm_schedule sc) {
+    if (!sc) return VSPMM_ERR_NULL;
+    schedule_free(sc);
     return VSPMM_OK;
 }
 
@@ -1533,7 +1761,6 @@ vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_
     if (!t_row_ptr || (h->nnz > 0 && (!t_col || !t_val))) return VSPMM_ERR_NULL;
     const OppositeWs need = carve_opposite(*h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-    ws_drop(ws);  // ws no longer holds a cached layout
     const DeviceInfo di = device_info(h->device);
     build_transpose(*h, carve_opposite(*h, ws), t_row_ptr, t_col, t_val, di.ok ? di.n_cu : 256,
                     stream);
@@ -1549,7 +1776,6 @@ vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_va
     if (h->nnz > 0 && (!t_values || !t_indices)) return VSPMM_ERR_NULL;
     const OppositeWs need = carve_opposite(*h, nullptr);
     if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-    ws_drop(ws);  // ws no longer holds a cached layout
     const DeviceInfo di = device_info(h->device);
     build_regroup(*h, carve_opposite(*h, ws), t_major_ptr, t_values, t_value_ptr, t_indices,
                   t_n_groups, di.ok ? di.n_cu : 256, stream);
@@ -1569,7 +1795,6 @@ vspmm_status vspmm_expand_vcs(vspmm_matrix h, vspmm_format format, int32_t sort_
     if (needs_ws) {
         const OppositeWs need = carve_opposite(*h, nullptr);
         if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
-        ws_drop(ws);  // ws no longer holds a cached layout
     }
     const DeviceInfo di = device_info(h->device);
     build_expand(*h, own, sort_indices != 0, needs_ws ? carve_opposite(*h, ws) : OppositeWs{}, ptr,

@@ -51,8 +51,8 @@ def replay_matches_eager(run, B, fresh, n_replays=3):
                                                    ("vcsr", "BA", "deterministic"),
                                                    ("vcsr", "BA", "atomic")])
 def test_vcs_graph(count60k, layout, direction, mode):
-    """VCSR@B (aligned), the tiled B@VCSC and B@VCSR (deterministic, schedule
-    built before the capture) and B@VCSR with float atomics (fill kernel, then
+    """VCSR@B (aligned), the tiled B@VCSC and B@VCSR (deterministic, through a
+    schedule built before the capture) and B@VCSR with float atomics (fill kernel, then
     the scatter), all at width 16."""
     dev = need_gpu()
     L = count60k[layout]
@@ -64,9 +64,12 @@ def test_vcs_graph(count60k, layout, direction, mode):
         (lambda k: W.dense_normal(np.random.default_rng(k), rows, 16))
     B = to_dev(gen(100), dev)
     out = torch.empty((n_out, 16), device=dev)
-    ws = A.workspace(direction, mode, 16) if mode == "deterministic" else None
-    replay_matches_eager(lambda: A.spmm(B, direction, mode=mode, out=out, workspace=ws), B,
-                         lambda k: to_dev(gen(k), dev))
+    if mode == "deterministic":
+        sc = A.schedule(direction, 16)
+        run = lambda: sc.spmm(B, out=out)
+    else:
+        run = lambda: A.spmm(B, direction, mode=mode, out=out)
+    replay_matches_eager(run, B, lambda k: to_dev(gen(k), dev))
 
 
 @pytest.mark.parametrize("width", [1, 32])

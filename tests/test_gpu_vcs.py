@@ -251,9 +251,10 @@ def test_bad_arguments_raise():
 
 
 def test_fresh_workspace_at_a_reused_address(orc, small):
-    """A workspace freed and reallocated at the same address (the caching
-    allocator's habit) after other data overwrote it: the binding's fresh
-    workspace drops the cache tag, so the schedule is rebuilt, not reused."""
+    """A workspace overwritten between two deterministic calls, then freed and
+    reallocated at the same address (the caching allocator's habit) after
+    other data overwrote it: every call builds its layout again, so neither
+    reads what another user left there."""
     dev = need_gpu()
     L = small["vcsr"]
     A = vcs_handle(L, dev)
@@ -263,6 +264,9 @@ def test_fresh_workspace_at_a_reused_address(orc, small):
     first = A.spmm(Bd, "BA", mode="deterministic", workspace=ws).clone()
     addr, n = ws.data_ptr(), ws.numel()
     ws.fill_(0x5A)  # another user of the memory
+    same = A.spmm(Bd, "BA", mode="deterministic", workspace=ws)
+    assert torch.equal(same.view(torch.int32), first.view(torch.int32))
+    ws.fill_(0x3C)
     del ws
     ws2 = A.workspace("BA", "deterministic")
     assert ws2.numel() == n
