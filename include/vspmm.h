@@ -234,6 +234,23 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
                            vspmm_direction dir, vspmm_mode mode, void *ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* vspmm_spmm_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument, and the call allocates nothing. Its workspace is a
+ * device array inside the library of VSPMM_NOALLOC_WS_BYTES (64 MiB), one
+ * per device, held from the library's first use on that device until the
+ * process ends. A product whose workspace
+ * (vspmm_workspace_size; with the width for an int64 CSR) exceeds it
+ * returns VSPMM_ERR_WORKSPACE and enqueues nothing; the tiled copy is taken
+ * when it fits. Every call on a device shares that device's array and leaves
+ * its contents behind (each call rebuilds what it reads): calls that overlap
+ * in time on one device race and must not be issued so (one stream, or a
+ * wait between them). Results equal vspmm_spmm_ex's bit for bit in
+ * deterministic mode. Errors: as vspmm_spmm_ex. */
+#define VSPMM_NOALLOC_WS_BYTES ((size_t)64 << 20)
+vspmm_status vspmm_spmm_noalloc(vspmm_matrix h, const void *B, void *out, int64_t width,
+                                vspmm_direction dir, vspmm_mode mode, hipStream_t stream);
+
 /* Bytes of workspace for a product of the given width: in deterministic
  * mode, what the tiled schedule needs when it applies (see vspmm_spmm_ex),
  * else the same as vspmm_workspace_size. bytes: host. Errors: as
@@ -252,17 +269,18 @@ vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vsp
  * product reads (the realized group count, not the worst case). Products
  * through it equal vspmm_spmm_ex's in deterministic mode bit for bit.
  *
- * vspmm_schedule_create builds it. scratch: device, 256-byte aligned, at
+ * vspmm_schedule_create builds it. build_ws: device, 256-byte aligned, at
  * least vspmm_workspace_size_width(h, dir, VSPMM_DETERMINISTIC, width) bytes,
- * used only during the call; or NULL, and the call allocates and frees
- * scratch of its own. Waits for `stream` (it reads back the group count).
- * Errors: _NULL, _ENUM, _DIM, _WORKSPACE (scratch too small), _HIP, _ALLOC.
+ * used only during the call; or NULL, and the call allocates and frees a
+ * build workspace of its own. Waits for `stream` (it reads back the group
+ * count). Errors: _NULL, _ENUM, _DIM, _WORKSPACE (build_ws too small), _HIP,
+ * _ALLOC.
  * For an aligned direction with no tiled copy (and for an empty matrix) the
  * schedule holds nothing and its products are the plain walk.
  *
  * The schedule reads the handle's arrays: destroy it before the handle. */
 vspmm_status vspmm_schedule_create(vspmm_schedule *sc, vspmm_matrix h, vspmm_direction dir,
-                                   int64_t width, void *scratch, size_t scratch_bytes,
+                                   int64_t width, void *build_ws, size_t build_ws_bytes,
                                    hipStream_t stream);
 
 /* out = A @ B or B @ A through schedule sc, in its direction; width must equal

@@ -46,6 +46,7 @@ EXPORTS = {
     "vspmm_workspace_size": ([_vp, ctypes.c_int, ctypes.c_int, _P(_sz)], ctypes.c_int),
     "vspmm_spmm_ex": ([_vp, _vp, _vp, _i64, ctypes.c_int, ctypes.c_int, _vp, _sz, _vp],
                       ctypes.c_int),
+    "vspmm_spmm_noalloc": ([_vp, _vp, _vp, _i64, ctypes.c_int, ctypes.c_int, _vp], ctypes.c_int),
     "vspmm_schedule_create": ([_P(_vp), _vp, ctypes.c_int, _i64, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_schedule_spmm": ([_vp, _vp, _vp, _i64, _vp], ctypes.c_int),
     "vspmm_schedule_bytes": ([_vp, _P(_sz)], ctypes.c_int),

@@ -62,15 +62,26 @@ struct vspmm_matrix_s {
     size_t val_elt() const { return dtype == VSPMM_F64 ? 8 : 4; }
 };
 
-// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory.
+// Lets a kernel use up to the whole LDS of a CU as dynamic shared memory
+// (once per kernel; a fixed table, so a product allocates no host memory).
 void vspmm::allow_lds(const void *fn) {
     static std::mutex mu;
-    static std::unordered_map<const void *, bool> done;
+    static const void *done[1024];
+    static int n_done = 0;
     std::lock_guard<std::mutex> lk(mu);
-    if (done[fn]) return;
+    for (int i = 0; i < n_done; ++i)
+        if (done[i] == fn) return;
     (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsMax));
-    done[fn] = true;
+    if (n_done < 1024) done[n_done++] = fn;
 }
+
+// The workspace of vspmm_spmm_noalloc: a file-scope device array, one copy
+// per device, held from the library's first use on a device until the
+// process ends. On the host its name is only a stand-in for the symbol: host
+// code takes each device's address of it with hipGetSymbolAddress and passes
+// that, never the name.
+constexpr size_t kStaticScratchBytes = VSPMM_NOALLOC_WS_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -95,6 +106,28 @@ DeviceInfo device_info(int dev) {
 }
 
 constexpr int64_t kI32Max = 2147483647;
+
+// Each device's address of `scratch`, taken once per device with that device
+// current (at handle creation, or at the first no-alloc product).
+std::mutex g_scratch_mutex;
+void *g_scratch[64] = {};
+
+vspmm_status static_scratch(int dev, void **p) {
+    if (dev < 0 || dev >= 64) return VSPMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return VSPMM_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return VSPMM_ERR_HIP;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr) return VSPMM_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *p = g_scratch[dev];
+    return VSPMM_OK;
+}
 
 // Waves per block of the k_vcs_seg walks over a layout's own slices.
 constexpr int kSegWaves = 16;
@@ -1205,9 +1238,9 @@ vspmm_status schedule_fill(vspmm_schedule_s *sc, const OppositeWs &S, int n_cu, 
     return st;
 }
 
-// Builds a schedule for (h, dir, width) with build scratch `scratch` of
-// scratch_bytes, or, when scratch is null, scratch of its own for the call.
-vspmm_status schedule_build(vspmm_schedule_s *sc, void *scratch, size_t scratch_bytes,
+// Builds a schedule for (h, dir, width) in the build workspace build_ws of
+// build_ws_bytes, or, when build_ws is null, in one of its own for the call.
+vspmm_status schedule_build(vspmm_schedule_s *sc, void *build_ws, size_t build_ws_bytes,
                             hipStream_t s) {
     const vspmm_matrix_s &h = *sc->h;
     const DeviceInfo di = device_info(h.device);
@@ -1232,11 +1265,11 @@ vspmm_status schedule_build(vspmm_schedule_s *sc, void *scratch, size_t scratch_
     }
     if (sc->kind == kSchedPlain) return VSPMM_OK;
     void *own = nullptr;
-    if (scratch) {
-        if (scratch_bytes < need || !aligned(scratch, 256)) return VSPMM_ERR_WORKSPACE;
+    if (build_ws) {
+        if (build_ws_bytes < need || !aligned(build_ws, 256)) return VSPMM_ERR_WORKSPACE;
     } else {
         if (hipMalloc(&own, std::max<size_t>(need, 256)) != hipSuccess) return VSPMM_ERR_HIP;
-        scratch = own;
+        build_ws = own;
     }
     vspmm_status st = VSPMM_OK;
     if (sc->kind == kSchedBlocked) {
@@ -1255,7 +1288,7 @@ vspmm_status schedule_build(vspmm_schedule_s *sc, void *scratch, size_t scratch_
             sub->dir = sc->dir;
             sub->width = sc->width;
             sub->kind = kSchedOpposite;
-            st = schedule_fill(sub, carve_opposite(*sub->h, scratch), n_cu, s);
+            st = schedule_fill(sub, carve_opposite(*sub->h, build_ws), n_cu, s);
         }
         if (!st && live > 1) {
             const size_t sum_bytes = size_t(h.n_cols) * size_t(sc->width) * h.elt();
@@ -1270,9 +1303,9 @@ vspmm_status schedule_build(vspmm_schedule_s *sc, void *scratch, size_t scratch_
     } else {
         const OppositeWs S =
             sc->kind == kSchedTiled
-                ? carve_opposite(h, scratch, sc->tp.n_bins(), sc->tp.n_bins() * sc->width,
+                ? carve_opposite(h, build_ws, sc->tp.n_bins(), sc->tp.n_bins() * sc->width,
                                  tiled_waves(sc->tp))
-                : carve_opposite(h, scratch);
+                : carve_opposite(h, build_ws);
         st = schedule_fill(sc, S, n_cu, s);
     }
     if (own) {
@@ -1383,6 +1416,10 @@ vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
         delete m;
         return VSPMM_ERR_HIP;
     }
+    // set-up of the no-alloc product on this device (a failure here is
+    // reported by vspmm_spmm_noalloc, which tries again)
+    void *unused = nullptr;
+    (void)static_scratch(m->device, &unused);
     if (m->flags & VSPMM_VALIDATE) {
         const vspmm_status st = vspmm_validate(m, s);
         if (st) {
@@ -1651,7 +1688,7 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
 }
 
 vspmm_status vspmm_schedule_create(vspmm_schedule *sc, vspmm_matrix h, vspmm_direction dir,
-                                   int64_t width, void *scratch, size_t scratch_bytes,
+                                   int64_t width, void *build_ws, size_t build_ws_bytes,
                                    hipStream_t stream) {
     if (!sc) return VSPMM_ERR_NULL;
     *sc = nullptr;
@@ -1665,7 +1702,7 @@ vspmm_status vspmm_schedule_create(vspmm_schedule *sc, vspmm_matrix h, vspmm_dir
     s->width = width;
     vspmm_status st;
     try {
-        st = schedule_build(s, scratch, scratch_bytes, stream);
+        st = schedule_build(s, build_ws, build_ws_bytes, stream);
     } catch (...) {
         st = VSPMM_ERR_ALLOC;
     }
@@ -1699,6 +1736,25 @@ vspmm_status vspmm_schedule_destroy(vspmm_schedule sc) {
     if (!sc) return VSPMM_ERR_NULL;
     schedule_free(sc);
     return VSPMM_OK;
+}
+
+vspmm_status vspmm_spmm_noalloc(vspmm_matrix h, const void *B, void *out, int64_t width,
+                                vspmm_direction dir, vspmm_mode mode, hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
+    if (dir != VSPMM_AB && dir != VSPMM_BA) return VSPMM_ERR_ENUM;
+    if (width < 0 || !fits_i32(width)) return VSPMM_ERR_DIM;
+    size_t need = 0;
+    if (vspmm_status st = vspmm_workspace_size_width(h, dir, mode, width, &need)) return st;
+    // a product that needs a workspace larger than the array, even without
+    // the tiled copy, is refused before anything is enqueued
+    size_t base_need = 0;
+    if (vspmm_status st = vspmm_workspace_size(h, dir, mode, &base_need)) return st;
+    if (h->ptr64 && mode == VSPMM_DETERMINISTIC && dir == VSPMM_BA) base_need = need;
+    if (base_need > kStaticScratchBytes) return VSPMM_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (vspmm_status st = static_scratch(h->device, &ws)) return st;
+    return run_product(*h, B, out, width, dir, mode, ws, kStaticScratchBytes, stream);
 }
 
 vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
