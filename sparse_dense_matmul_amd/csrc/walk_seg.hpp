@@ -323,6 +323,9 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
 
         while (E < E_b) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this round's loads
+            // the current slice is the first one RE holds (row0): its end
+            // (a round that closed all 64 slices it held left kFar in e1)
+            cur.e1 = cur.i < cur.s_end ? readlane(RE, 0) : kFar;
             // the round ends at the run's end, after NWR windows, or where the
             // groups held in GS end (group K + 64 GWR - 1 starts there)
             int gs_last = readlane(GS[GWR - 1], 63);
