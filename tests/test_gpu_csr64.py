@@ -4,7 +4,8 @@ while the column indices can stay int32). The library cuts the rows into
 blocks of whole rows and walks each as an int32 CSR. Small block sizes drive
 the blocked products against the float64 oracle at sizes it finishes in
 seconds; one matrix of more than 2^31 entries, built on the device, is checked
-on sampled rows against the oracle and by the dot-product identity."""
+against the oracle on sampled rows of A @ x and on every output of B @ A, in
+float32 and with float32 values summed in float64."""
 
 import numpy as np
 import pytest
@@ -127,14 +128,20 @@ def test_structure_and_workspace_errors(regrid32):
     assert info["entry_lanes"] >= 1
 
 
+@pytest.mark.timeout(900)
 def test_more_than_2_31_entries(orc):
     """2^21 rows of 1,025 entries: 2,149,580,800 entries, past int32. Column
     indices uniform on 4,096 columns and values U(0,1) drawn on the device
-    (seeded), float32 values summed in float64. A @ x on sampled rows (the
-    first and last rows of each block, the row holding entry 2^31, and random
-    rows) against the oracle row by row; B @ A (atomic and deterministic)
-    through <A x, y> = <x, A^T y> and against each other; the deterministic
-    product repeats bit for bit."""
+    (seeded); x and y U(0,1) in float32. Two instances over the same arrays:
+    float32 values summed in float64, and float32 throughout. For each: A @ x
+    on sampled rows (the first and last rows of each block, the row holding
+    entry 2^31, and random rows) against the oracle row by row; B @ A (atomic,
+    deterministic through vspmm_spmm_ex, and through a schedule) on every one
+    of the 4,096 outputs against the oracle run over the host copy of the
+    matrix in row chunks (each under 2^31 entries; their float64 sums added);
+    the deterministic products repeat bit for bit and the schedule's equal
+    spmm_ex's. Values and operands are nonnegative, so |A||B| = AB is the
+    error scale."""
     import sparse_dense_matmul_amd as sdm
     dev = need_gpu()
     n_rows, L, n_cols = 2**21, 1025, 4096
@@ -150,26 +157,44 @@ def test_more_than_2_31_entries(orc):
         col[s:e] = torch.randint(0, n_cols, (e - s,), generator=g, device=dev, dtype=torch.int32)
         val[s:e] = torch.rand(e - s, generator=g, device=dev)
     row_ptr = torch.arange(n_rows + 1, dtype=torch.int64, device=dev) * L
-    A = sdm.CsrMatrix.from_arrays((n_rows, n_cols), row_ptr, col, val, dtype=torch.float64)
-    x = torch.rand(n_cols, 1, generator=g, device=dev, dtype=torch.float64)
-    y = torch.rand(n_rows, 1, generator=g, device=dev, dtype=torch.float64)
-    Ax = A.spmm(x, "AB")
-    yA_atomic = A.spmm(y, "BA")
-    ws = A.workspace("BA", "deterministic", 1)
-    yA = A.spmm(y, "BA", mode="deterministic", workspace=ws)
-    assert torch.equal(yA, A.spmm(y, "BA", mode="deterministic", workspace=ws))
+    x32 = torch.rand(n_cols, 1, generator=g, device=dev)
+    y32 = torch.rand(n_rows, 1, generator=g, device=dev)
+    got = {}
+    for name, dt in (("f32 values, f64 sums", torch.float64), ("f32", torch.float32)):
+        A = sdm.CsrMatrix.from_arrays((n_rows, n_cols), row_ptr, col, val, dtype=dt)
+        x, y = x32.to(dt), y32.to(dt)
+        Ax = A.spmm(x, "AB")
+        yA_atomic = A.spmm(y, "BA")
+        ws = A.workspace("BA", "deterministic", 1)
+        yA = A.spmm(y, "BA", mode="deterministic", workspace=ws)
+        assert torch.equal(yA, A.spmm(y, "BA", mode="deterministic", workspace=ws)), name
+        del ws
+        sc = A.schedule("BA", 1)
+        assert torch.equal(sc.spmm(y), yA), name
+        del sc
+        got[name] = (Ax.cpu().numpy(), yA.cpu().numpy(), yA_atomic.cpu().numpy())
+        del A, Ax, yA, yA_atomic
+        torch.cuda.empty_cache()
+    col_h, val_h = col.cpu().numpy(), val.cpu().numpy()
+    xh, yh = x32.cpu().numpy(), y32.cpu().numpy()
     # rows per block of 2^30 entries: 1,047,552
     per = (2**30) // L
     sample = [0, 1, per - 1, per, per + 1, 2 * per - 1, 2 * per, (2**31) // L, n_rows - 1]
     sample += np.random.default_rng(7).integers(0, n_rows, 24).tolist()
-    xh = x.cpu().numpy()
-    got = Ax.cpu().numpy()
+    tols = {"f32 values, f64 sums": 1e-12, "f32": 1e-5}
     for r in sample:
-        C1 = W.Csr((1, n_cols), np.array([0, L], dtype=np.int32),
-                   col[r * L:(r + 1) * L].cpu().numpy(), val[r * L:(r + 1) * L].cpu().numpy())
-        check_close(orc, C1, "AB", xh, got[r:r + 1], tol=1e-12, where=f"row {r}")
-    lhs = float((Ax * y).sum())
-    for name, v in (("deterministic", yA), ("atomic", yA_atomic)):
-        rhs = float((x * v).sum())
-        assert abs(lhs - rhs) <= 1e-10 * abs(lhs), (name, lhs, rhs)
-    assert torch.allclose(yA, yA_atomic, rtol=1e-12, atol=0)
+        C1 = W.Csr((1, n_cols), np.array([0, L], dtype=np.int32), col_h[r * L:(r + 1) * L],
+                   val_h[r * L:(r + 1) * L])
+        for name, (Ax, _, _) in got.items():
+            check_close(orc, C1, "AB", xh, Ax[r:r + 1], tol=tols[name], where=f"{name} row {r}")
+    ref = np.zeros((n_cols, 1))
+    rows_per = 2**18  # 268,697,600 entries per chunk
+    for r0 in range(0, n_rows, rows_per):
+        r1 = min(n_rows, r0 + rows_per)
+        Cc = W.Csr((r1 - r0, n_cols), (np.arange(r1 - r0 + 1, dtype=np.int64) * L).astype(np.int32),
+                   col_h[r0 * L:r1 * L], val_h[r0 * L:r1 * L])
+        ref += orc.spmm(Cc, "BA", yh[r0:r1])
+    for name, (_, yA, yA_atomic) in got.items():
+        for mode, v in (("deterministic", yA), ("atomic", yA_atomic)):
+            rel, zeros_ok = orc.max_rel_error(v, ref, ref)
+            assert zeros_ok and rel <= tols[name], (name, mode, rel)

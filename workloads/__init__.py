@@ -366,3 +366,46 @@ def tiny_real(m: int, n: int, density: float, rng: np.random.Generator, dtype=np
     rows, cols = np.nonzero(mask)
     vals = rng.random(rows.size).astype(dtype)
     return Triplets((m, n), rows.astype(np.int64), cols.astype(np.int64), vals)
+
+
+def shuffled_vcs(L: Vcs, rng: np.random.Generator, n_dup: int = 0) -> Vcs:
+    """The same matrix stored in another order the layout allows: the value
+    groups of each slice permuted, and the indices of each group permuted.
+    With ``n_dup`` > 0, that many entries are also repeated: an index of one
+    group is appended to another group of the same slice, so that slice holds
+    the index twice, under two values (stored entries add, as a COO sum does;
+    this changes the matrix)."""
+    n_major = L.major_ptr.size - 1
+    G = L.values.size
+    sizes = np.diff(L.value_ptr.astype(np.int64))
+    slice_of_group = np.repeat(np.arange(n_major), np.diff(L.major_ptr.astype(np.int64)))
+    perm = np.lexsort((rng.random(G), slice_of_group))  # new group k = old group perm[k]
+    newpos = np.empty(G, dtype=np.int64)
+    newpos[perm] = np.arange(G)
+    group_of_entry = np.repeat(np.arange(G), sizes)
+    ent_group = newpos[group_of_entry]
+    ent_idx = L.indices.astype(np.int64)
+    ent_key = rng.random(ent_idx.size)
+    if n_dup and G:
+        # entries whose slice has at least two groups
+        n_groups_of_slice = np.diff(L.major_ptr.astype(np.int64))
+        ok = np.flatnonzero(n_groups_of_slice[slice_of_group[group_of_entry]] >= 2)
+        pick = rng.choice(ok, size=min(n_dup, ok.size), replace=False)
+        extra_group, extra_idx = [], []
+        for e in pick:
+            g = group_of_entry[e]
+            s = slice_of_group[g]
+            g0, g1 = int(L.major_ptr[s]), int(L.major_ptr[s + 1])
+            other = int(rng.integers(g0, g1 - 1))
+            other += other >= g  # any group of the slice but g
+            extra_group.append(newpos[other])
+            extra_idx.append(ent_idx[e])
+        ent_group = np.concatenate([ent_group, np.array(extra_group, np.int64)])
+        ent_idx = np.concatenate([ent_idx, np.array(extra_idx, np.int64)])
+        ent_key = np.concatenate([ent_key, rng.random(len(extra_idx))])
+    order = np.lexsort((ent_key, ent_group))
+    new_sizes = np.bincount(ent_group, minlength=G)
+    value_ptr = np.zeros(G + 1, dtype=np.int64)
+    np.cumsum(new_sizes, out=value_ptr[1:])
+    return Vcs(L.layout, L.shape, L.major_ptr.copy(), L.values[perm].copy(),
+               value_ptr.astype(np.int32), ent_idx[order].astype(np.int32))
