@@ -76,6 +76,11 @@ def load(path: str | None = None):
     lib.orc_spmm_csr_threaded.argtypes = [ctypes.c_int, i64, i64, i32p, i32p, dp, dp, i64, dp,
                                           ctypes.c_int]
     lib.orc_spmm_csr_threaded.restype = ctypes.c_int
+    lib.orc_spmm_vcs_scaled.argtypes = [ctypes.c_int, ctypes.c_int, i64, i32p, dp, i32p, i32p,
+                                        dp, dp, dp, i64, dp]
+    lib.orc_spmm_vcs_scaled.restype = None
+    lib.orc_spmm_csr_scaled.argtypes = [ctypes.c_int, i64, i32p, i32p, dp, dp, dp, dp, i64, dp]
+    lib.orc_spmm_csr_scaled.restype = None
     lib.orc_expand_vcs.argtypes = [i64, i32p, vp, i32p, i32p, i32p, i32p, vp]
     lib.orc_expand_vcs.restype = None
     lib.orc_transpose_csr.argtypes = [i64, i64, i32p, i32p, vp, ctypes.c_int, i32p, i32p, vp]
@@ -209,6 +214,50 @@ def spmm_threaded(A, direction, B, threads, lib=None) -> np.ndarray:
     if st != 0:
         raise MemoryError("the threaded oracle could not allocate its private outputs")
     return out
+
+
+def spmm_view(A, direction, B, row_stat, col_stat, lib=None) -> np.ndarray:
+    """The product of the normalized view whose stored entries (r, c, v) act
+    as v * row_stat[r] * col_stat[c] (the library's "scale" view); otherwise
+    as :func:`spmm`."""
+    lib = lib or load()
+    m, n = A.shape
+    B = _f64(B)
+    w = B.shape[1] if B.ndim == 2 else 1
+    n_in, n_out = (n, m) if direction == "AB" else (m, n)
+    if B.shape[0] != n_in:
+        raise ValueError(f"dense operand has {B.shape[0]} rows, expected {n_in}")
+    rs, cs = _f64(row_stat).reshape(-1), _f64(col_stat).reshape(-1)
+    if rs.size != m or cs.size != n:
+        raise ValueError("row_stat and col_stat must have n_rows and n_cols entries")
+    out = np.zeros((n_out, w), dtype=np.float64)
+    if hasattr(A, "major_ptr"):
+        major_ptr, value_ptr, indices = _i32(A.major_ptr), _i32(A.value_ptr), _i32(A.indices)
+        n_major = m if A.layout == "vcsr" else n
+        lib.orc_spmm_vcs_scaled(LAYOUTS[A.layout], DIRS[direction], n_major, _p(major_ptr),
+                                _p(_f64(A.values)), _p(value_ptr), _p(indices), _p(rs), _p(cs),
+                                _p(B), w, _p(out))
+    else:
+        row_ptr, col = _i32(A.row_ptr), _i32(A.col)
+        lib.orc_spmm_csr_scaled(DIRS[direction], m, _p(row_ptr), _p(col), _p(_f64(A.val)),
+                                _p(rs), _p(cs), _p(B), w, _p(out))
+    return out
+
+
+def abs_scale_view(A, direction, B, row_stat, col_stat, lib=None) -> np.ndarray:
+    """``|G| |B|`` for the "scale" view's transformed entries G: the scale of
+    each output's rounding error."""
+    absA = _abs_values(A)
+    return spmm_view(absA, direction, np.abs(_f64(B)), np.abs(_f64(row_stat)),
+                     np.abs(_f64(col_stat)), lib=lib)
+
+
+def _abs_values(A):
+    """The same container with every stored value replaced by its magnitude."""
+    import dataclasses
+    if hasattr(A, "major_ptr"):
+        return dataclasses.replace(A, values=np.abs(np.asarray(A.values)))
+    return dataclasses.replace(A, val=np.abs(np.asarray(A.val)))
 
 
 def abs_scale(A, direction, B, want=None, lib=None) -> np.ndarray:

@@ -131,6 +131,39 @@ void orc_spmm_csr(int dir, int64_t n_rows, const int32_t *row_ptr, const int32_t
             entry(dir, r, col[p], val[p], B, w, out, want);
 }
 
+/* --------------------------------------------- products, normalized view */
+
+/* The product of a normalized view (vsparse page, introduction: a view
+ * transforms each stored value on the fly; section "The layout stays
+ * compressed": it carries O(n_rows + n_cols) statistics). The page does not
+ * give its transforms; this is the library's one closed form: a stored entry
+ * (r, c, v) contributes g = v * row_stat[r] * col_stat[c] in place of v.
+ * Otherwise as orc_spmm_vcs and orc_spmm_csr (out zeroed by the caller). */
+void orc_spmm_vcs_scaled(int layout, int dir, int64_t n_major,
+                         const int32_t *major_ptr, const double *values,
+                         const int32_t *value_ptr, const int32_t *indices,
+                         const double *row_stat, const double *col_stat,
+                         const double *B, int64_t w, double *out) {
+    for (int64_t s = 0; s < n_major; ++s)
+        for (int64_t k = major_ptr[s]; k < major_ptr[s + 1]; ++k)
+            for (int64_t p = value_ptr[k]; p < value_ptr[k + 1]; ++p) {
+                int64_t r = layout == 1 ? s : indices[p];
+                int64_t c = layout == 1 ? indices[p] : s;
+                double g = values[k] * row_stat[r] * col_stat[c];
+                entry(dir, r, c, g, B, w, out, NULL);
+            }
+}
+
+void orc_spmm_csr_scaled(int dir, int64_t n_rows, const int32_t *row_ptr, const int32_t *col,
+                         const double *val, const double *row_stat, const double *col_stat,
+                         const double *B, int64_t w, double *out) {
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int64_t p = row_ptr[r]; p < row_ptr[r + 1]; ++p) {
+            double g = val[p] * row_stat[r] * col_stat[col[p]];
+            entry(dir, r, col[p], g, B, w, out, NULL);
+        }
+}
+
 /* ------------------------------------------------- products, threaded mode */
 
 /* The timed mode of the same products, on n_threads host threads (OpenMP).

@@ -16,10 +16,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MUTANTS = [
     ("sign", "dst[c] += v * src[c];", "dst[c] -= v * src[c];"),
     ("dropped_last_entry", "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1]; ++p) {\n"
-     "                int64_t r = layout", "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1] - 1; ++p) {\n"
-     "                int64_t r = layout"),
-    ("transposed_layout", "int64_t r = layout == 1 ? s : indices[p];\n                int64_t c = layout == 1 ? indices[p] : s;",
-     "int64_t r = layout == 2 ? s : indices[p];\n                int64_t c = layout == 2 ? indices[p] : s;"),
+     "                int64_t r = layout == 1 ? s : indices[p];\n"
+     "                int64_t c = layout == 1 ? indices[p] : s;\n"
+     "                entry(dir, r, c, values[k]",
+     "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1] - 1; ++p) {\n"
+     "                int64_t r = layout == 1 ? s : indices[p];\n"
+     "                int64_t c = layout == 1 ? indices[p] : s;\n"
+     "                entry(dir, r, c, values[k]"),
+    ("transposed_layout", "int64_t r = layout == 1 ? s : indices[p];\n                int64_t c = layout == 1 ? indices[p] : s;\n"
+     "                entry(dir, r, c, values[k]",
+     "int64_t r = layout == 2 ? s : indices[p];\n                int64_t c = layout == 2 ? indices[p] : s;\n"
+     "                entry(dir, r, c, values[k]"),
     ("first_group_value", "entry(dir, r, c, values[k], B, w, out, want);",
      "entry(dir, r, c, values[major_ptr[s]], B, w, out, want);"),
     ("transposed_operand", "if (!want || want[r]) axpy(v, B + c * w, out + r * w, w);",
@@ -40,6 +47,21 @@ MUTANTS = [
      "for (int64_t u = 0; u + 1 < nt; ++u) out[e] += priv[u * n_el + e];"),
     ("threaded_shared_copy", "double *dst = rows_are_slices ? out : priv + t * n_el;",
      "double *dst = rows_are_slices ? out : priv;"),
+    # the normalized view
+    ("view_drops_col_stat", "double g = values[k] * row_stat[r] * col_stat[c];",
+     "double g = values[k] * row_stat[r];"),
+    ("view_dropped_last_entry", "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1]; ++p) {\n"
+     "                int64_t r = layout == 1 ? s : indices[p];\n"
+     "                int64_t c = layout == 1 ? indices[p] : s;\n"
+     "                double g",
+     "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1] - 1; ++p) {\n"
+     "                int64_t r = layout == 1 ? s : indices[p];\n"
+     "                int64_t c = layout == 1 ? indices[p] : s;\n"
+     "                double g"),
+    ("view_row_stat_twice", "double g = values[k] * row_stat[r] * col_stat[c];",
+     "double g = values[k] * row_stat[r] * row_stat[r];"),
+    ("view_csr_drops_row_stat", "double g = val[p] * row_stat[r] * col_stat[col[p]];",
+     "double g = val[p] * col_stat[col[p]];"),
 ]
 
 
@@ -74,6 +96,8 @@ PY_MUTANTS = [
      "np.abs(_f64(A.val)),\n                    _f64(B)"),
     ("abs_scale_signed_values", "np.abs(_f64(A.values))", "_f64(A.values)"),
     ("abs_scale_signed_csr_values", "np.abs(_f64(A.val))", "_f64(A.val)"),
+    ("abs_scale_view_signed_stats", "np.abs(_f64(row_stat)),\n                     np.abs(_f64(col_stat))",
+     "_f64(row_stat),\n                     _f64(col_stat)"),
 ]
 
 

@@ -497,3 +497,51 @@ def test_threaded_real_data(orc, threads):
             else:
                 rel, zeros_ok = orc.max_rel_error(got, seq, orc.abs_scale(L, direction, B))
                 assert rel <= 1e-13 and zeros_ok, (name, direction, rel)
+
+
+# ------------------------------------------------------ normalized view
+
+@pytest.mark.parametrize("seed", range(8))
+def test_view_brute_force_integer_exact(orc, seed):
+    """The "scale" view's product equals the triple loop over the dense
+    matrix with every entry multiplied by its row's and its column's
+    statistic (integer statistics, zeros and negatives included, so every
+    sum is exact): all layouts, both directions."""
+    rng = np.random.default_rng(3000 + seed)
+    m, n = (int(x) for x in rng.integers(1, 11, size=2))
+    t = W.tiny_count(m, n, rng.uniform(0.2, 0.9), 16, rng)
+    r = rng.integers(-3, 4, size=m).astype(np.float64)
+    c = rng.integers(-3, 4, size=n).astype(np.float64)
+    G = dense_of(t) * r[:, None] * c[None, :]
+    w = int(rng.integers(1, 5))
+    for direction, rows in (("AB", n), ("BA", m)):
+        B = W.dense_int(rng, rows, w, dtype=np.float64)
+        want = brute(G, direction, B)
+        for name, L in layouts_of(t).items():
+            assert np.array_equal(orc.spmm_view(L, direction, B, r, c), want), (name, direction)
+
+
+def test_view_hand_worked(orc):
+    """A = [[1, 2], [1, -2]], row statistics (2, -1), column statistics (3,
+    0.5): the transformed entries are [[6, 2], [-3, 1]]. By hand: G B =
+    [[4, 20], [-4, -8]], |G||B| = [[8, 20], [4, 10]]; for B G (B given
+    transposed): [[-3, -9], [5, -1]], with scale [[15, 9], [5, 3]]."""
+    t, B, Bt = _signed_hand_matrix()
+    r, c = np.array([2.0, -1.0]), np.array([3.0, 0.5])
+    for name, L in layouts_of(t).items():
+        assert np.array_equal(orc.spmm_view(L, "AB", B, r, c), [[4.0, 20.0], [-4.0, -8.0]]), name
+        assert np.array_equal(orc.abs_scale_view(L, "AB", B, r, c), [[8.0, 20.0], [4.0, 10.0]])
+        assert np.array_equal(orc.spmm_view(L, "BA", Bt, r, c), [[-3.0, -9.0], [5.0, -1.0]]), name
+        assert np.array_equal(orc.abs_scale_view(L, "BA", Bt, r, c), [[15.0, 9.0], [5.0, 3.0]])
+
+
+def test_view_unit_statistics_is_the_product(orc):
+    """Statistics of 1 leave every value as stored: the view's product is the
+    plain product, bit for bit, on real data."""
+    rng = np.random.default_rng(41)
+    t = W.tiny_real(9, 7, 0.5, rng)
+    for name, L in layouts_of(t).items():
+        for direction, rows in (("AB", 7), ("BA", 9)):
+            B = rng.standard_normal((rows, 3))
+            got = orc.spmm_view(L, direction, B, np.ones(9), np.ones(7))
+            assert np.array_equal(got, orc.spmm(L, direction, B)), (name, direction)
