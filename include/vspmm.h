@@ -251,6 +251,37 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
 vspmm_status vspmm_spmm_noalloc(vspmm_matrix h, const void *B, void *out, int64_t width,
                                 vspmm_direction dir, vspmm_mode mode, hipStream_t stream);
 
+/* Normalized views. On the vsparse page a view of the counts transforms each
+ * stored value on the fly (introduction), carries O(n_rows + n_cols)
+ * statistics beside the four arrays and never an expanded copy (section "The
+ * layout stays compressed"), and a transform the device code does not know
+ * fails loudly (section "Testing"). The page does not give its transforms;
+ * this library offers the identity and one closed form:
+ *   VSPMM_VIEW_SCALE: stored entry (r, c, v) acts as v * row_stat[r] * col_stat[c].
+ * Every product on the handle (vspmm_spmm, _spmm_ex, _spmm_noalloc,
+ * _schedule_spmm) then computes diag(out_stat) A diag(in_stat) B: B's rows
+ * are scaled by their axis's statistic into a buffer the handle owns, the
+ * walk runs over that, and out's rows are scaled by the other axis's
+ * statistic; in exact arithmetic that is the product with every entry
+ * transformed. */
+typedef enum { VSPMM_VIEW_IDENTITY = 0, VSPMM_VIEW_SCALE = 1 } vspmm_view;
+
+/* Sets the handle's view. row_stat: device [n_rows], col_stat: device
+ * [n_cols], of the dense operands' type (float for VSPMM_F32 and VCS, double
+ * otherwise), borrowed; ignored for VSPMM_VIEW_IDENTITY (which clears a
+ * view). max_width: the widest product the view will serve; the handle
+ * allocates max(n_rows, n_cols) x max_width elements for the scaled input,
+ * and products wider than that return VSPMM_ERR_DIM. Products through one
+ * handle with a SCALE view share that buffer: they must not overlap in time;
+ * call this only while none is in flight. Errors: _NULL, _ENUM (unknown
+ * view), _DIM, _HIP. */
+vspmm_status vspmm_set_view(vspmm_matrix h, int32_t view, const void *row_stat,
+                            const void *col_stat, int64_t max_width);
+
+/* The name of a view code ("identity", "scale"), or NULL for a code this
+ * library does not implement (bindings check their list against it). */
+const char *vspmm_view_name(int32_t view);
+
 /* Bytes of workspace for a product of the given width: in deterministic
  * mode, what the tiled schedule needs when it applies (see vspmm_spmm_ex),
  * else the same as vspmm_workspace_size. bytes: host. Errors: as

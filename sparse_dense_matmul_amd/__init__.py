@@ -27,6 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libvspmm.so")
 LAYOUTS = {"csr": 0, "vcsr": 1, "vcsc": 2}
 DIRECTIONS = {"AB": 0, "BA": 1}
 MODES = {"atomic": 0, "deterministic": 1}
+# normalized views the binding offers; the library must implement each one
+VIEWS = {"identity": 0, "scale": 1}
 SPLIT_WIDTH, SPLIT_MATRIX, VALIDATE = 1, 2, 4
 
 _vp, _i64, _i32, _u32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
@@ -61,6 +63,8 @@ EXPORTS = {
     "vspmm_plan_info": ([_vp, _i64, ctypes.c_int, ctypes.c_int, _P(_i32), _P(_i32), _P(_i32),
                          _P(_i32), _P(_i32), _P(_i32), _P(_i32)], ctypes.c_int),
     "vspmm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "vspmm_set_view": ([_vp, _i32, _vp, _vp, _i64], ctypes.c_int),
+    "vspmm_view_name": ([_i32], ctypes.c_char_p),
 }
 
 
@@ -76,6 +80,13 @@ def _load():
                               "`python -m sparse_dense_matmul_amd.build`") from e
         fn.argtypes = argtypes
         fn.restype = restype
+    # every view the binding offers must be one the library implements:
+    # otherwise fail here, loudly, instead of computing another product
+    for name, code in VIEWS.items():
+        got = handle.vspmm_view_name(code)
+        if got is None or got.decode() != name:
+            raise ImportError(f"{LIB_PATH} does not implement the normalized view '{name}' "
+                              f"(code {code})")
     return handle
 
 
@@ -242,6 +253,29 @@ class SparseMatrix:
         _check(st, "vspmm_schedule_create")
         return Schedule(h, self, direction, int(width))
 
+    def normalized(self, view: str, row_stat=None, col_stat=None,
+                   max_width: int = 64) -> "SparseMatrix":
+        """A view of the same arrays whose stored entries (r, c, v) act as
+        g(v, r, c): ``"identity"`` (v) or ``"scale"`` (v * row_stat[r] *
+        col_stat[c], statistics of the dense operands' type on the device).
+        Products up to ``max_width`` columns (see ``vspmm_set_view``)."""
+        if view not in VIEWS:
+            raise ValueError(f"unknown normalized view {view!r}; known: {sorted(VIEWS)}")
+        m, n = self.shape
+        stats = ()
+        if view != "identity":
+            row_stat = _dev_tensor(row_stat, self.dtype, self.device, "row_stat")
+            col_stat = _dev_tensor(col_stat, self.dtype, self.device, "col_stat")
+            if row_stat.numel() != m or col_stat.numel() != n:
+                raise ValueError(f"statistics must have {m} and {n} entries")
+            stats = (row_stat, col_stat)
+        other = self._clone_handle()
+        st = lib.vspmm_set_view(other._h, VIEWS[view], _ptr(stats[0]) if stats else None,
+                                _ptr(stats[1]) if stats else None, int(max_width))
+        _check(st, "vspmm_set_view")
+        other._view = (view, stats, int(max_width))
+        return other
+
     def validate(self) -> bool:
         st = lib.vspmm_validate(self._h, _stream(self.device))
         if st == 4:
@@ -351,7 +385,16 @@ class VcsMatrix(SparseMatrix):
     def T(self) -> "VcsMatrix":
         """The transpose: the same arrays read as the other layout."""
         other = "vcsc" if self.layout == "vcsr" else "vcsr"
-        return VcsMatrix.from_arrays(other, (self.shape[1], self.shape[0]), *self._arrays,
+        t = VcsMatrix.from_arrays(other, (self.shape[1], self.shape[0]), *self._arrays,
+                                  flags=self.flags & ~VALIDATE, force_group=self.force_group)
+        view = getattr(self, "_view", None)
+        if view is not None and view[0] != "identity":
+            # the transposed view: the statistics change axes
+            t = t.normalized(view[0], view[1][1], view[1][0], view[2])
+        return t
+
+    def _clone_handle(self) -> "VcsMatrix":
+        return VcsMatrix.from_arrays(self.layout, self.shape, *self._arrays,
                                      flags=self.flags & ~VALIDATE, force_group=self.force_group)
 
     def regroup(self, workspace: torch.Tensor | None = None) -> "VcsMatrix":
@@ -439,7 +482,15 @@ class CsrMatrix(SparseMatrix):
                                           _ptr(col), _ptr(val), code, flags, force_group,
                                           _stream(dev))
         _check(st, "vspmm_create_csr64" if ptr64 else "vspmm_create_csr")
-        return cls(h, (row_ptr, col, val), (m, n), "csr", dtype, dev, flags, force_group)
+        out = cls(h, (row_ptr, col, val), (m, n), "csr", dtype, dev, flags, force_group)
+        out._block_nnz = block_nnz
+        return out
+
+    def _clone_handle(self) -> "CsrMatrix":
+        return CsrMatrix.from_arrays(self.shape, *self._arrays, flags=self.flags & ~VALIDATE,
+                                     force_group=self.force_group, dtype=self.dtype,
+                                     ptr64=self.row_ptr.dtype == torch.int64,
+                                     block_nnz=getattr(self, "_block_nnz", 0))
 
     @property
     def row_ptr(self):

@@ -723,6 +723,27 @@ __global__ void __launch_bounds__(256) k_accumulate(T *__restrict__ out, const T
         out[i] += src[i];
 }
 
+// dst[r][c] = src[r][c] * stat[r] for an n_rows x w row-major block (dst may
+// be src): one thread per row chunk of 64 elements, so the row's factor is
+// read once.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_scale_rows(T *dst, const T *src, const T *__restrict__ stat, long long n_rows, int w) {
+    const long long chunks = (w + 63) / 64;
+    const long long n = n_rows * chunks;
+    const long long stride = (long long)gridDim.x * (blockDim.x >> 6);
+    const int lane = threadIdx.x & 63;
+    for (long long q = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); q < n;
+         q += stride) {
+        const long long r = q / chunks;
+        const int c = (int)(q - r * chunks) * 64 + lane;
+        if (c < w) {
+            const size_t e = (size_t)r * w + c;
+            dst[e] = src[e] * stat[r];
+        }
+    }
+}
+
 // Structure checks: flag bit 1 = pointer array does not start at 0, bit 2 =
 // decreasing, bit 4 = last pointer differs from count, bit 8 = index out of
 // range.

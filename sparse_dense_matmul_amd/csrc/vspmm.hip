@@ -55,6 +55,14 @@ struct vspmm_matrix_s {
     std::vector<vspmm_matrix_s *> blocks;
     std::vector<int64_t> block_row0;
     int32_t *block_ptr = nullptr;
+    // normalized view (VSPMM_VIEW_SCALE): entry (r, c, v) acts as
+    // v * row_stat[r] * col_stat[c]; statistics borrowed, in the dense
+    // operands' type; view_buf (owned) holds the scaled dense input of up to
+    // view_width columns
+    int view = VSPMM_VIEW_IDENTITY;
+    const void *row_stat = nullptr, *col_stat = nullptr;
+    void *view_buf = nullptr;
+    int64_t view_width = 0;
     int64_t n_major() const { return layout == VSPMM_VCSC ? n_cols : n_rows; }
     int64_t n_minor() const { return layout == VSPMM_VCSC ? n_rows : n_cols; }
     // bytes of a dense element (the type the sums run in) and of a stored value
@@ -1159,6 +1167,45 @@ vspmm_status run_blocked(const vspmm_matrix_s &h, const void *B, void *out, int 
     return hip_status();
 }
 
+// ------------------------------------------------------------ views
+
+void launch_scale_rows(void *dst, const void *src, const void *stat, int64_t n_rows, int w,
+                       size_t e, int n_cu, hipStream_t s) {
+    const int64_t chunks = (w + 63) / 64;
+    const int64_t waves = std::max<int64_t>(1, n_rows * chunks);
+    const unsigned g = (unsigned)std::min<int64_t>((waves + 3) / 4, int64_t(n_cu) * 16);
+    if (e == 8)
+        hipLaunchKernelGGL(k_scale_rows<double>, dim3(g), dim3(256), 0, s,
+                           static_cast<double *>(dst), static_cast<const double *>(src),
+                           static_cast<const double *>(stat), (long long)n_rows, w);
+    else
+        hipLaunchKernelGGL(k_scale_rows<float>, dim3(g), dim3(256), 0, s,
+                           static_cast<float *>(dst), static_cast<const float *>(src),
+                           static_cast<const float *>(stat), (long long)n_rows, w);
+}
+
+// A product under the handle's normalized view. With VSPMM_VIEW_SCALE the
+// product is diag(out_stat) A diag(in_stat) B: B's rows scaled by the
+// statistic of their axis into the handle's buffer, the walk (`walk`, any of
+// the product paths) over that, then out's rows scaled by the other axis's
+// statistic.
+template <typename F>
+vspmm_status with_view(const vspmm_matrix_s &h, const void *B, void *out, int64_t width, int dir,
+                       hipStream_t s, F walk) {
+    if (h.view == VSPMM_VIEW_IDENTITY) return walk(B);
+    if (width > h.view_width) return VSPMM_ERR_DIM;
+    const int64_t ni = n_in(h, dir), no = n_out(h, dir);
+    if (width == 0 || no == 0) return walk(B);
+    const DeviceInfo di = device_info(h.device);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    const void *in_stat = dir == VSPMM_AB ? h.col_stat : h.row_stat;
+    const void *out_stat = dir == VSPMM_AB ? h.row_stat : h.col_stat;
+    if (ni > 0) launch_scale_rows(h.view_buf, B, in_stat, ni, int(width), h.elt(), n_cu, s);
+    if (vspmm_status st = walk(ni > 0 ? h.view_buf : B)) return st;
+    launch_scale_rows(out, out, out_stat, no, int(width), h.elt(), n_cu, s);
+    return hip_status();
+}
+
 // ------------------------------------------------------------- schedules
 
 enum SchedKind { kSchedPlain = 0, kSchedOpposite = 1, kSchedTiled = 2, kSchedBlocked = 3 };
@@ -1402,6 +1449,7 @@ vspmm_status list_long_rows(vspmm_matrix_s *m, hipStream_t s) {
 }
 
 void free_handle(vspmm_matrix_s *m) {
+    if (m->view_buf) (void)hipFree(m->view_buf);
     if (m->seg_he) (void)hipFree(m->seg_he);
     if (m->seg_desc) (void)hipFree(m->seg_desc);
     if (m->long_rows) (void)hipFree(m->long_rows);
@@ -1660,7 +1708,10 @@ vspmm_status vspmm_destroy(vspmm_matrix h) {
 vspmm_status vspmm_spmm(vspmm_matrix h, const void *B, void *out, int64_t width,
                         vspmm_direction dir, hipStream_t stream) {
     if (vspmm_status st = check_handle(h)) return st;
-    return run_product(*h, B, out, width, dir, VSPMM_ATOMIC, nullptr, 0, stream);
+    if (vspmm_status st = check_product(*h, B, out, width, dir)) return st;
+    return with_view(*h, B, out, width, dir, stream, [&](const void *Bv) {
+        return run_product(*h, Bv, out, width, dir, VSPMM_ATOMIC, nullptr, 0, stream);
+    });
 }
 
 vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
@@ -1684,7 +1735,11 @@ vspmm_status vspmm_spmm_ex(vspmm_matrix h, const void *B, void *out, int64_t wid
                            vspmm_direction dir, vspmm_mode mode, void *ws, size_t ws_bytes,
                            hipStream_t stream) {
     if (vspmm_status st = check_handle(h)) return st;
-    return run_product(*h, B, out, width, dir, mode, ws, ws_bytes, stream);
+    if (vspmm_status st = check_product(*h, B, out, width, dir)) return st;
+    if (mode != VSPMM_ATOMIC && mode != VSPMM_DETERMINISTIC) return VSPMM_ERR_ENUM;
+    return with_view(*h, B, out, width, dir, stream, [&](const void *Bv) {
+        return run_product(*h, Bv, out, width, dir, mode, ws, ws_bytes, stream);
+    });
 }
 
 vspmm_status vspmm_schedule_create(vspmm_schedule *sc, vspmm_matrix h, vspmm_direction dir,
@@ -1720,7 +1775,8 @@ vspmm_status vspmm_schedule_spmm(vspmm_schedule sc, const void *B, void *out, in
     if (vspmm_status st = check_product(*sc->h, B, out, width, sc->dir)) return st;
     if (width != sc->width) return VSPMM_ERR_DIM;
     if (width == 0 || n_out(*sc->h, sc->dir) == 0) return VSPMM_OK;
-    return schedule_product(*sc, B, out, stream);
+    return with_view(*sc->h, B, out, width, sc->dir, stream,
+                     [&](const void *Bv) { return schedule_product(*sc, Bv, out, stream); });
 }
 
 vspmm_status vspmm_schedule_bytes(vspmm_schedule sc, size_t *bytes) {
@@ -1754,7 +1810,47 @@ vspmm_status vspmm_spmm_noalloc(vspmm_matrix h, const void *B, void *out, int64_
     if (base_need > kStaticScratchBytes) return VSPMM_ERR_WORKSPACE;
     void *ws = nullptr;
     if (vspmm_status st = static_scratch(h->device, &ws)) return st;
-    return run_product(*h, B, out, width, dir, mode, ws, kStaticScratchBytes, stream);
+    if (vspmm_status st = check_product(*h, B, out, width, dir)) return st;
+    return with_view(*h, B, out, width, dir, stream, [&](const void *Bv) {
+        return run_product(*h, Bv, out, width, dir, mode, ws, kStaticScratchBytes, stream);
+    });
+}
+
+const char *vspmm_view_name(int32_t view) {
+    switch (view) {
+        case VSPMM_VIEW_IDENTITY: return "identity";
+        case VSPMM_VIEW_SCALE: return "scale";
+    }
+    return nullptr;
+}
+
+vspmm_status vspmm_set_view(vspmm_matrix h, int32_t view, const void *row_stat,
+                            const void *col_stat, int64_t max_width) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (!vspmm_view_name(view)) return VSPMM_ERR_ENUM;
+    if (view == VSPMM_VIEW_SCALE) {
+        if ((h->n_rows > 0 && !row_stat) || (h->n_cols > 0 && !col_stat)) return VSPMM_ERR_NULL;
+        if (max_width < 1 || !fits_i32(max_width)) return VSPMM_ERR_DIM;
+        if (!aligned(row_stat, h->elt()) || !aligned(col_stat, h->elt())) return VSPMM_ERR_DIM;
+    }
+    void *buf = nullptr;
+    if (view == VSPMM_VIEW_SCALE) {
+        const size_t rows = size_t(std::max(h->n_rows, h->n_cols));
+        const size_t bytes = std::max<size_t>(rows * size_t(max_width) * h->elt(), 256);
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return VSPMM_ERR_HIP;
+        if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return VSPMM_ERR_HIP;
+        const hipError_t e = hipMalloc(&buf, bytes);
+        if (cur != h->device) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return VSPMM_ERR_HIP;
+    }
+    if (h->view_buf) (void)hipFree(h->view_buf);
+    h->view = view;
+    h->row_stat = view == VSPMM_VIEW_SCALE ? row_stat : nullptr;
+    h->col_stat = view == VSPMM_VIEW_SCALE ? col_stat : nullptr;
+    h->view_buf = buf;
+    h->view_width = view == VSPMM_VIEW_SCALE ? max_width : 0;
+    return VSPMM_OK;
 }
 
 vspmm_status vspmm_workspace_size_width(vspmm_matrix h, vspmm_direction dir, vspmm_mode mode,
