@@ -85,6 +85,9 @@ def load(path: str | None = None):
     lib.orc_expand_vcs.restype = None
     lib.orc_transpose_csr.argtypes = [i64, i64, i32p, i32p, vp, ctypes.c_int, i32p, i32p, vp]
     lib.orc_transpose_csr.restype = None
+    lib.orc_assemble_csr.argtypes = [ctypes.c_int, i64, i64, i64, i32p, i32p, i32p, dp, i64,
+                                     i32p, i32p, dp]
+    lib.orc_assemble_csr.restype = None
     lib.orc_regroup_vcs.argtypes = [i64, i64, i32p, vp, i32p, i32p, i32p, vp, i32p, i32p]
     lib.orc_regroup_vcs.restype = ctypes.c_int64
     if path == _LIB_PATH:
@@ -325,6 +328,43 @@ def transpose_csr(n_minor, ptr, idx, val, lib=None):
     lib.orc_transpose_csr(n_major, n_minor, _p(ptr), _p(idx), _p(val), val.itemsize,
                           _p(t_ptr), _p(t_idx), _p(t_val))
     return t_ptr, t_idx, t_val
+
+
+def transpose_csr_scaled(n_minor, ptr, idx, val, factor, lib=None):
+    """The exact transpose with each entry scaled by a factor of its own
+    (regridding page, section "API": the conservative transpose scales each
+    entry of the exact transpose by its own element's cells and shares .T's
+    indices): entry p becomes val[p] * factor[p], one rounding to val's type
+    (the product of two float32 numbers is exact in float64)."""
+    val = np.ascontiguousarray(val)
+    scaled = (val.astype(np.float64) * np.asarray(factor, dtype=np.float64)).astype(val.dtype)
+    return transpose_csr(n_minor, ptr, idx, scaled, lib=lib)
+
+
+ROLES = {"own": 0, "shared": 1, "summed": 2, "sum_of": 3}
+
+
+def assembled_shape(role, n_elem, n_out, n_in):
+    """(rows, columns) of the operator a role assembles."""
+    r = ROLES[role]
+    return (n_elem * n_out if r <= 1 else n_out, n_elem * n_in if r in (0, 2) else n_in)
+
+
+def assemble_csr(role, n_elem, n_out, n_in, elem_ptr, out_idx, in_idx, weight, lib=None):
+    """The regridder's operator from its elements' weights, by the two-pass
+    counting sort (see orc_assemble_csr): (row_ptr, col, val) with val in
+    weight's type (copied, not computed)."""
+    lib = lib or load()
+    elem_ptr, out_idx, in_idx = _i32(elem_ptr), _i32(out_idx), _i32(in_idx)
+    weight = np.ascontiguousarray(weight)
+    n_rows, _ = assembled_shape(role, n_elem, n_out, n_in)
+    nnz = out_idx.size
+    row_ptr = np.empty(n_rows + 1, dtype=np.int32)
+    col = np.empty(nnz, dtype=np.int32)
+    val = np.empty(nnz, dtype=np.float64)
+    lib.orc_assemble_csr(ROLES[role], n_elem, n_out, n_in, _p(elem_ptr), _p(out_idx),
+                         _p(in_idx), _p(_f64(weight)), n_rows, _p(row_ptr), _p(col), _p(val))
+    return row_ptr, col, val.astype(weight.dtype)
 
 
 def regroup_vcs(n_minor, major_ptr, values, value_ptr, indices, lib=None):

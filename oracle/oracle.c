@@ -14,7 +14,8 @@
  *    output's disjoint axis is the major axis or it is not).
  *  - regridding, "Regridder", section "How it is built" (a CSR operator built
  *    by a two-pass counting sort in which each row keeps its entries in
- *    source order; the exact transpose, section "API").
+ *    source order; the exact transpose, section "API"; the roles of the
+ *    orthogonal axis, the table in section "API").
  *
  * Semantics (COO sum): a stored entry (r, c, v) adds v to A[r][c]. Repeated
  * coordinates, empty groups and explicit zeros are all legal; repeats sum.
@@ -284,6 +285,46 @@ void orc_transpose_csr(int64_t n_major, int64_t n_minor, const int32_t *ptr,
             t_idx[at] = (int32_t)s;
             memcpy((char *)t_val + at * val_bytes, (const char *)val + p * val_bytes,
                    (size_t)val_bytes);
+        }
+    free(cursor);
+}
+
+/* ---------------------------------------------------------------- assembly */
+
+/* A regridder's operator assembled from its elements (regridding page,
+ * section "API", the roles of the orthogonal axis; section "How it is
+ * built", the two-pass counting sort). Element e holds entries [elem_ptr[e],
+ * elem_ptr[e + 1]) of (out_idx, in_idx, weight). The role places entry
+ * (e, o, i): role 0 (each element its own input and output) at row
+ * e * n_out + o, column e * n_in + i; role 1 (one shared input) at row
+ * e * n_out + o, column i; role 2 (outputs summed) at row o, column
+ * e * n_in + i; role 3 (the elements' sum) at row o, column i. Pass one
+ * counts each row's entries; pass two walks the elements in order and puts
+ * each entry at its row's cursor, so a row lists its entries by element and
+ * then in the order given. row_ptr has n_rows + 1 entries. */
+static int64_t assembled_row(int role, int64_t e, int64_t o, int64_t n_out) {
+    return role <= 1 ? e * n_out + o : o;
+}
+
+static int64_t assembled_col(int role, int64_t e, int64_t i, int64_t n_in) {
+    return (role == 0 || role == 2) ? e * n_in + i : i;
+}
+
+void orc_assemble_csr(int role, int64_t n_elem, int64_t n_out, int64_t n_in,
+                      const int32_t *elem_ptr, const int32_t *out_idx, const int32_t *in_idx,
+                      const double *weight, int64_t n_rows, int32_t *row_ptr, int32_t *col,
+                      double *val) {
+    int64_t *cursor = (int64_t *)calloc((size_t)n_rows + 1, sizeof(int64_t));
+    for (int64_t e = 0; e < n_elem; ++e)
+        for (int64_t p = elem_ptr[e]; p < elem_ptr[e + 1]; ++p)
+            cursor[assembled_row(role, e, out_idx[p], n_out) + 1] += 1;
+    for (int64_t r = 0; r < n_rows; ++r) cursor[r + 1] += cursor[r];
+    for (int64_t r = 0; r <= n_rows; ++r) row_ptr[r] = (int32_t)cursor[r];
+    for (int64_t e = 0; e < n_elem; ++e)
+        for (int64_t p = elem_ptr[e]; p < elem_ptr[e + 1]; ++p) {
+            int64_t at = cursor[assembled_row(role, e, out_idx[p], n_out)]++;
+            col[at] = (int32_t)assembled_col(role, e, in_idx[p], n_in);
+            val[at] = weight[p];
         }
     free(cursor);
 }

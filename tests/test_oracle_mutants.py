@@ -50,6 +50,19 @@ MUTANTS = [
     # the normalized view
     ("view_drops_col_stat", "double g = values[k] * row_stat[r] * col_stat[c];",
      "double g = values[k] * row_stat[r];"),
+    # the assembly of a regridder's operator
+    ("assembly_count_own_row", "cursor[assembled_row(role, e, out_idx[p], n_out) + 1] += 1;",
+     "cursor[assembled_row(role, e, out_idx[p], n_out)] += 1;"),
+    ("assembly_shared_column_per_element", "return (role == 0 || role == 2) ? e * n_in + i : i;",
+     "return (role == 0 || role == 1 || role == 2) ? e * n_in + i : i;"),
+    ("assembly_elements_reversed", "    for (int64_t e = 0; e < n_elem; ++e)\n"
+     "        for (int64_t p = elem_ptr[e]; p < elem_ptr[e + 1]; ++p) {\n"
+     "            int64_t at",
+     "    for (int64_t e = n_elem - 1; e >= 0; --e)\n"
+     "        for (int64_t p = elem_ptr[e]; p < elem_ptr[e + 1]; ++p) {\n"
+     "            int64_t at"),
+    ("assembly_summed_rows_per_element", "return role <= 1 ? e * n_out + o : o;",
+     "return role <= 2 ? e * n_out + o : o;"),
     ("view_dropped_last_entry", "for (int64_t p = value_ptr[k]; p < value_ptr[k + 1]; ++p) {\n"
      "                int64_t r = layout == 1 ? s : indices[p];\n"
      "                int64_t c = layout == 1 ? indices[p] : s;\n"
@@ -96,6 +109,12 @@ PY_MUTANTS = [
      "np.abs(_f64(A.val)),\n                    _f64(B)"),
     ("abs_scale_signed_values", "np.abs(_f64(A.values))", "_f64(A.values)"),
     ("abs_scale_signed_csr_values", "np.abs(_f64(A.val))", "_f64(A.val)"),
+    ("scaled_transpose_ignores_factor",
+     "scaled = (val.astype(np.float64) * np.asarray(factor, dtype=np.float64)).astype(val.dtype)",
+     "scaled = val"),
+    ("scaled_transpose_factor_reversed",
+     "scaled = (val.astype(np.float64) * np.asarray(factor, dtype=np.float64)).astype(val.dtype)",
+     "scaled = (val.astype(np.float64) * np.asarray(factor, dtype=np.float64)[::-1]).astype(val.dtype)"),
     ("abs_scale_view_signed_stats", "np.abs(_f64(row_stat)),\n                     np.abs(_f64(col_stat))",
      "_f64(row_stat),\n                     _f64(col_stat)"),
 ]

@@ -545,3 +545,107 @@ def test_view_unit_statistics_is_the_product(orc):
             B = rng.standard_normal((rows, 3))
             got = orc.spmm_view(L, direction, B, np.ones(9), np.ones(7))
             assert np.array_equal(got, orc.spmm(L, direction, B)), (name, direction)
+
+
+# ------------------------------------------------------------- assembly
+
+def _elements(rng, n_elem, n_out, n_in, max_nnz):
+    """Random elements with integer weights (repeated coordinates and empty
+    elements included) and each element's dense matrix."""
+    sizes = rng.integers(0, max_nnz + 1, n_elem)
+    sizes[rng.random(n_elem) < 0.2] = 0
+    elem_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    nnz = int(elem_ptr[-1])
+    out_idx = rng.integers(0, n_out, nnz).astype(np.int32)
+    in_idx = rng.integers(0, n_in, nnz).astype(np.int32)
+    weight = rng.integers(1, 10, nnz).astype(np.float64)
+    dense = np.zeros((n_elem, n_out, n_in))
+    for e in range(n_elem):
+        for p in range(elem_ptr[e], elem_ptr[e + 1]):
+            dense[e, out_idx[p], in_idx[p]] += weight[p]
+    return elem_ptr, out_idx, in_idx, weight, dense
+
+
+def _role_dense(role, dense):
+    """The operator each role of the regridding page's table describes,
+    written with dense blocks: own = block diagonal, shared = elements
+    stacked over one input, summed = elements side by side, sum_of = their
+    sum."""
+    import scipy.linalg
+    if role == "own":
+        return scipy.linalg.block_diag(*dense)
+    if role == "shared":
+        return np.vstack(list(dense))
+    if role == "summed":
+        return np.hstack(list(dense))
+    return dense.sum(axis=0)
+
+
+def _csr_dense(shape, row_ptr, col, val):
+    A = np.zeros(shape)
+    for r in range(shape[0]):
+        for p in range(row_ptr[r], row_ptr[r + 1]):
+            A[r, col[p]] += val[p]
+    return A
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("role", ["own", "shared", "summed", "sum_of"])
+def test_assembly_is_the_role_operator(orc, role, seed):
+    rng = np.random.default_rng(4000 + seed)
+    n_elem, n_out, n_in = (int(x) for x in rng.integers(1, 6, size=3))
+    ep, oi, ii, wt, dense = _elements(rng, n_elem, n_out, n_in, 7)
+    row_ptr, col, val = orc.assemble_csr(role, n_elem, n_out, n_in, ep, oi, ii, wt)
+    shape = orc.assembled_shape(role, n_elem, n_out, n_in)
+    assert shape == _role_dense(role, dense).shape
+    assert np.array_equal(_csr_dense(shape, row_ptr, col, val), _role_dense(role, dense))
+
+
+@pytest.mark.parametrize("role", ["own", "shared", "summed", "sum_of"])
+def test_assembly_rows_keep_element_order(orc, role):
+    """Weights that number the entries (their position in the element
+    lists): every row must list them in increasing order, so by element and
+    then as given; and the row counts are the rows' entry counts."""
+    rng = np.random.default_rng(77)
+    n_elem, n_out, n_in = 5, 4, 3
+    ep, oi, ii, _, _ = _elements(rng, n_elem, n_out, n_in, 9)
+    nnz = int(ep[-1])
+    tag = np.arange(nnz, dtype=np.float64)
+    row_ptr, col, val = orc.assemble_csr(role, n_elem, n_out, n_in, ep, oi, ii, tag)
+    for r in range(row_ptr.size - 1):
+        assert np.all(np.diff(val[row_ptr[r]:row_ptr[r + 1]]) > 0), r
+    elem = np.repeat(np.arange(n_elem), np.diff(ep))
+    rows = elem * n_out + oi if role in ("own", "shared") else oi
+    assert np.array_equal(np.diff(row_ptr), np.bincount(rows, minlength=row_ptr.size - 1))
+
+
+def test_scaled_transpose_hand_worked(orc):
+    """A = [[1, 2], [0, 3]] with entry factors 10, 100, 1000 (stored order):
+    the scaled transpose holds [[10, 0], [200, 3000]] with .T's indices."""
+    ptr, idx = np.array([0, 2, 3], np.int32), np.array([0, 1, 1], np.int32)
+    val = np.array([1.0, 2.0, 3.0], np.float32)
+    t = orc.transpose_csr_scaled(2, ptr, idx, val, np.array([10.0, 100.0, 1000.0], np.float32))
+    assert t[0].tolist() == [0, 1, 3] and t[1].tolist() == [0, 0, 1]
+    assert t[2].tolist() == [10.0, 200.0, 3000.0]
+    plain = orc.transpose_csr(2, ptr, idx, val)
+    assert np.array_equal(plain[0], t[0]) and np.array_equal(plain[1], t[1])
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_scaled_transpose_brute_force(orc, dtype):
+    """Against the dense transpose of the matrix whose entries are scaled
+    (numpy's .T); unit factors give the exact transpose bit for bit."""
+    rng = np.random.default_rng(5)
+    t = W.tiny_real(11, 7, 0.4, rng, dtype=dtype)
+    C = W.build_csr(t)
+    f = rng.uniform(0.5, 2.0, C.nnz).astype(dtype)
+    tp, ti, tv = orc.transpose_csr_scaled(7, C.row_ptr, C.col, C.val, f)
+    D = np.zeros(C.shape)
+    for r in range(C.shape[0]):
+        for p in range(C.row_ptr[r], C.row_ptr[r + 1]):
+            D[r, C.col[p]] += float(dtype(float(C.val[p]) * float(f[p])))
+    assert np.array_equal(_csr_dense((7, 11), tp, ti, tv.astype(np.float64)), D.T)
+    ones = orc.transpose_csr_scaled(7, C.row_ptr, C.col, C.val, np.ones(C.nnz, dtype))
+    plain = orc.transpose_csr(7, C.row_ptr, C.col, C.val)
+    for a, b in zip(ones, plain):
+        assert np.array_equal(a, b)
