@@ -364,6 +364,63 @@ vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_va
 /* Formats of an expanded matrix (one value per entry): the CSR of A (row
  * pointers over the rows, column indices) or its CSC (column pointers over
  * the columns, row indices). */
+/* The exact transpose with every entry scaled by a factor of its own: the
+ * shape of the regridding page's conservative transpose (section "API"),
+ * which scales each entry of the exact transpose by its own element's cells
+ * (not two diagonal scalings) and shares the indices of .T. The factors are
+ * the caller's (the cell volumes behind them need grids the pages do not
+ * give). factor: device [nnz] of the stored value type, one per stored entry
+ * in the handle's order; entry p's value in the transpose is val[p] *
+ * factor[p], rounded once. t_row_ptr and t_col equal vspmm_transpose_csr's.
+ * Other arguments and errors as vspmm_transpose_csr. */
+vspmm_status vspmm_transpose_csr_scaled(vspmm_matrix h, const void *factor, int32_t *t_row_ptr,
+                                        int32_t *t_col, void *t_val, void *ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
+/* Roles of a regridder's orthogonal axis (regridding page, section "API",
+ * the roles table), for an operator of n_elem elements, each a sparse
+ * matrix from n_in input cells to n_out output cells:
+ *   VSPMM_ROLE_OWN     (weights N, input N, output N): each element applies
+ *                      to its own input: rows e n_out + o, columns e n_in + i;
+ *   VSPMM_ROLE_SHARED  (N, 1, N): every element applies to the same input:
+ *                      rows e n_out + o, columns i;
+ *   VSPMM_ROLE_SUMMED  (N, N, 1): the elements' outputs are summed: rows o,
+ *                      columns e n_in + i;
+ *   VSPMM_ROLE_SUM_OF  (N, 1, 1): the sum of the elements applies: rows o,
+ *                      columns i.
+ * The table's batch axis (weights 1, input M, output M: the same matrix
+ * applied to every input) is the width of the dense operands. */
+typedef enum {
+    VSPMM_ROLE_OWN = 0,
+    VSPMM_ROLE_SHARED = 1,
+    VSPMM_ROLE_SUMMED = 2,
+    VSPMM_ROLE_SUM_OF = 3
+} vspmm_role;
+
+/* Assembles the elements' weights into one CSR operator (regridding page,
+ * section "How it is built": a two-pass counting sort in which every row
+ * keeps its entries in the order of the elements), so that one product
+ * applies them all. Element e's weights are entries [elem_ptr[e],
+ * elem_ptr[e + 1]) of (out_idx, in_idx, weight): device arrays, out_idx in
+ * [0, n_out), in_idx in [0, n_in), weight float (VSPMM_F32) or double
+ * (VSPMM_F64). Output (device): row_ptr [rows + 1], col [nnz], val [nnz] of
+ * the weight type, rows and columns as the role gives; a row lists its
+ * entries by element, then in the order given (repeated coordinates stay
+ * separate entries, which products add). Malformed element pointers or
+ * indices give an undefined operator (nothing is written out of range).
+ * ws: device, 256-byte aligned, vspmm_assemble_workspace_size bytes. Errors:
+ * _NULL, _ENUM, _DIM (rows + 1 or columns above int32), _WORKSPACE, _HIP. */
+vspmm_status vspmm_assemble_csr(int32_t role, int64_t n_elem, int64_t n_out, int64_t n_in,
+                                int64_t nnz, const int32_t *elem_ptr, const int32_t *out_idx,
+                                const int32_t *in_idx, const void *weight, vspmm_dtype dtype,
+                                int32_t *row_ptr, int32_t *col, void *val, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of vspmm_assemble_csr. bytes: host. Errors: _NULL, _ENUM,
+ * _DIM. */
+vspmm_status vspmm_assemble_workspace_size(int32_t role, int64_t n_elem, int64_t n_out,
+                                           int64_t n_in, int64_t nnz, size_t *bytes);
+
 typedef enum { VSPMM_FORMAT_CSR = 0, VSPMM_FORMAT_CSC = 1 } vspmm_format;
 
 /* A VCS handle expanded to one value per entry (vsparse page, section

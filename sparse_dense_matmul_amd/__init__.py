@@ -19,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["VcsMatrix", "CsrMatrix", "Schedule", "VspmmError", "lib", "LIB_PATH", "EXPORTS"]
+__all__ = ["VcsMatrix", "CsrMatrix", "Schedule", "VspmmError", "assemble_csr", "lib", "LIB_PATH",
+           "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvspmm.so")
@@ -27,6 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libvspmm.so")
 LAYOUTS = {"csr": 0, "vcsr": 1, "vcsc": 2}
 DIRECTIONS = {"AB": 0, "BA": 1}
 MODES = {"atomic": 0, "deterministic": 1}
+# roles of a regridder's orthogonal axis (see vspmm_assemble_csr)
+ROLES = {"own": 0, "shared": 1, "summed": 2, "sum_of": 3}
 # normalized views the binding offers; the library must implement each one
 VIEWS = {"identity": 0, "scale": 1}
 SPLIT_WIDTH, SPLIT_MATRIX, VALIDATE = 1, 2, 4
@@ -55,6 +58,10 @@ EXPORTS = {
     "vspmm_schedule_destroy": ([_vp], ctypes.c_int),
     "vspmm_validate": ([_vp, _vp], ctypes.c_int),
     "vspmm_transpose_csr": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_transpose_csr_scaled": ([_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_assemble_csr": ([_i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                            _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "vspmm_assemble_workspace_size": ([_i32, _i64, _i64, _i64, _i64, _P(_sz)], ctypes.c_int),
     "vspmm_regroup_vcs": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_expand_vcs": ([_vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "vspmm_footprint": ([_vp, _P(_sz), _P(_sz)], ctypes.c_int),
@@ -504,6 +511,27 @@ class CsrMatrix(SparseMatrix):
     def val(self):
         return self._arrays[2]
 
+    def transpose_scaled(self, factor, workspace: torch.Tensor | None = None) -> "CsrMatrix":
+        """The exact transpose with entry p's value multiplied by factor[p]
+        (one factor per stored entry, in stored order; the indices are the
+        exact transpose's), see ``vspmm_transpose_csr_scaled``."""
+        m, n = self.shape
+        nnz = self.col.numel()
+        dev = self.device
+        factor = _dev_tensor(factor, self.val.dtype, dev, "factor")
+        if factor.numel() != nnz:
+            raise ValueError(f"factor must have {nnz} entries")
+        t_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+        t_col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        t_val = torch.empty(max(nnz, 1), dtype=self.val.dtype, device=dev)
+        ws = workspace if workspace is not None else self.workspace("BA")
+        st = lib.vspmm_transpose_csr_scaled(self._h, _ptr(factor), _ptr(t_ptr), _ptr(t_col),
+                                            _ptr(t_val), _ptr(ws), ws.numel(), _stream(dev))
+        _check(st, "vspmm_transpose_csr_scaled")
+        return CsrMatrix.from_arrays((n, m), t_ptr, t_col[:nnz], t_val[:nnz],
+                                     flags=self.flags & ~VALIDATE, force_group=self.force_group,
+                                     dtype=self.dtype)
+
     def transpose(self, workspace: torch.Tensor | None = None) -> "CsrMatrix":
         """The exact transpose (each new row lists its entries by ascending
         source row), bit-identical to a sequential counting sort."""
@@ -520,3 +548,44 @@ class CsrMatrix(SparseMatrix):
         return CsrMatrix.from_arrays((n, m), t_ptr, t_col[:nnz], t_val[:nnz],
                                      flags=self.flags & ~VALIDATE, force_group=self.force_group,
                                      dtype=self.dtype)
+
+
+def assemble_csr(role: str, n_out: int, n_in: int, elem_ptr, out_idx, in_idx, weight,
+                 workspace: torch.Tensor | None = None, **kw) -> CsrMatrix:
+    """A regridder's operator from its elements' weights (``vspmm_assemble_csr``):
+    element e's entries are ``[elem_ptr[e], elem_ptr[e+1])`` of (out_idx,
+    in_idx, weight), device arrays; ``role`` is one of ``ROLES``. Returns the
+    assembled CSR (float32 or float64 like ``weight``); ``kw`` goes to
+    :meth:`CsrMatrix.from_arrays`."""
+    if role not in ROLES:
+        raise ValueError(f"unknown role {role!r}; known: {sorted(ROLES)}")
+    dev = torch.as_tensor(elem_ptr).device
+    elem_ptr = _dev_tensor(elem_ptr, torch.int32, dev, "elem_ptr")
+    out_idx = _dev_tensor(out_idx, torch.int32, dev, "out_idx")
+    in_idx = _dev_tensor(in_idx, torch.int32, dev, "in_idx")
+    weight = torch.as_tensor(weight)
+    if weight.dtype not in (torch.float32, torch.float64):
+        raise TypeError(f"weight must be float32 or float64, got {weight.dtype}")
+    weight = _dev_tensor(weight, weight.dtype, dev, "weight")
+    n_elem, nnz = elem_ptr.numel() - 1, out_idx.numel()
+    if in_idx.numel() != nnz or weight.numel() != nnz:
+        raise ValueError("out_idx, in_idx and weight must have the same length")
+    r = ROLES[role]
+    rows = n_elem * n_out if r <= 1 else n_out
+    cols = n_elem * n_in if r in (0, 2) else n_in
+    need = _sz(0)
+    _check(lib.vspmm_assemble_workspace_size(r, n_elem, n_out, n_in, nnz, ctypes.byref(need)),
+           "vspmm_assemble_workspace_size")
+    ws = workspace if workspace is not None else \
+        torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=dev)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    val = torch.empty(max(nnz, 1), dtype=weight.dtype, device=dev)
+    with torch.cuda.device(dev):
+        st = lib.vspmm_assemble_csr(r, n_elem, n_out, n_in, nnz, _ptr(elem_ptr), _ptr(out_idx),
+                                    _ptr(in_idx), _ptr(weight),
+                                    1 if weight.dtype == torch.float64 else 0, _ptr(row_ptr),
+                                    _ptr(col), _ptr(val), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(dev))
+    _check(st, "vspmm_assemble_csr")
+    return CsrMatrix.from_arrays((rows, cols), row_ptr, col[:nnz], val[:nnz], **kw)

@@ -457,15 +457,69 @@ k_gather_index(int nnz, const int *__restrict__ pay, const int *__restrict__ idx
 
 // ------------------------------------------------------------- transpose
 
+// The transpose's e-th entry is the source's entry pay[e]; with factor, its
+// value is scaled by that entry's own factor (one rounding, as a product).
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_transpose_emit(int nnz, const int *__restrict__ pay, const int *__restrict__ slice_of,
-                 const T *__restrict__ val, int *__restrict__ t_idx, T *__restrict__ t_val) {
+                 const T *__restrict__ val, const T *__restrict__ factor, int *__restrict__ t_idx,
+                 T *__restrict__ t_val) {
     const int stride = gridDim.x * blockDim.x;
     for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nnz; e += stride) {
         const int p = pay[e];
         t_idx[e] = slice_of[p];
-        t_val[e] = val[p];
+        t_val[e] = factor ? val[p] * factor[p] : val[p];
+    }
+}
+
+// ------------------------------------------------------------- assembly
+
+// The operator of a regridder's elements: element e's entries are
+// [elem_ptr[e], elem_ptr[e + 1]); the orthogonal axis's role places entry
+// (e, o, i) at row e * n_out + o (each element its own output: roles 0 and
+// 1) or o (outputs summed: 2 and 3), column e * n_in + i (each element its
+// own input: 0 and 2) or i (one shared input: 1 and 3).
+__device__ __forceinline__ int role_row(int role, int e, int o, int n_out) {
+    return role <= 1 ? e * n_out + o : o;
+}
+__device__ __forceinline__ int role_col(int role, int e, int i, int n_in) {
+    return (role == 0 || role == 2) ? e * n_in + i : i;
+}
+
+// elem_of[p] = the element holding entry p (pointers clamped to [0, nnz], so
+// a malformed list writes nothing out of range).
+__global__ void __launch_bounds__(256)
+k_elem_of(int n_elem, const int *__restrict__ elem_ptr, int nnz, int *__restrict__ elem_of) {
+    const int lane = threadIdx.x & 63;
+    const int waves = blockDim.x >> 6;
+    for (int e = blockIdx.x * waves + (threadIdx.x >> 6); e < n_elem; e += gridDim.x * waves) {
+        const int p0 = min(max(elem_ptr[e], 0), nnz), p1 = min(max(elem_ptr[e + 1], 0), nnz);
+        for (int p = p0 + lane; p < p1; p += 64) elem_of[p] = e;
+    }
+}
+
+// Row keys of the entries (the counting sort's keys), payload = position.
+__global__ void __launch_bounds__(256)
+k_role_keys(int nnz, const int *__restrict__ elem_of, const int *__restrict__ out_idx, int role,
+            int n_out, uint32_t *__restrict__ keys, int *__restrict__ pay) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < nnz; p += stride) {
+        keys[p] = (uint32_t)role_row(role, elem_of[p], out_idx[p], n_out);
+        pay[p] = p;
+    }
+}
+
+// The q-th entry of the operator is source entry pay[q]: its column and value.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_role_emit(int nnz, const int *__restrict__ pay, const int *__restrict__ elem_of,
+            const int *__restrict__ in_idx, const T *__restrict__ w, int role, int n_in,
+            int *__restrict__ col, T *__restrict__ val) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < nnz; q += stride) {
+        const int p = pay[q];
+        col[q] = role_col(role, elem_of[p], in_idx[p], n_in);
+        val[q] = w[p];
     }
 }
 

@@ -613,9 +613,11 @@ void bin_starts(const uint32_t *keys, int64_t nnz, int64_t n_bins, int32_t *tptr
                        keys, int(n_bins), tptr);
 }
 
-// The exact CSR transpose into (t_ptr, t_idx, t_val).
+// The exact CSR transpose into (t_ptr, t_idx, t_val); with factor (one per
+// stored entry, in the handle's order), each value scaled by its own factor.
 void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_ptr,
-                     int32_t *t_idx, void *t_val, int n_cu, hipStream_t s) {
+                     int32_t *t_idx, void *t_val, int n_cu, hipStream_t s,
+                     const void *factor = nullptr) {
     if (h.nnz <= 0) {
         bin_starts(nullptr, 0, h.n_minor(), t_ptr, n_cu, s);
         return;
@@ -629,10 +631,12 @@ void build_transpose(const vspmm_matrix_s &h, const OppositeWs &w, int32_t *t_pt
     bin_starts(ka, h.nnz, h.n_minor(), t_ptr, n_cu, s);
     if (h.val_elt() == 8)
         hipLaunchKernelGGL(k_transpose_emit<double>, dim3(grid), dim3(256), 0, s, int(h.nnz), pa,
-                           w.slice_of, (const double *)h.vals, t_idx, (double *)t_val);
+                           w.slice_of, (const double *)h.vals, (const double *)factor, t_idx,
+                           (double *)t_val);
     else
         hipLaunchKernelGGL(k_transpose_emit<float>, dim3(grid), dim3(256), 0, s, int(h.nnz), pa,
-                           w.slice_of, (const float *)h.vals, t_idx, (float *)t_val);
+                           w.slice_of, (const float *)h.vals, (const float *)factor, t_idx,
+                           (float *)t_val);
 }
 
 // A VCS expanded to one value per entry (vsparse page, section "Benchmarks":
@@ -1507,6 +1511,40 @@ vspmm_status finish_create(vspmm_matrix_s *m, vspmm_matrix *h, hipStream_t s) {
     return VSPMM_OK;
 }
 
+// Workspace of vspmm_assemble_csr: the element of each entry, the sort's key
+// and payload pairs, its histograms and scan sums.
+struct AssembleWs {
+    int32_t *elem_of = nullptr;
+    uint32_t *keys_a = nullptr, *keys_b = nullptr;
+    int32_t *pay_a = nullptr, *pay_b = nullptr;
+    int32_t *hist = nullptr, *bsums = nullptr;
+    size_t bytes = 0;
+};
+
+AssembleWs carve_assemble(int64_t nnz, int64_t n_rows, void *base) {
+    AssembleWs w;
+    Bump b{static_cast<char *>(base)};
+    const size_t n = size_t(std::max<int64_t>(nnz, 0));
+    w.elem_of = b.take<int32_t>(n);
+    w.keys_a = b.take<uint32_t>(n);
+    w.keys_b = b.take<uint32_t>(n);
+    w.pay_a = b.take<int32_t>(n);
+    w.pay_b = b.take<int32_t>(n);
+    const size_t nblocks = (n + kSortTile - 1) / kSortTile;
+    w.hist = b.take<int32_t>(256 * std::max<size_t>(nblocks, 1));
+    const size_t scan_len = std::max({n, size_t(n_rows) + 1, 256 * std::max<size_t>(nblocks, 1)});
+    w.bsums = b.take<int32_t>((scan_len + kScanTile - 1) / kScanTile + 1);
+    w.bytes = align256(b.off);
+    return w;
+}
+
+// Rows and columns of an assembled operator (see vspmm_assemble_csr).
+void role_dims(int role, int64_t n_elem, int64_t n_out, int64_t n_in, int64_t *rows,
+               int64_t *cols) {
+    *rows = role <= 1 ? n_elem * n_out : n_out;
+    *cols = (role == 0 || role == 2) ? n_elem * n_in : n_in;
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -1918,6 +1956,83 @@ vspmm_status vspmm_transpose_csr(vspmm_matrix h, int32_t *t_row_ptr, int32_t *t_
                     stream);
     return hip_status();
 }
+
+vspmm_status vspmm_transpose_csr_scaled(vspmm_matrix h, const void *factor, int32_t *t_row_ptr,
+                                        int32_t *t_col, void *t_val, void *ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+    if (vspmm_status st = check_handle(h)) return st;
+    if (h->layout != VSPMM_CSR) return VSPMM_ERR_ENUM;
+    if (h->ptr64) return VSPMM_ERR_UNSUPPORTED;
+    if (!t_row_ptr || (h->nnz > 0 && (!t_col || !t_val || !factor))) return VSPMM_ERR_NULL;
+    if (h->nnz > 0 && !aligned(factor, h->val_elt())) return VSPMM_ERR_DIM;
+    const OppositeWs need = carve_opposite(*h, nullptr);
+    if (!ws || ws_bytes < need.bytes || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+    const DeviceInfo di = device_info(h->device);
+    build_transpose(*h, carve_opposite(*h, ws), t_row_ptr, t_col, t_val, di.ok ? di.n_cu : 256,
+                    stream, factor);
+    return hip_status();
+}
+
+vspmm_status vspmm_assemble_workspace_size(int32_t role, int64_t n_elem, int64_t n_out,
+                                           int64_t n_in, int64_t nnz, size_t *bytes) {
+    if (!bytes) return VSPMM_ERR_NULL;
+    if (role < VSPMM_ROLE_OWN || role > VSPMM_ROLE_SUM_OF) return VSPMM_ERR_ENUM;
+    if (n_elem < 0 || n_out < 0 || n_in < 0 || !fits_i32(nnz)) return VSPMM_ERR_DIM;
+    int64_t rows, cols;
+    role_dims(role, n_elem, n_out, n_in, &rows, &cols);
+    if (!fits_i32(rows + 1) || !fits_i32(cols)) return VSPMM_ERR_DIM;
+    *bytes = carve_assemble(nnz, rows, nullptr).bytes;
+    return VSPMM_OK;
+}
+
+vspmm_status vspmm_assemble_csr(int32_t role, int64_t n_elem, int64_t n_out, int64_t n_in,
+                                int64_t nnz, const int32_t *elem_ptr, const int32_t *out_idx,
+                                const int32_t *in_idx, const void *weight, vspmm_dtype dtype,
+                                int32_t *row_ptr, int32_t *col, void *val, void *ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    size_t need = 0;
+    if (vspmm_status st = vspmm_assemble_workspace_size(role, n_elem, n_out, n_in, nnz, &need))
+        return st;
+    if (dtype != VSPMM_F32 && dtype != VSPMM_F64) return VSPMM_ERR_ENUM;
+    if (!fits_i32(n_elem) || !fits_i32(n_out) || !fits_i32(n_in)) return VSPMM_ERR_DIM;
+    if (!elem_ptr || !row_ptr) return VSPMM_ERR_NULL;
+    if (nnz > 0 && (!out_idx || !in_idx || !weight || !col || !val)) return VSPMM_ERR_NULL;
+    if (!ws || ws_bytes < need || !aligned(ws, 256)) return VSPMM_ERR_WORKSPACE;
+    int64_t rows, cols;
+    role_dims(role, n_elem, n_out, n_in, &rows, &cols);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return VSPMM_ERR_HIP;
+    const DeviceInfo di = device_info(dev);
+    const int n_cu = di.ok ? di.n_cu : 256;
+    const AssembleWs w = carve_assemble(nnz, rows, ws);
+    if (nnz == 0) {
+        bin_starts(nullptr, 0, rows, row_ptr, n_cu, stream);
+        return hip_status();
+    }
+    // the counting sort by operator row: stable, so a row keeps its entries
+    // in element order and, within an element, in the order given
+    const int ge = int(std::max<int64_t>(1, std::min<int64_t>((n_elem + 3) / 4, n_cu * 16)));
+    if (n_elem > 0)
+        hipLaunchKernelGGL(k_elem_of, dim3(ge), dim3(256), 0, stream, int(n_elem), elem_ptr,
+                           int(nnz), w.elem_of);
+    const int grid = grid_for(nnz, n_cu);
+    uint32_t *ka = w.keys_a, *kb = w.keys_b;
+    int32_t *pa = w.pay_a, *pb = w.pay_b;
+    hipLaunchKernelGGL(k_role_keys, dim3(grid), dim3(256), 0, stream, int(nnz), w.elem_of,
+                       out_idx, int(role), int(n_out), ka, pa);
+    radix_sort(&ka, &pa, &kb, &pb, nnz, key_bits(rows), w.hist, w.bsums, stream);
+    bin_starts(ka, nnz, rows, row_ptr, n_cu, stream);
+    if (dtype == VSPMM_F64)
+        hipLaunchKernelGGL(k_role_emit<double>, dim3(grid), dim3(256), 0, stream, int(nnz), pa,
+                           w.elem_of, in_idx, static_cast<const double *>(weight), int(role),
+                           int(n_in), col, static_cast<double *>(val));
+    else
+        hipLaunchKernelGGL(k_role_emit<float>, dim3(grid), dim3(256), 0, stream, int(nnz), pa,
+                           w.elem_of, in_idx, static_cast<const float *>(weight), int(role),
+                           int(n_in), col, static_cast<float *>(val));
+    return hip_status();
+}
+
 
 vspmm_status vspmm_regroup_vcs(vspmm_matrix h, int32_t *t_major_ptr, float *t_values,
                                int32_t *t_value_ptr, int32_t *t_indices, int32_t *t_n_groups,
