@@ -457,6 +457,136 @@ def expansions(layouts, dev, steps, copies=8):
                         "caching allocator (no device work), workspace given", "products": out}
 
 
+def time_launches(run, steps, stream):
+    """Average microseconds of run() over `steps` back-to-back launches
+    between two events (after one untimed call)."""
+    import torch
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for k in range(steps):
+        run(k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / steps
+
+
+def csr_small_products(dev, steps, copies=16):
+    """The 2,000 x 500 CSR (Poisson(10) entries per row, U(0,1) values,
+    float32): A @ B and B @ A at width 8, and SpMV (width 1) both ways; B @ A
+    atomic and deterministic (through a schedule). Cold copies rotated.
+    Algorithmic bytes: 4(m+1) + 8 nnz + 4 w (n_in + n_out)."""
+    import torch
+
+    import sparse_dense_matmul_amd as sdm
+    import workloads as W
+
+    _, C = W.config1()
+    m, n = C.shape
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    hs = [sdm.CsrMatrix.from_arrays(C.shape, up(C.row_ptr), up(C.col), up(C.val))
+          for _ in range(copies)]
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for w in (1, 8):
+        for direction in ("AB", "BA"):
+            n_in, n_out = (n, m) if direction == "AB" else (m, n)
+            rng = np.random.default_rng(w)
+            Bs = [up(rng.standard_normal((n_in, w)).astype(np.float32)) for _ in range(copies)]
+            Os = [torch.empty((n_out, w), device=dev) for _ in range(copies)]
+            for mode in (["atomic"] if direction == "AB" else ["atomic", "deterministic"]):
+                if mode == "deterministic":
+                    scs = [h.schedule(direction, w) for h in hs]
+                    run = lambda k=0: scs[k % copies].spmm(Bs[k % copies], out=Os[k % copies])
+                else:
+                    run = lambda k=0: hs[k % copies].spmm(Bs[k % copies], direction,
+                                                          out=Os[k % copies])
+                us = time_launches(run, steps, stream)
+                nb = 4 * (m + 1) + 8 * C.nnz + 4 * w * (n_in + n_out)
+                key = f"w={w} {'A@B' if direction == 'AB' else 'B@A'}" + \
+                      ("" if direction == "AB" else f" {mode}")
+                out[key] = {"us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                            "kernel": hs[0].plan_info(w, direction, mode)["kernel_name"]}
+    return {"workload": f"CSR {m} x {n}, {C.nnz} entries (Poisson(10) per row), float32; "
+                        "launch-bound at this size (the matrix is 0.2 MB)", "products": out}
+
+
+def large_vcs_products(dev, steps, widths=(8, 32)):
+    """The 1,000,000 x 20,000 count matrix (~200M entries, values up to 255):
+    the VCSR from the generator, the VCSC regrouped on the device by the
+    library; widths 8 and 32, the four directions each the headline's way
+    (deterministic through a schedule where the direction has one, else the
+    plain walk) plus atomic mode for the misaligned two. One copy: the matrix
+    (0.9 GB) is several times the 256 MB Infinity Cache. Device footprint
+    against the expanded CSR, and each schedule's resident bytes."""
+    import torch
+
+    import sparse_dense_matmul_amd as sdm
+    import workloads as W
+
+    workers = max(1, min(16, cpu_threads()))
+    t0 = time.perf_counter()
+    L = W.config5_vcsr(workers=workers)
+    log(f"1M x 20k VCSR generated in {time.perf_counter() - t0:.1f} s ({L.nnz} entries)")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    A = {"vcsr": sdm.VcsMatrix.from_arrays("vcsr", L.shape, up(L.major_ptr), up(L.values),
+                                           up(L.value_ptr), up(L.indices))}
+    A["vcsc"] = A["vcsr"].regroup()
+    torch.cuda.synchronize()
+    m, n = L.shape
+    nbytes = {lay: a.footprint()[0] for lay, a in A.items()}
+    stream = torch.cuda.current_stream(dev)
+    res = {"footprint_bytes": nbytes, "expanded_csr_bytes": A["vcsr"].footprint()[1],
+           "footprint_ratio": {lay: round(b / A["vcsr"].footprint()[1], 3)
+                               for lay, b in nbytes.items()}}
+    for w in widths:
+        rng = np.random.default_rng(w)
+        B = {"AB": up(W.dense_normal(rng, n, w)), "BA": up(W.dense_normal(rng, m, w))}
+        per, tot_us, tot_b = {}, 0.0, 0
+        for name, lay, direction, walk in DIRECTIONS:
+            h = A[lay]
+            o = torch.empty((m if direction == "AB" else n, w), device=dev)
+            has_sc = h.workspace_size(direction, "deterministic", w) > 0
+            entry = {}
+            if has_sc:
+                t0 = time.perf_counter()
+                sc = h.schedule(direction, w)
+                entry["schedule_build_ms"] = round(1e3 * (time.perf_counter() - t0), 1)
+                entry["schedule_bytes"] = sc.nbytes
+                run = lambda k=0: sc.spmm(B[direction], out=o)
+            else:
+                sc = None
+                run = lambda k=0: h.spmm(B[direction], direction, out=o)
+            us = time_launches(run, steps, stream)
+            other = "vcsc" if lay == "vcsr" else "vcsr"
+            walked = nbytes[lay] if walk == "aligned" else nbytes[other]
+            nb = walked + dense_bytes(L.shape, direction, w)
+            info = h.plan_info(w, direction, "deterministic" if has_sc else "atomic")
+            entry.update(us=round(us, 1), GBps=round(nb / (us * 1e-6) / 1e9, 1),
+                         frac=round(nb / (us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+                         kernel=info["kernel_name"] +
+                         (f" (tiled, {info['tiles']} tiles) + k_tile_sum" if info["tiles"] else ""))
+            if walk == "scatter":
+                ua = time_launches(lambda k=0: h.spmm(B[direction], direction, out=o), steps,
+                                   stream)
+                ba = nbytes[lay] + dense_bytes(L.shape, direction, w)
+                entry["atomic"] = {"us": round(ua, 1), "GBps": round(ba / (ua * 1e-6) / 1e9, 1)}
+            per[name] = entry
+            tot_us += us
+            tot_b += nb
+            del sc, o
+            torch.cuda.empty_cache()
+        res[f"w={w}"] = {"GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+                         "frac": round(tot_b / (tot_us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+                         "directions": per}
+        del B
+    del A
+    torch.cuda.empty_cache()
+    return {"workload": f"VCS count matrix {m} x {n}, {L.nnz} entries, {L.n_groups} groups "
+                        f"(VCSR), cold HBM", **res}
+
+
 def other_widths(layouts, dev, widths, steps, copies=8):
     """The same four directions at other widths of the pages' workload (by
     default 1, 8, 32 and 64), beside the headline (not in it): each direction the way the
@@ -535,6 +665,9 @@ def main():
                     help="skip the timings of the CSR past 2^31 entries")
     ap.add_argument("--other-widths", default="1,8,32,64",
                     help="widths also timed beside the headline (comma list, empty for none)")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the 1M x 20k matrix (widths 8 and 32, four directions)")
+    ap.add_argument("--no-csr-small", action="store_true", help="skip the 2,000 x 500 CSR")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the secondary ceilings (LDS/L2 gathers, atomics, launches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -747,7 +880,7 @@ def main():
                      "algorithmic_bytes": per_dir[dom]["min_bytes"],
                      "launch_us": per_dir[dom]["us"],
                      # what bounds the walk below the HBM roofline (SQ counters)
-                     "secondary": ceiling_record("k_vcs_rows")},
+                     "secondary": ceiling_record(per_dir[dom]["kernel"].split()[0])},
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
@@ -758,6 +891,12 @@ def main():
         log("timing the other widths (reported beside the headline)")
         result["other_widths"] = other_widths(
             layouts, dev, [int(x) for x in args.other_widths.split(",")], args.steps)
+    if not args.no_csr_small:
+        log("timing the 2,000 x 500 CSR (reported beside the headline)")
+        result["csr_small"] = csr_small_products(dev, args.steps)
+    if not args.no_large:
+        log("timing the 1M x 20k matrix (reported beside the headline)")
+        result["large"] = large_vcs_products(dev, max(3, min(args.steps, 10)))
     if not args.no_csr:
         log("timing the CSR operator (reported beside the headline)")
         result["csr"] = csr_products(dev, args.steps)

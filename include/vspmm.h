@@ -219,7 +219,9 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * 2 MB, a multiple of 8 of them, each fitting one XCD's L2: the blocks of a
  * tile, all on one XCD and as many as the XCD holds at once, gather it from
  * global memory. A smaller B with rows of up to 64 bytes is cut into tiles
- * that fit in LDS, and each block stages its tile there; where the fewest such
+ * that fit in LDS, and each block stages its tile there, as long as the
+ * partial rows the tiles write and read back stay within half the matrix's
+ * own bytes (otherwise the untiled walk gathers B from L2); where the fewest such
  * tiles would leave (tile, output row) parts of 1,024 entries or more on
  * average, the tile count rises to a multiple of 8 until the mean is at most
  * 512. The
@@ -460,7 +462,8 @@ typedef enum {
     VSPMM_KERNEL_PLAIN = 0,   /* slices side by side, one lane group each */
     VSPMM_KERNEL_SHORT = 1,   /* a wave walks a block of short slices in register rounds */
     VSPMM_KERNEL_LONG = 2,    /* a block of waves walks one long slice */
-    VSPMM_KERNEL_SCATTER = 3  /* misaligned walk with float atomics */
+    VSPMM_KERNEL_SCATTER = 3, /* misaligned walk with float atomics */
+    VSPMM_KERNEL_SEG = 4      /* VCS: each wave walks a planned run of entries across slices */
 } vspmm_kernel;
 
 /* The lane split a product would use (host outputs, any may be NULL):

@@ -308,6 +308,7 @@ class SparseMatrix:
             {"vcsr": "vcsc", "vcsc": "vcsr", "csr": "csr"}[self.layout]
         vcs = walked != "csr"
         info["kernel_name"] = {0: "k_aligned", 1: "k_vcs_rows" if vcs else "k_short",
+                               4: "k_vcs_seg",
                                2: "k_vcs_long" if vcs else "k_long",
                                3: "k_scatter"}[info["kernel"]]
         return info

@@ -834,6 +834,15 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
         if (tr < 64) return tp;
     }
     tiles = (ni + tr - 1) / tr;  // (rounding tr may drop one)
+    // B fits an XCD's L2 here, where the untiled walk gathers it at a fair
+    // rate: tiles pay only while their partial rows (written, then read back
+    // to be added) stay within half the matrix's own bytes (1M x 20k at width
+    // 8: 8 tiles of 1M partial rows, 512 MB, against 0.9 GB, measured 1.24
+    // ms tiled and 0.98 ms untiled)
+    const size_t partial_traffic = 2 * size_t(tiles) * size_t(no) * row_bytes;
+    const size_t matrix_bytes = 4 * size_t(h.n_major() + 1) + 8 * size_t(h.n_groups) + 4 +
+                                4 * size_t(h.nnz);
+    if (2 * partial_traffic > matrix_bytes) return tp;
     const int64_t nv = tiles * no;
     if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
     const int64_t mean = h.nnz / nv;
@@ -2122,11 +2131,15 @@ vspmm_status vspmm_plan_info(vspmm_matrix h, int64_t width, vspmm_direction dir,
     if (vec) *vec = pl.vec;
     if (slices_per_wave) *slices_per_wave = pl.R;
     if (lds_staged) *lds_staged = pl.lds ? 1 : 0;
+    // the short VCS walk runs as k_vcs_seg at up to 4 width lanes per entry
+    // (every VCS walk carries its per-wave plan)
+    const bool seg = vcs && !scatter && pl.kind == kShort && pl.sp.log_ww <= 2;
     if (kernel)
         *kernel = scatter ? VSPMM_KERNEL_SCATTER
-                          : pl.kind == kLong ? VSPMM_KERNEL_LONG
-                                             : pl.kind == kShort ? VSPMM_KERNEL_SHORT
-                                                                 : VSPMM_KERNEL_PLAIN;
+                  : seg   ? VSPMM_KERNEL_SEG
+                  : pl.kind == kLong ? VSPMM_KERNEL_LONG
+                  : pl.kind == kShort ? VSPMM_KERNEL_SHORT
+                                      : VSPMM_KERNEL_PLAIN;
     return VSPMM_OK;
 }
 

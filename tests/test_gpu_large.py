@@ -118,7 +118,7 @@ def test_large_tiled(orc, large, layout, width):
     A = large[layout]
     want = large["want"]["BA"]
     info = A.plan_info(width, "BA", "deterministic")
-    assert info["tiles"] > 8 and info["kernel_name"] == "k_vcs_rows"
+    assert info["tiles"] > 8 and info["kernel_name"] == ("k_vcs_seg" if width <= 16 else "k_vcs_rows")
     B = W.dense_normal(np.random.default_rng(81), L.shape[0], width)
     Bd = to_dev(B, dev)
     t0 = time.time()

@@ -57,7 +57,7 @@ def test_tiled_parity(orc, count60k, layout, direction, width):
     L = count60k[layout]
     A = vcs_handle(L, dev)
     info = A.plan_info(width, direction, "deterministic")
-    assert info["tiles"] > 1 and info["kernel_name"] == "k_vcs_rows" and info["lds_staged"] == 1
+    assert info["tiles"] > 1 and info["kernel_name"] == "k_vcs_seg" and info["lds_staged"] == 1
     B, out, ws = run_det(A, L, direction, width)
     check_close(orc, L, direction, B, out, where=f"tiled {layout} {direction} w={width}")
     again = A.spmm(to_dev(B, dev), direction, mode="deterministic", workspace=ws)
@@ -97,21 +97,24 @@ def test_width1_tiles_follow_slice_length(orc, count60k, layout, direction, widt
     L = count60k[layout]
     A = vcs_handle(L, dev)
     info = A.plan_info(width, direction, "deterministic")
-    assert info["tiles"] == 8 and info["kernel_name"] == "k_vcs_rows" and info["lds_staged"] == 1
+    assert info["tiles"] == 8 and info["kernel_name"] == "k_vcs_seg" and info["lds_staged"] == 1
     B, out, ws = run_det(A, L, direction, width)
     check_close(orc, L, direction, B, out, where=f"width 1 {layout} {direction}")
     again = A.spmm(to_dev(B, dev), direction, mode="deterministic", workspace=ws)
     assert torch.equal(again.view(torch.int32), out.view(torch.int32))
 
 
-@pytest.mark.parametrize("name,direction", [("vcsr", "BA"), ("vcsc", "BA"), ("vcsc_empty", "BA")])
-def test_tiled_ragged(orc, ragged, name, direction):
+@pytest.mark.parametrize("name,direction,width", [("vcsr", "BA", 16), ("vcsc", "BA", 8),
+                                                  ("vcsc_empty", "BA", 8)])
+def test_tiled_ragged(orc, ragged, name, direction, width):
+    """(The VCSC, with fewer groups than the VCSR, takes tiles at width 8; at
+    width 16 its tiles' partial rows would outweigh half the matrix.)"""
     dev = need_gpu()
     L = ragged[name]
     A = vcs_handle(L, dev)
-    assert A.plan_info(16, direction, "deterministic")["tiles"] > 1
+    assert A.plan_info(width, direction, "deterministic")["tiles"] > 1
     for integer in (False, True):
-        B, out, _ = run_det(A, L, direction, 16, seed=5, integer=integer)
+        B, out, _ = run_det(A, L, direction, width, seed=5, integer=integer)
         if integer:
             want = orc.spmm(L, direction, B)
             assert np.array_equal(out.cpu().numpy().astype(np.float64), want), name
@@ -120,10 +123,9 @@ def test_tiled_ragged(orc, ragged, name, direction):
 
 
 def test_workspace_shared_across_widths(orc, count60k):
-    """One workspace large enough for every width: the schedule is rebuilt when
-    the tile size changes and reused when it does not (widths 32 and 64 cut the
-    same 8 L2 tiles, so the second reuses the first's layout with its own
-    partial rows)."""
+    """One workspace large enough for every width, shared by products of
+    widths 16, 8, 32 and 64 in turn (each call builds its tiled copy again in
+    it): every width's result repeats bit for bit when it comes round again."""
     dev = need_gpu()
     L = count60k["vcsr"]
     A = vcs_handle(L, dev)
