@@ -314,6 +314,21 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             const int j = cur.i - row0;
             cur.e1 = cur.i < cur.s_end && j < 64 ? readlane(RE, j) : kFar;
         };
+        // closes slice cur.i and starts the next one with v * b (the sum's
+        // tree and the next slice's products are independent, so they overlap)
+        auto close_into = [&](const T (&b)[VEC], T v) {
+            T res[Sum::VO];
+            slot_sum<LOG_WW, VEC>(acc, res);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = fma_t(v, b[e], T(0));
+            if (Sum::writer(lane) && act) {
+                T *o = out + (size_t)cur.i * w + col + Sum::base(lane);
+                store_vec<T, Sum::VO>(o, res);
+            }
+            ++cur.i;
+            const int j = cur.i - row0;
+            cur.e1 = cur.i < cur.s_end && j < 64 ? readlane(RE, j) : kFar;
+        };
 
         // the end of slice cur.i + 1 (past every entry when it is not held)
         auto next_end = [&]() {
@@ -455,9 +470,10 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                             full(bv, vt);
                             close();
                         } else {
-                            if (slot < qb) full(bv, vt);
-                            close();
-                            if (slot >= qb) full(bv, vt);
+                            // (zero values instead of masked lanes: one
+                            // straight run of instructions)
+                            full(bv, slot < qb ? vt : T(0));
+                            close_into(bv, slot < qb ? T(0) : vt);
                         }
                     });
                     return;
@@ -474,9 +490,10 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                     const int stop = min(rend, s + G);
                     if (s >= stop) return;  // past the round's end
                     auto add = [&](int lo, int hi) {  // slots holding entries [lo, hi)
-                        if (hi > lo && slot >= lo - s && slot < hi - s) {
+                        if (hi > lo) {
+                            const T vm = slot >= lo - s && slot < hi - s ? vt : T(0);
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e) acc[e] = fma_t(vt, b[e], acc[e]);
+                            for (int e = 0; e < VEC; ++e) acc[e] = fma_t(vm, b[e], acc[e]);
                         }
                     };
                     int lo = s;
