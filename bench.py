@@ -125,6 +125,25 @@ def ceiling_record(kernel):
     return None
 
 
+def probe_record():
+    """The measured secondary ceilings (LDS and L2 row gathers, float atomics,
+    empty launches) from the probe record in profiles/, when the probe source
+    hashes to the value recorded; else None."""
+    h = hashlib.sha256(open(os.path.join(CSRC, "probe.hip"), "rb").read()).hexdigest()
+    pat = re.compile(r"^probe-ceilings:\s*(.*)$")
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(f):
+            m = pat.match(line.strip())
+            if not m:
+                continue
+            kv = dict(tok.split("=", 1) for tok in m.group(1).split())
+            if kv.get("source_sha256") == h:
+                out = {k: float(v) for k, v in kv.items() if k != "source_sha256"}
+                out["source"] = os.path.relpath(f, ROOT)
+                return out
+    return None
+
+
 def copy_calibration(mib):
     """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -842,6 +861,14 @@ def main():
     repeat_ok = bool(torch.equal(r1, r2) and torch.equal(r3, r4))
 
     traffic, traffic_src = traffic_record(per_dir[dom]["kernel"], dom, w)
+    # atomic mode against the measured float-atomic ceiling (a width-16 scatter's
+    # adds at the probe's rate; the probe adds 16 columns per entry)
+    probe = probe_record()
+    if probe and not args.no_atomic and w == 16:
+        rate = probe["atomic_w16_G_entries_per_s"] * 1e9
+        for name, e in per_dir.items():
+            if "atomic" in e:
+                e["atomic"]["frac_of_atomic_ceiling"] = round(t.nnz / rate * 1e6 / e["atomic"]["us"], 3)
     atomic_us = sum(e["atomic"]["us"] if "atomic" in e else e["us"] for e in per_dir.values())
     atomic_bytes = sum(e["atomic"]["min_bytes"] if "atomic" in e else e["min_bytes"]
                        for e in per_dir.values())
@@ -880,7 +907,10 @@ def main():
                      "algorithmic_bytes": per_dir[dom]["min_bytes"],
                      "launch_us": per_dir[dom]["us"],
                      # what bounds the walk below the HBM roofline (SQ counters)
-                     "secondary": ceiling_record(per_dir[dom]["kernel"].split()[0])},
+                     # what bounds the walk below the HBM roofline: its SQ counters,
+                     # and the measured ceilings of the other resources it uses
+                     "secondary": {"counters": ceiling_record(per_dir[dom]["kernel"].split()[0]),
+                                   "ceilings": probe}},
         "repeat_bitwise": repeat_ok,
         "wall_s_timed": round(wall, 3),
     }
