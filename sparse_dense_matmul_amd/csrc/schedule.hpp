@@ -705,10 +705,19 @@ k_slice_starts(int n_slices, int n_groups, const int *__restrict__ sptr,
 // The starts of the waves of a k_vcs_seg launch of `grid` blocks of `wpb`
 // waves over a VCS of n_slices slices (as `tiles` runs): block b owns the
 // slices seg_block_range gives it; its waves cut the block's entries into
-// wpb equal shares, and wave k takes the slices that start in its share (the
-// last wave also every empty slice at the end). One thread per wave. Reads
-// stay in bounds for any structure (group numbers clamped to [0, n_groups]);
-// a malformed one gets a meaningless plan, as its products are undefined.
+// wpb shares, and wave k takes the slices that start in its share (the last
+// wave also every empty slice at the end). One thread per wave. Reads stay in
+// bounds for any structure (group numbers clamped to [0, n_groups]); a
+// malformed one gets a meaningless plan, as its products are undefined.
+//
+// The shares are not equal. A block's waves go to the CU's four SIMDs in
+// turn, so wave k is the (4k / wpb)-th wave on its SIMD, and a SIMD issues
+// from its oldest wave first: with equal shares the first quarter of a
+// block's waves end well before the last, whose SIMDs then run with fewer
+// waves than they can overlap. Shares weighted 20 : 17 : 15 : 12 by that
+// place (with k_vcs_seg's issue priorities) let a block's waves end nearly
+// together. The weights change only which wave walks a slice, never the
+// slice's result.
 __global__ void __launch_bounds__(256)
 k_seg_plan(int n_slices, int n_groups, const int *__restrict__ sptr,
            const int *__restrict__ vptr, const int *__restrict__ he, int tiles, int grid, int wpb,
@@ -719,9 +728,15 @@ k_seg_plan(int n_slices, int n_groups, const int *__restrict__ sptr,
     int bb, be, tile;
     seg_block_range(b, grid, tiles, n_slices, bb, be, tile);
     const int EB = he[bb], EE = he[be];
+    // share weights by a wave's place on its SIMD
+    auto weight = [&](int k) { return k * 4 < wpb ? 20 : k * 2 < wpb ? 17 : k * 4 < 3 * wpb ? 15 : 12; };
+    long long w_all = 0;
+    for (int k = 0; k < wpb; ++k) w_all += weight(k);
     auto first_at = [&](int k) {  // the first slice in [bb, be] starting at or after cut k
         if (k >= wpb) return be;
-        const int cut = EB + (int)((long long)(EE - EB) * k / wpb);
+        long long w_before = 0;
+        for (int j = 0; j < k; ++j) w_before += weight(j);
+        const int cut = EB + (int)((long long)(EE - EB) * w_before / w_all);
         int lo = bb, hi = be;  // he[be] = EE >= cut
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;

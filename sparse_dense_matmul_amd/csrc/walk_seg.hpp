@@ -2,8 +2,9 @@
 // windows packed across slice boundaries.
 //
 // A block (one per CU when B is staged in LDS) owns a contiguous range of
-// slices; its 16 waves cut the range's entries into equal runs (cut at slice
-// starts), so every wave streams about the same number of entries. A run is
+// slices; its 16 waves cut the range's entries into runs (cut at slice
+// starts) sized by each wave's place on its SIMD (k_seg_plan), so the waves
+// of a SIMD end about together whatever the slice lengths. A run is
 // taken in rounds of at most 64 * kRowsNWR entries and 64 * kRowsGWR - 1
 // groups, whose index windows, group starts and group values are loaded one
 // round ahead. Inside a round:
@@ -24,10 +25,18 @@
 //    the end, sums the G slots (SlotSum: two permlane swap levels, then DPP),
 //    writes the row, and goes on with the lanes after it.
 //
+// A wave's issue priority falls as it gets through its run (3 in the first
+// quarter, 0 in the last): a SIMD otherwise issues from its oldest wave
+// first, its waves drift apart, and the last one ends alone. With the plan's
+// weighted shares a block's waves end nearly together.
+//
 // Each slot accumulates its entries of a slice in increasing position order
-// with fused multiply-adds and the tree is fixed; which slot takes an entry
-// depends only on the entry's position within its wave's run, and the runs
-// only on the matrix and the launch shape: results repeat bit for bit.
+// with fused multiply-adds. A slice starting at slot r gives its entry j to
+// slot (r + j) mod G, and the tree adds slots that differ in the highest slot
+// bit first: slot s and s + G/2 (mod G), then within each half likewise, so
+// every level pairs the same residue classes of j whatever r is. A slice's
+// result thus depends only on its entries in stored order, not on where runs,
+// rounds or windows start: results repeat bit for bit, whatever the plan.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -300,6 +309,21 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] = T(0);
 
+        // issue priority by progress through the run, checked every other
+        // window: one less each time the wave passes a quarter of its entries
+        const int quarter = (E_b - E_a) >> 2;
+        int p_next = E_a + quarter, p_lev = 3;
+        __builtin_amdgcn_s_setprio(3);
+        auto pace = [&](int at) {
+            if (at >= p_next) {
+                --p_lev;
+                p_next = p_lev > 0 ? p_next + quarter : kFar;
+                if (p_lev == 2) __builtin_amdgcn_s_setprio(2);
+                else if (p_lev == 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
+        };
+
         // sums slice cur.i over the slots, writes its row, moves on
         auto close = [&]() {
             T res[Sum::VO];
@@ -434,6 +458,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                     if (k + 1 < nwin) issue(std::integral_constant<int, k + 1>{});
                 }
                 const int wbase = E + 64 * k;
+                if constexpr ((k & 1) == 0) pace(wbase);
                 // (the cursor is the same in every lane; saying so keeps the
                 // branches below scalar)
                 cur.i = uni(cur.i);
