@@ -338,13 +338,14 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             const int j = cur.i - row0;
             cur.e1 = cur.i < cur.s_end && j < 64 ? readlane(RE, j) : kFar;
         };
-        // closes slice cur.i and starts the next one with v * b (the sum's
-        // tree and the next slice's products are independent, so they overlap)
-        auto close_into = [&](const T (&b)[VEC], T v) {
+        // closes slice cur.i and starts the next one with v * b in the lanes
+        // that `keep` (zero elsewhere; the sum's tree and the next slice's
+        // products are independent, so they overlap)
+        auto close_into = [&](const T (&b)[VEC], T v, bool keep) {
             T res[Sum::VO];
             slot_sum<LOG_WW, VEC>(acc, res);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] = fma_t(v, b[e], T(0));
+            for (int e = 0; e < VEC; ++e) acc[e] = keep ? fma_t(v, b[e], T(0)) : T(0);
             if (Sum::writer(lane) && act) {
                 T *o = out + (size_t)cur.i * w + col + Sum::base(lane);
                 store_vec<T, Sum::VO>(o, res);
@@ -495,10 +496,15 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                             full(bv, vt);
                             close();
                         } else {
-                            // (zero values instead of masked lanes: one
-                            // straight run of instructions)
-                            full(bv, slot < qb ? vt : T(0));
-                            close_into(bv, slot < qb ? T(0) : vt);
+                            // (selects instead of masked lanes: one
+                            // straight run of instructions; a lane holding
+                            // the other slice's entry keeps its sum as is,
+                            // so a non-finite B element or value never
+                            // reaches a slice it is not stored in)
+                            const bool mine = slot < qb;
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) acc[e] = mine ? fma_t(vt, bv[e], acc[e]) : acc[e];
+                            close_into(bv, vt, !mine);
                         }
                     });
                     return;
@@ -516,9 +522,9 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                     if (s >= stop) return;  // past the round's end
                     auto add = [&](int lo, int hi) {  // slots holding entries [lo, hi)
                         if (hi > lo) {
-                            const T vm = slot >= lo - s && slot < hi - s ? vt : T(0);
+                            const bool in = slot >= lo - s && slot < hi - s;
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e) acc[e] = fma_t(vm, b[e], acc[e]);
+                            for (int e = 0; e < VEC; ++e) acc[e] = in ? fma_t(vt, b[e], acc[e]) : acc[e];
                         }
                     };
                     int lo = s;
