@@ -324,6 +324,14 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             }
         };
 
+        // the end of slice i: lane i - row0 of RE, or past every entry when RE
+        // does not hold it (no branch: the lane is read modulo 64, then the
+        // result selected on i < s_end and i - row0 < 64 as one sign test)
+        auto end_at = [&](int i) {
+            const int j = i - row0;
+            const int r = readlane(RE, j & 63);
+            return ((i - cur.s_end) & (j - 64)) < 0 ? r : kFar;
+        };
         // sums slice cur.i over the slots, writes its row, moves on
         auto close = [&]() {
             T res[Sum::VO];
@@ -335,8 +343,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = T(0);
             ++cur.i;
-            const int j = cur.i - row0;
-            cur.e1 = cur.i < cur.s_end && j < 64 ? readlane(RE, j) : kFar;
+            cur.e1 = end_at(cur.i);
         };
         // closes slice cur.i and starts the next one with v * b in the lanes
         // that `keep` (zero elsewhere; the sum's tree and the next slice's
@@ -351,15 +358,11 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                 store_vec<T, Sum::VO>(o, res);
             }
             ++cur.i;
-            const int j = cur.i - row0;
-            cur.e1 = cur.i < cur.s_end && j < 64 ? readlane(RE, j) : kFar;
+            cur.e1 = end_at(cur.i);
         };
 
         // the end of slice cur.i + 1 (past every entry when it is not held)
-        auto next_end = [&]() {
-            const int j = cur.i + 1 - row0;
-            return cur.i + 1 < cur.s_end && j < 64 ? readlane(RE, j) : kFar;
-        };
+        auto next_end = [&]() { return end_at(cur.i + 1); };
 
         while (E < E_b) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this round's loads
@@ -479,13 +482,15 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                 }
                 // the end of the slice after the current one
                 const int e2 = next_end();
-                if (cur.e1 > wbase && rend >= wbase + 64 && e2 > wbase + 64) {
+                // (cur.e1 > wbase, rend >= wbase + 64 and e2 > wbase + 64 as
+                // one sign test, so the branch stays scalar)
+                if (((cur.e1 - wbase - 1) | (rend - wbase - 64) | (e2 - wbase - 65)) >= 0) {
                     // exactly one slice ends in the window, after entry b - 1:
                     // the step holding that entry adds its first qb slots,
                     // closes the slice, then adds the rest; every other step
                     // adds all its slots
                     const int b = cur.e1 - wbase;  // 1 .. 64
-                    const int tb = (b - 1) / G, qb = b - G * tb;
+                    const int tb = (int)((unsigned)(b - 1) >> (6 - LOG_WW)), qb = b - G * tb;
                     static_for<NSTEP>([&](auto t_c) {
                         constexpr int TT = decltype(t_c)::value;
                         const T(&bv)[VEC] = bvs[k & 1][TT];
