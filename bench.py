@@ -126,9 +126,9 @@ def ceiling_record(kernel):
 
 
 def probe_record():
-    """The measured secondary ceilings (LDS and L2 row gathers, float atomics,
-    empty launches) from the probe record in profiles/, when the probe source
-    hashes to the value recorded; else None."""
+    """The measured secondary ceilings (LDS and L2 row gathers, global and LDS
+    float atomics, empty launches) from the probe record in profiles/, when
+    the probe source hashes to the value recorded; else None."""
     h = hashlib.sha256(open(os.path.join(CSRC, "probe.hip"), "rb").read()).hexdigest()
     pat = re.compile(r"^probe-ceilings:\s*(.*)$")
     for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
@@ -160,8 +160,8 @@ def ceilings(reps=20):
     """Measured ceilings of the resources the walks use besides HBM (the
     probe kernels of libvspmm_probe.so, shaped like the aligned walk's inner
     loop): 64-byte row gathers from LDS and from global memory (L2), global
-    float atomics as a width-16 scatter issues them, and back-to-back empty
-    launches. Rates are per chip; 'us_per_6M' is the time 6,000,000 such
+    and LDS float atomics as a width-16 scatter issues them, and back-to-back
+    empty launches. Rates are per chip; 'us_per_6M' is the time 6,000,000 such
     rows (or 6M entries' adds at width 16) take at that rate."""
     import ctypes
 
@@ -217,6 +217,13 @@ def ceilings(reps=20):
         res[name] = {"G_entries_per_s": round(rate / 1e9, 3),
                      "G_instr_per_s": round(rate / 4 / 1e9, 3),
                      "us_per_6M": round(6e6 / rate * 1e6, 1)}
+    it_a = 16
+    ms = run(4, 0, 2000, it_a)
+    rate = grid * 16 * it_a * 64 / (ms * 1e-3)
+    res["lds_atomic_f32_w16_128KB_copy"] = {
+        "G_entries_per_s": round(rate / 1e9, 3),
+        "lanes_per_clk_per_CU": round(rate * 16 / (clk_ghz * 1e9 * n_cu), 3),
+        "us_per_6M": round(6e6 / rate * 1e6, 1)}
     res["empty_launch_us"] = round(1e3 * run(3, 0, 1, 0, g=1024), 2)
     return {"device_cus": n_cu, "clock_ghz_assumed": clk_ghz, "grid": grid,
             "threads_per_block": 1024, "reps": reps, "ceilings": res}

@@ -1,6 +1,6 @@
 // Measured ceilings of the resources the walks lean on besides HBM, on gfx950:
 // gathers of 64-byte rows (a width-16 float row) from LDS and from L2, global
-// float atomics, and the fixed cost of a launch. Built into
+// and LDS float atomics, and the fixed cost of a launch. Built into
 // libvspmm_probe.so, which only the benchmark's ceilings mode loads; the
 // product library does not contain or call any of this.
 //
@@ -100,6 +100,27 @@ k_atomic(float *out, const int *idx, int n_win, int iters) {
     }
 }
 
+// LDS float atomics the same way, into a per-block LDS copy of an n_rows x 16
+// float output (the scatter walk's private copy of out): in step t lane group
+// g takes the row held by lane 16g + t and adds into its 16 columns.
+__global__ void __launch_bounds__(kThreads)
+k_lds_atomic(int n_rows, const int *idx, int n_win, int iters, float *sink) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    const int lane = threadIdx.x & 63;
+    for (int k = threadIdx.x; k < n_rows * 16; k += blockDim.x) lds[k] = 0.0f;
+    __syncthreads();
+    for (int it = 0; it < iters; ++it) {
+        const int ix = window(idx, n_win, it)[lane];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int r = __builtin_amdgcn_ds_bpermute(((lane >> 4) * 16 + t) * 4, ix);
+            atomicAdd(lds + r * 16 + (lane & 15), 1.0f);
+        }
+    }
+    __syncthreads();
+    sink[blockIdx.x * blockDim.x + threadIdx.x] = lds[threadIdx.x % (n_rows * 16)];
+}
+
 __global__ void k_empty(float *sink) {
     if (sink && threadIdx.x == 0 && blockIdx.x == 0x7fffffff) sink[0] = 0;
 }
@@ -110,7 +131,8 @@ extern "C" {
 
 // kind 0: LDS gathers (mode 0, 1, 2 as k_lds_gather), table of n_rows <= 2560
 // rows; 1: global gathers; 2: global float atomics into out (n_rows x 16
-// floats); 3: empty launches. idx: n_win * 64 row numbers in [0, n_rows).
+// floats); 3: empty launches; 4: LDS float atomics into a per-block n_rows x
+// 16 copy (n_rows <= 2560). idx: n_win * 64 row numbers in [0, n_rows).
 // sink: grid * 1024 floats. Runs `reps` launches between two events on
 // `stream` and returns their total milliseconds in *ms. Returns 0, or -1 on
 // bad arguments, or the HIP error code.
@@ -124,8 +146,12 @@ int vspmm_probe(int kind, int mode, const float *table, int n_rows, const int *i
         return -1;
     if (kind == 1 && (!table || !sink)) return -1;
     if (kind == 2 && !out) return -1;
-    if (kind < 0 || kind > 3) return -1;
-    const size_t lds = kind == 0 ? (size_t)n_rows * 64 : 0;
+    if (kind == 4 && (n_rows > 2560 || !sink)) return -1;
+    if (kind < 0 || kind > 4) return -1;
+    const size_t lds = kind == 0 || kind == 4 ? (size_t)n_rows * 64 : 0;
+    if (kind == 4)
+        (void)hipFuncSetAttribute((const void *)&k_lds_atomic,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (kind == 0) {
         const void *fns[3] = {(const void *)&k_lds_gather<0>, (const void *)&k_lds_gather<1>,
                               (const void *)&k_lds_gather<2>};
@@ -144,6 +170,7 @@ int vspmm_probe(int kind, int mode, const float *table, int n_rows, const int *i
                 break;
             case 1: hipLaunchKernelGGL(k_l2_gather, g, t, 0, stream, table, idx, n_win, iters, sink); break;
             case 2: hipLaunchKernelGGL(k_atomic, g, t, 0, stream, out, idx, n_win, iters); break;
+            case 4: hipLaunchKernelGGL(k_lds_atomic, g, t, lds, stream, n_rows, idx, n_win, iters, sink); break;
             default: hipLaunchKernelGGL(k_empty, g, dim3(256), 0, stream, sink); break;
         }
     };
