@@ -710,14 +710,14 @@ k_slice_starts(int n_slices, int n_groups, const int *__restrict__ sptr,
 // bounds for any structure (group numbers clamped to [0, n_groups]); a
 // malformed one gets a meaningless plan, as its products are undefined.
 //
-// The shares are not equal. A block's waves go to the CU's four SIMDs in
-// turn, so wave k is the (4k / wpb)-th wave on its SIMD, and a SIMD issues
-// from its oldest wave first: with equal shares the first quarter of a
-// block's waves end well before the last, whose SIMDs then run with fewer
+// The shares of a 16-wave block are not equal. Its waves go to the CU's four
+// SIMDs in turn, so wave k is the (k / 4)-th wave on its SIMD, and a SIMD
+// issues from its oldest wave first: with equal shares the block's first
+// four waves end well before its last four, whose SIMDs then run with fewer
 // waves than they can overlap. Shares weighted 20 : 17 : 15 : 12 by that
 // place (with k_vcs_seg's issue priorities) let a block's waves end nearly
-// together. The weights change only which wave walks a slice, never the
-// slice's result.
+// together. Blocks of 4 waves (one per SIMD) take equal shares. The weights
+// change only which wave walks a slice, never the slice's result.
 __global__ void __launch_bounds__(256)
 k_seg_plan(int n_slices, int n_groups, const int *__restrict__ sptr,
            const int *__restrict__ vptr, const int *__restrict__ he, int tiles, int grid, int wpb,
@@ -728,8 +728,12 @@ k_seg_plan(int n_slices, int n_groups, const int *__restrict__ sptr,
     int bb, be, tile;
     seg_block_range(b, grid, tiles, n_slices, bb, be, tile);
     const int EB = he[bb], EE = he[be];
-    // share weights by a wave's place on its SIMD
-    auto weight = [&](int k) { return k * 4 < wpb ? 20 : k * 2 < wpb ? 17 : k * 4 < 3 * wpb ? 15 : 12; };
+    // share weights by a wave's place on its SIMD (blocks of 16 waves, four
+    // per SIMD; smaller blocks put one wave per SIMD and take equal shares)
+    auto weight = [&](int k) {
+        const int place = k >> 2;
+        return wpb != 16 ? 1 : place == 0 ? 20 : place == 1 ? 17 : place == 2 ? 15 : 12;
+    };
     long long w_all = 0;
     for (int k = 0; k < wpb; ++k) w_all += weight(k);
     auto first_at = [&](int k) {  // the first slice in [bb, be] starting at or after cut k
