@@ -296,9 +296,14 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
         // rows), plus, for B in LDS, the LDS address where B starts
         const uint32_t coff4 = (act ? 4u * col : 0u) + b_lds0;
         if (c0 > 0) {  // a later width pass walks the run again
-            E = E_a;
-            K = d.K_a;
-            if (E_a < E_b) {
+            // (the run's start is hidden from the compiler here, so the first
+            // round's addresses are not kept live across the whole pass for
+            // this reload)
+            int ea = E_a, ka = d.K_a;
+            asm volatile("" : "+s"(ea), "+s"(ka));
+            E = ea;
+            K = ka;
+            if (ea < E_b) {
                 load_round(E, K, W, GS, GV);
                 load_ends();
             }
