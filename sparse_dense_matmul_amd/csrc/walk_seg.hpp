@@ -218,24 +218,11 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
     const uint32_t b_lds0 =
         LDS_B ? (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem : 0u;
 
-    // B into LDS first, as direct global->LDS copies (16 bytes per lane, 1 KB
-    // per wave instruction; no registers).
     const size_t b_el = (size_t)b_rows * w;
     const bool b_dma = LDS_B && (b_el * sizeof(T)) % 16 == 0 && ((uintptr_t)B % 16) == 0;
-    if constexpr (LDS_B) {
-        if (b_dma) {
-            const int nq = (int)(b_el * sizeof(T) / 16);
-            const uint4 *src = reinterpret_cast<const uint4 *>(B);
-            for (int c = wave; c * 64 < nq; c += waves) {
-                if (c * 64 + lane < nq)
-                    __builtin_amdgcn_global_load_lds(
-                        src + c * 64 + lane,
-                        (__attribute__((address_space(3))) void *)(smem + (size_t)c * 1024), 16, 0, 0);
-            }
-        }
-    }
-    // this wave's run, planned ahead (k_seg_plan): its loads go out while B
-    // is being staged
+    // this wave's run, planned ahead (k_seg_plan); its first round's loads go
+    // out before B's copies, which would otherwise delay the plan's own load
+    // and so the whole chain
     const SegDesc d = desc[blockIdx.x * waves + wave];
     const int s_a = d.s_a, s_b = d.s_b, E_a = d.E_a, E_b = d.E_b, K_b = d.K_b;
     // lane L = q WW + t holds entry G t + q of a window; it reads its group
@@ -276,6 +263,20 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
     if (E_a < E_b) {
         load_round(E, K, W, GS, GV);
         load_ends();
+    }
+    // B into LDS as direct global->LDS copies (16 bytes per lane, 1 KB per
+    // wave instruction; no registers)
+    if constexpr (LDS_B) {
+        if (b_dma) {
+            const int nq = (int)(b_el * sizeof(T) / 16);
+            const uint4 *src = reinterpret_cast<const uint4 *>(B);
+            for (int c = wave; c * 64 < nq; c += waves) {
+                if (c * 64 + lane < nq)
+                    __builtin_amdgcn_global_load_lds(
+                        src + c * 64 + lane,
+                        (__attribute__((address_space(3))) void *)(smem + (size_t)c * 1024), 16, 0, 0);
+            }
+        }
     }
     const char *Bb = reinterpret_cast<const char *>(B);
     if constexpr (LDS_B) {
