@@ -46,9 +46,14 @@
  *  - Work is enqueued on the given stream and returns before it finishes,
  *    except vspmm_validate, which waits for its result, and
  *    vspmm_create_csr, which waits once for its list of long rows.
- *  - Handles are immutable after creation apart from the workspace cache
- *    tag (guarded by a lock), so products on different streams may run
- *    concurrently if their outputs and workspaces are distinct.
+ *  - A handle changes after creation only through vspmm_set_view. Products
+ *    on different streams may run concurrently if their outputs and
+ *    workspaces are distinct, except on a handle with a SCALE view, whose
+ *    products share the handle's scaled-input buffer.
+ *  - Non-finite values spread only through stored entries: an element of out
+ *    is NaN or +-Inf exactly when IEEE arithmetic over the entries of its own
+ *    slice makes it so (a lane that a walk pads with another slice's entry
+ *    keeps its sum, never adding zero times a non-finite B element).
  */
 #ifndef VSPMM_H
 #define VSPMM_H
