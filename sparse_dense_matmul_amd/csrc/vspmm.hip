@@ -818,50 +818,67 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     // the block's slice-header table: 8 bytes per slice, at most 2,048 slices
     // per block (blocks per tile are chosen below to keep it so)
     const size_t header_margin = 8 * (2048 + 8);
-    int64_t tr = int64_t((kLdsMax - fixed - header_margin) / row_bytes) & ~int64_t(3);
-    if (tr < 64) return tp;  // rows too wide for a useful tile
-    int64_t tiles = (ni + tr - 1) / tr;
-    // a multiple of 8 tiles lets each XCD (8 on the chip) own whole tiles,
-    // so a tile of B is fetched into one XCD's L2 instead of all eight
-    if (tiles >= 4) tiles = (tiles + 7) / 8 * 8;
-    tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);  // balanced tiles
-    // virtual slices too long for the short walk (a narrow B makes few,
-    // large tiles): more tiles, a multiple of 8, until their mean is at most
-    // 512 entries
-    if (h.nnz / std::max<int64_t>(tiles * no, 1) >= kLongMean) {
-        tiles = std::max<int64_t>(tiles, (h.nnz + no * 512 - 1) / (no * 512));
-        tiles = (tiles + 7) / 8 * 8;
-        tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);
-        if (tr < 64) return tp;
-    }
-    tiles = (ni + tr - 1) / tr;  // (rounding tr may drop one)
-    // B fits an XCD's L2 here, where the untiled walk gathers it at a fair
-    // rate: tiles pay only while their partial rows (written, then read back
-    // to be added) stay within half the matrix's own bytes (1M x 20k at width
-    // 8: 8 tiles of 1M partial rows, 512 MB, against 0.9 GB, measured 1.24
-    // ms tiled and 0.98 ms untiled)
-    const size_t partial_traffic = 2 * size_t(tiles) * size_t(no) * row_bytes;
-    const size_t matrix_bytes = 4 * size_t(h.n_major() + 1) + 8 * size_t(h.n_groups) + 4 +
-                                4 * size_t(h.nnz);
-    if (2 * partial_traffic > matrix_bytes) return tp;
-    const int64_t nv = tiles * no;
-    if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return tp;
-    const int64_t mean = h.nnz / nv;
-    if (mean < 16 || mean >= kLongMean) return tp;
-    // blocks per tile: enough to fill the chip, and enough that a block's
-    // slice-header table (8 bytes per slice, in LDS) stays at 2,048 slices
-    const int64_t bpt = std::max<int64_t>({int64_t(1), n_cu / tiles, (no + 2047) / 2048});
-    const int64_t grid = tiles * bpt;
-    if (!fits_i32(grid)) return tp;
-    const size_t b_al = (size_t(tr) * row_bytes + 15) & ~size_t(15);
-    const size_t lds = b_al + fixed + 8 * size_t(rows_header_cap(int(nv), int(grid)));
-    if (lds > kLdsMax) return tp;
-    Plan pl = make_plan(nv, h.nnz, w, 4, split_matrix, h.force_group, B, part, n_cu, tr, true);
-    if (pl.kind != kShort || pl.R != 1) return tp;
-    pl.lds = true;
-    pl.lds_bytes = lds;
-    pl.block = 1024;
-    pl.grid = int(grid);
+    const int64_t tr_max = int64_t((kLdsMax - fixed - header_margin) / row_bytes) & ~int64_t(3);
+    if (tr_max < 64) return tp;  // rows too wide for a useful tile
+    // the plan for a given least tile count (false when tiles do not pay)
+    int64_t tr = 0, tiles = 0;
+    Plan pl;
+    auto try_tiles = [&](int64_t t0, bool whole_xcds) -> bool {
+        tiles = t0;
+        // a multiple of 8 tiles lets each XCD (8 on the chip) own whole
+        // tiles, so a tile of B is fetched into one XCD's L2 instead of all
+        // eight
+        if (whole_xcds) tiles = (tiles + 7) / 8 * 8;
+        tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);  // balanced tiles
+        // virtual slices too long for the short walk (a narrow B makes few,
+        // large tiles): more tiles, a multiple of 8, until their mean is at
+        // most 512 entries
+        if (h.nnz / std::max<int64_t>(tiles * no, 1) >= kLongMean) {
+            tiles = std::max<int64_t>(tiles, (h.nnz + no * 512 - 1) / (no * 512));
+            tiles = (tiles + 7) / 8 * 8;
+            tr = (((ni + tiles - 1) / tiles) + 3) & ~int64_t(3);
+            if (tr < 64) return false;
+        }
+        tiles = (ni + tr - 1) / tr;  // (rounding tr may drop one)
+        // B fits an XCD's L2 here, where the untiled walk gathers it at a
+        // fair rate: tiles pay only while their partial rows (written, then
+        // read back to be added) stay within half the matrix's own bytes (1M
+        // x 20k at width 8: 8 tiles of 1M partial rows, 512 MB, against 0.9
+        // GB, measured 1.24 ms tiled and 0.98 ms untiled)
+        const size_t partial_traffic = 2 * size_t(tiles) * size_t(no) * row_bytes;
+        const size_t matrix_bytes = 4 * size_t(h.n_major() + 1) + 8 * size_t(h.n_groups) + 4 +
+                                    4 * size_t(h.nnz);
+        if (2 * partial_traffic > matrix_bytes) return false;
+        const int64_t nv = tiles * no;
+        if (!fits_i32(nv + 1) || ni >= (int64_t(1) << 24)) return false;
+        const int64_t mean = h.nnz / nv;
+        if (mean < 16 || mean >= kLongMean) return false;
+        // blocks per tile: enough to fill the chip, and enough that a block's
+        // slice-header table (8 bytes per slice, in LDS) stays at 2,048
+        // slices
+        const int64_t bpt = std::max<int64_t>({int64_t(1), n_cu / tiles, (no + 2047) / 2048});
+        const int64_t grid = tiles * bpt;
+        if (!fits_i32(grid)) return false;
+        const size_t b_al = (size_t(tr) * row_bytes + 15) & ~size_t(15);
+        const size_t lds = b_al + fixed + 8 * size_t(rows_header_cap(int(nv), int(grid)));
+        if (lds > kLdsMax) return false;
+        pl = make_plan(nv, h.nnz, w, 4, split_matrix, h.force_group, B, part, n_cu, tr, true);
+        if (pl.kind != kShort || pl.R != 1) return false;
+        pl.lds = true;
+        pl.lds_bytes = lds;
+        pl.block = 1024;
+        pl.grid = int(grid);
+        return true;
+    };
+    // the fewest tiles that fit LDS, as a multiple of 8 where four or more;
+    // when the partial rows of that many outweigh the matrix (a B of a few
+    // hundred KB over a million output rows), the fewest tiles as they are:
+    // such a B is cheap to fetch into every XCD's L2 (1M x 20k at width 8:
+    // 5 tiles against 8; on a 100,000 x 20,000 matrix 84 us tiled against
+    // 108 untiled)
+    const int64_t t_min = (ni + tr_max - 1) / tr_max;
+    if (!try_tiles(t_min, t_min >= 4) && !(t_min >= 4 && t_min % 8 != 0 && try_tiles(t_min, false)))
+        return tp;
     tp.ok = true;
     tp.tr = int(tr);
     tp.tiles = int(tiles);
