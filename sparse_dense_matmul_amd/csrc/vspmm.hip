@@ -805,12 +805,12 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     n_cu = std::max(n_cu, 1);
     const int64_t no = n_out(h, dir), ni = n_in(h, dir);
     const size_t row_bytes = size_t(w) * 4;
-    // B over 4 MB: L2 tiles; else rows of up to 64 bytes: LDS tiles (wider
-    // rows gather from L2 at a better rate per byte)
-    {
-        const TilePlan t2 = tile_plan_l2(h, no, ni, w, n_cu, split_matrix, B, part);
-        if (t2.ok || row_bytes > 64) return t2;
-    }
+    // rows over 64 bytes gather from L2 at a better rate per byte: L2 tiles
+    // (for a B over 4 MB); rows of up to 64 bytes: LDS tiles, or L2 tiles for
+    // a B over 4 MB when LDS tiles do not pay (1M x 20k, B @ A at width 8:
+    // 248 LDS tiles, 0.76 ms, against 16 L2 tiles, 1.04 ms)
+    if (row_bytes > 64) return tile_plan_l2(h, no, ni, w, n_cu, split_matrix, B, part);
+    const bool big_b = size_t(ni) * row_bytes > (size_t(4) << 20);
     const size_t fixed = size_t(16) * kRowsWaveLds + 16;
     // B fits whole: the plain walks stage it already
     if (size_t(ni) * row_bytes + fixed + 8 * size_t(rows_header_cap(int(std::min<int64_t>(no, kI32Max)), n_cu)) <= kLdsMax)
@@ -878,7 +878,7 @@ TilePlan tile_plan(const vspmm_matrix_s &h, int dir, int64_t w, int n_cu, bool s
     // 108 untiled)
     const int64_t t_min = (ni + tr_max - 1) / tr_max;
     if (!try_tiles(t_min, t_min >= 4) && !(t_min >= 4 && t_min % 8 != 0 && try_tiles(t_min, false)))
-        return tp;
+        return big_b ? tile_plan_l2(h, no, ni, w, n_cu, split_matrix, B, part) : tp;
     tp.ok = true;
     tp.tr = int(tr);
     tp.tiles = int(tiles);

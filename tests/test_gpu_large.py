@@ -110,10 +110,11 @@ def test_large_integer_exact(orc, large):
 @pytest.mark.parametrize("width", [8, 16, 32])
 @pytest.mark.parametrize("layout", ["vcsr", "vcsc"])
 def test_large_tiled(orc, large, layout, width):
-    """B @ A on the tiled schedule: B (1,000,000 rows, 32 / 64 / 128 MB) is
-    larger than one XCD's L2, so it is cut into L2 tiles of ~2 MB: 16 tiles at
-    width 8 (320,000 virtual slices of ~625 entries), 32 at width 16, 64 at
-    width 32, one XCD's worth of blocks per tile."""
+    """B @ A on the tiled schedule: B (1,000,000 rows, 32 / 64 / 128 MB) is cut
+    into tiles: at width 8 into 248 LDS tiles (~5M virtual slices of ~40
+    entries, their partial rows within half the matrix's bytes); at widths 16
+    and 32, where LDS tiles' partial rows would outweigh that, into L2 tiles of
+    ~2 MB (32 and 64), one XCD's worth of blocks per tile."""
     L, dev = large["L"], large["dev"]
     A = large[layout]
     want = large["want"]["BA"]
