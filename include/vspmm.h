@@ -220,19 +220,21 @@ vspmm_status vspmm_workspace_size(vspmm_matrix h, vspmm_direction dir, vspmm_mod
  * for this width, deterministic mode instead builds a tiled copy of the
  * matrix: B's rows are cut into tiles and each output row's entries are split
  * by tile, every (tile, output row) part grouped by value as in the pages'
- * value-grouped layouts. A B larger than 4 MB is cut into tiles of about
- * 2 MB, a multiple of 8 of them, each fitting one XCD's L2: the blocks of a
- * tile, all on one XCD and as many as the XCD holds at once, gather it from
- * global memory. A smaller B with rows of up to 64 bytes is cut into tiles
- * that fit in LDS, and each block stages its tile there, as long as the
+ * value-grouped layouts. With rows of up to 64 bytes, B is cut into tiles
+ * that fit in LDS and each block stages its tile there, as long as the
  * partial rows the tiles write and read back stay within half the matrix's
- * own bytes (otherwise the untiled walk gathers B from L2); where the fewest such
+ * own bytes: the fewest such tiles, rounded up to a multiple of 8 (each XCD
+ * then owns whole tiles) when there are four or more, or left as they are
+ * when only that count keeps the partial rows within bounds; where the fewest
  * tiles would leave (tile, output row) parts of 1,024 entries or more on
  * average, the tile count rises to a multiple of 8 until the mean is at most
- * 512. The
- * product writes one partial row per (tile, output row) into ws and adds them
- * in a fixed order; it repeats bit for bit. A smaller ws falls back to the
- * path above (aligned: the plain walk, ws unused).
+ * 512. Otherwise (wider rows, or LDS tiles that do not pay) a B larger than
+ * 4 MB is cut into tiles of about 2 MB, a multiple of 8 of them, each fitting
+ * one XCD's L2: the blocks of a tile, all on one XCD and as many as the XCD
+ * holds at once, gather it from global memory; a smaller B is gathered
+ * untiled from L2. The product writes one partial row per (tile, output row)
+ * into ws and adds them in a fixed order; it repeats bit for bit. A smaller ws
+ * falls back to the path above (aligned: the plain walk, ws unused).
  *
  * ws: device, 256-byte aligned, at least vspmm_workspace_size bytes; unused
  * (may be NULL) when the size is 0. Errors: as vspmm_spmm, plus
