@@ -750,18 +750,18 @@ struct TilePlan {
     int tiles = 0;
     int64_t n_out = 0;   // output rows (virtual slices per tile)
     int64_t n_in = 0;    // B's rows
-    Plan pl;             // the k_vcs_rows launch over the tiled layout
+    Plan pl;             // the short walk's launch over the tiled layout
     int64_t n_bins() const { return int64_t(tiles) * n_out; }
 };
 
 // A B larger than one XCD's L2 (4 MB) is fetched from the Infinity Cache by
 // every XCD when the walk gathers from global memory, and cut into LDS tiles
-// it needs so many tiles that their partial rows (written and read back per
-// (tile, output row)) outweigh the matrix. L2 tiles: B cut into a multiple of
-// 8 tiles of about 2 MB, the blocks of a tile on one XCD (as for LDS tiles),
-// as many blocks per tile as one XCD holds at once, so an XCD walks its tiles
-// one after another with one tile in its L2; the walk gathers from global
-// memory.
+// it may need so many tiles that their partial rows (written and read back
+// per (tile, output row)) outweigh the matrix, or its rows may be too wide for
+// LDS tiles to pay. L2 tiles: B cut into a multiple of 8 tiles of about 2 MB,
+// the blocks of a tile on one XCD (as for LDS tiles), as many blocks per tile
+// as one XCD holds at once, so an XCD walks its tiles one after another with
+// one tile in its L2; the walk gathers from global memory.
 TilePlan tile_plan_l2(const vspmm_matrix_s &h, int64_t no, int64_t ni, int64_t w, int n_cu,
                       bool split_matrix, const void *B, const void *part) {
     TilePlan tp;
