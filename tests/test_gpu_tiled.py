@@ -31,7 +31,7 @@ def count60k():
 
 @pytest.fixture(scope="module")
 def ragged():
-    """50,003 x 1,500, Poisson(60) per row: the last of 23 tiles is short;
+    """50,003 x 1,500, Poisson(60) per row: the last of the tiles is short;
     runs of 70 empty groups inserted in some slices."""
     t = W.count_matrix(50_003, 1_500, 60.0, 255, W.rng_for(43))
     out = {lay: W.build_vcs(t, lay) for lay in ("vcsr", "vcsc")}
@@ -120,6 +120,36 @@ def test_tiled_ragged(orc, ragged, name, direction, width):
             assert np.array_equal(out.cpu().numpy().astype(np.float64), want), name
         else:
             check_close(orc, L, direction, B, out, where=f"ragged {name}")
+
+
+@pytest.fixture(scope="module")
+def tall():
+    """50,000 x 20,000, Poisson(200) per row (~10M entries): at width 8 its
+    B (640 KB) needs 5 LDS tiles, and 8 (a multiple of 8) would write more
+    partial rows than half the matrix's bytes."""
+    t = W.count_matrix(50_000, 20_000, 200.0, 64, W.rng_for(47))
+    return {lay: W.build_vcs(t, lay) for lay in ("vcsr", "vcsc")}
+
+
+@pytest.mark.parametrize("layout,direction", [("vcsr", "AB"), ("vcsc", "AB")])
+def test_unrounded_tile_count(orc, tall, layout, direction):
+    """The fewest LDS tiles as they are (5) when a multiple of 8 does not pay:
+    VCSR@B (aligned) and VCSC@B (misaligned) at width 8, deterministic mode,
+    against the float64 oracle, bit for bit on repeat and through a schedule,
+    and exactly on integer data."""
+    dev = need_gpu()
+    L = tall[layout]
+    A = vcs_handle(L, dev)
+    info = A.plan_info(8, direction, "deterministic")
+    assert info["tiles"] == 5 and info["kernel_name"] == "k_vcs_seg" and info["lds_staged"] == 1
+    B, out, ws = run_det(A, L, direction, 8, seed=3)
+    check_close(orc, L, direction, B, out, where=f"5 tiles {layout} {direction}")
+    Bd = to_dev(B, dev)
+    again = A.spmm(Bd, direction, mode="deterministic", workspace=ws)
+    assert torch.equal(again.view(torch.int32), out.view(torch.int32))
+    assert torch.equal(A.schedule(direction, 8).spmm(Bd).view(torch.int32), out.view(torch.int32))
+    Bi, outi, _ = run_det(A, L, direction, 8, seed=4, ws=ws, integer=True)
+    assert np.array_equal(outi.cpu().numpy().astype(np.float64), orc.spmm(L, direction, Bi))
 
 
 def test_workspace_shared_across_widths(orc, count60k):
