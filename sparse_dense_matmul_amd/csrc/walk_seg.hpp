@@ -338,7 +338,8 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             const int r = readlane(RE, j & 63);
             return ((i - cur.s_end) & (j - 64)) < 0 ? r : kFar;
         };
-        // sums slice cur.i over the slots, writes its row, moves on
+        // sums slice cur.i over the slots, writes its row, moves on (close
+        // leaves cur.e1 as it was; close_track looks up the next end)
         auto close = [&]() {
             T res[Sum::VO];
             slot_sum<LOG_WW, VEC>(acc, res);
@@ -349,6 +350,9 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[e] = T(0);
             ++cur.i;
+        };
+        auto close_track = [&]() {
+            close();
             cur.e1 = end_at(cur.i);
         };
         // closes slice cur.i and starts the next one with v * b in the lanes
@@ -364,11 +368,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                 store_vec<T, Sum::VO>(o, res);
             }
             ++cur.i;
-            cur.e1 = end_at(cur.i);
         };
-
-        // the end of slice cur.i + 1 (past every entry when it is not held)
-        auto next_end = [&]() { return end_at(cur.i + 1); };
 
         while (E < E_b) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this round's loads
@@ -393,7 +393,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             // 64 or more empty slices at E (every slice RE holds ends at or
             // before E): close them and load the ends from the next slice
             while (readlane(RE, 63) <= E && cur.i < cur.s_end) {
-                while (cur.e1 <= E) close();
+                while (cur.e1 <= E) close_track();
                 row0 = cur.i;
                 RE = he[min(row0 + 1 + lane, s_b)];
                 __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -419,6 +419,17 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                                   gvt);
 
             const int nwin = (rend - E + 63) >> 6;
+            // where the slices closing in this round end: lane j of wv holds
+            // the window of slice row0 + j's last entry (NWR when the slice
+            // does not close in this round, or ends at or before E: an empty
+            // slice at the round's start). Bit k of `whole` says that window
+            // k lies inside the round and no slice ends in it at or before
+            // its start (only window 0 can hold such an end).
+            const bool closes = lane < cur.s_end - row0 && RE <= rend;
+            const int wv = closes && RE > E ? (RE - 1 - E) >> 6 : NWR;
+            const int nfull = (rend - E) >> 6;
+            int whole = nfull >= NWR ? (1 << NWR) - 1 : (1 << nfull) - 1;
+            if (__ballot(closes && RE <= E) != 0) whole &= ~1;
             // the value of every window's entries, for the whole round at
             // once (independent chains): each window's group numbers by a
             // max-scan of its marks, raised to the last number of the windows
@@ -472,13 +483,14 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                 // (the cursor is the same in every lane; saying so keeps the
                 // branches below scalar)
                 cur.i = uni(cur.i);
-                cur.e1 = uni(cur.e1);
                 const T v = V[k];
                 auto full = [&](const T(&b)[VEC], T vt) {
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) acc[e] = fma_t(vt, b[e], acc[e]);
                 };
-                if (min(cur.e1, rend) > wbase + 64) {
+                // the slices (lanes of RE) whose last entry is in this window
+                const uint64_t em = (whole >> k) & 1 ? __ballot(wv == k) : ~0ull;
+                if (em == 0) {
                     // every step inside the current slice and round
                     static_for<NSTEP>([&](auto t_c) {
                         constexpr int TT = decltype(t_c)::value;
@@ -486,42 +498,56 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                     });
                     return;
                 }
-                // the end of the slice after the current one
-                const int e2 = next_end();
-                // (cur.e1 > wbase, rend >= wbase + 64 and e2 > wbase + 64 as
-                // one sign test, so the branch stays scalar)
-                if (((cur.e1 - wbase - 1) | (rend - wbase - 64) | (e2 - wbase - 65)) >= 0) {
-                    // exactly one slice ends in the window, after entry b - 1:
-                    // the step holding that entry adds its first qb slots,
-                    // closes the slice, then adds the rest; every other step
-                    // adds all its slots
-                    const int b = cur.e1 - wbase;  // 1 .. 64
+                if ((em & (em - 1)) == 0) {
+                    // exactly one slice (cur.i) ends in the window, after
+                    // entry b - 1: the step holding that entry adds its first
+                    // qb slots, closes the slice, then adds the rest; every
+                    // other step adds all its slots
+                    const int b = readlane(RE, (int)__builtin_ctzll(em)) - wbase;  // 1 .. 64
                     const int tb = (int)((unsigned)(b - 1) >> (6 - LOG_WW)), qb = b - G * tb;
-                    static_for<NSTEP>([&](auto t_c) {
-                        constexpr int TT = decltype(t_c)::value;
-                        const T(&bv)[VEC] = bvs[k & 1][TT];
-                        const T vt = group_bcast<LOG_WW, TT>(v);
-                        if (TT != tb) {
-                            full(bv, vt);
-                        } else if (qb == G) {
-                            full(bv, vt);
-                            close();
-                        } else {
-                            // (selects instead of masked lanes: one
-                            // straight run of instructions; a lane holding
-                            // the other slice's entry keeps its sum as is,
-                            // so a non-finite B element or value never
-                            // reaches a slice it is not stored in)
-                            const bool mine = slot < qb;
+                    // the step holding the end: slots below qb add their
+                    // entry to the closing slice, the others start the next
+                    // one (selects instead of masked lanes: a lane holding
+                    // the other slice's entry keeps its sum as is, so a
+                    // non-finite B element or value never reaches a slice
+                    // it is not stored in; qb = G needs no case of its own)
+                    auto split = [&](const T(&bv)[VEC], T vt) {
+                        const bool mine = slot < qb;
 #pragma unroll
-                            for (int e = 0; e < VEC; ++e) acc[e] = mine ? fma_t(vt, bv[e], acc[e]) : acc[e];
-                            close_into(bv, vt, !mine);
-                        }
-                    });
+                        for (int e = 0; e < VEC; ++e) acc[e] = mine ? fma_t(vt, bv[e], acc[e]) : acc[e];
+                        close_into(bv, vt, !mine);
+                    };
+                    // one straight run of steps per split step (few steps
+                    // per window: no merges between the steps)
+                    auto run = [&](auto tb_c) {
+                        constexpr int TB = decltype(tb_c)::value;
+                        static_for<NSTEP>([&](auto t_c) {
+                            constexpr int TT = decltype(t_c)::value;
+                            if constexpr (TT == TB) split(bvs[k & 1][TT], group_bcast<LOG_WW, TT>(v));
+                            else full(bvs[k & 1][TT], group_bcast<LOG_WW, TT>(v));
+                        });
+                    };
+                    if constexpr (NSTEP <= 8) {
+                        bool done = false;
+                        static_for<NSTEP>([&](auto tb_c) {
+                            constexpr int TB = decltype(tb_c)::value;
+                            if (!done && (TB + 1 == NSTEP || tb == TB)) {
+                                run(tb_c);
+                                done = true;
+                            }
+                        });
+                    } else {
+                        static_for<NSTEP>([&](auto t_c) {
+                            constexpr int TT = decltype(t_c)::value;
+                            if (TT != tb) full(bvs[k & 1][TT], group_bcast<LOG_WW, TT>(v));
+                            else split(bvs[k & 1][TT], group_bcast<LOG_WW, TT>(v));
+                        });
+                    }
                     return;
                 }
                 // several slice ends, empty slices, or the round's end: step
                 // by step
+                cur.e1 = end_at(cur.i);
                 static_for<NSTEP>([&](auto t_c) {
                     constexpr int TT = decltype(t_c)::value;
                     const T (&b)[VEC] = bvs[k & 1][TT];
@@ -542,7 +568,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                     while (cur.e1 <= stop) {
                         add(lo, cur.e1);
                         lo = max(lo, cur.e1);
-                        close();
+                        close_track();
                     }
                     add(lo, stop);
                 });
