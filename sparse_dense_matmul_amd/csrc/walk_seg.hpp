@@ -106,6 +106,15 @@ __device__ __forceinline__ void gather(const char *Bg, uint32_t off, float (&r)[
     }
 }
 
+// a * b + c, fused, into a register of its own (the three-address form; the
+// compiler keeps a chain of fused adds in one register, and where a window's
+// paths merge it then copies the sums to where the other paths left theirs)
+__device__ __forceinline__ float fma_to(float a, float b, float c) {
+    float d;
+    asm("v_fma_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 // The value of the first active lane (for values every lane holds alike,
 // e.g. read from one LDS address: the compiler then keeps them in scalar
 // registers and branches on them without masks).
@@ -241,15 +250,32 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
         }
     };
     // round state: entries [E, ...) with groups from K; windows W and group
-    // starts/values GS, GV (group K + 64 j + lane), loaded a round ahead
+    // starts/values GS, GV (group K + 64 j + lane), loaded a round ahead.
+    // The loads go through raw buffers based at the round's first entry and
+    // group: a load past a buffer's end (past the run) returns 0 and reads no
+    // memory, so no lane clamps its address, and the offsets of the windows
+    // and group rows are immediates. An index read as 0 gathers row 0 of B,
+    // which no slice adds; group starts past the run are set at the round's
+    // start (fix_starts).
+    auto buf = [](const void *p, int n) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 4 * n, 0x00020000);
+    };
     auto load_round = [&](int E0, int K0, int (&Wd)[NWR], int (&GSd)[GWR], T (&GVd)[GWR]) {
+        const auto ri = buf(idx + E0, min(E_b - E0, 64 * NWR));
 #pragma unroll
-        for (int k = 0; k < NWR; ++k) Wd[k] = idx[min(E0 + 64 * k + perm, E_b - 1)];
+        for (int k = 0; k < NWR; ++k) Wd[k] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, perm4 + 256 * k, 0, 0);
+        const auto rg = buf(vptr + K0, min(K_b - K0 + 1, 64 * GWR));
+        const auto rv = buf(vals + K0, min(K_b - K0, 64 * GWR));
 #pragma unroll
         for (int j = 0; j < GWR; ++j) {
-            GSd[j] = vptr[min(K0 + 64 * j + lane, K_b)];
-            GVd[j] = vals[max(min(K0 + 64 * j + lane, K_b - 1), 0)];
+            GSd[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(rg, 4 * lane + 256 * j, 0, 0);
+            GVd[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, 4 * lane + 256 * j, 0, 0));
         }
+    };
+    // group starts past the run's last group (read as 0) lie past every entry
+    auto fix_starts = [&](int K0, int (&GSd)[GWR]) {
+#pragma unroll
+        for (int j = 0; j < GWR; ++j) GSd[j] = K0 + 64 * j + lane <= K_b ? GSd[j] : kFar;
     };
     int E = E_a, K = d.K_a;
     int W[NWR], GS[GWR];
@@ -372,6 +398,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
 
         while (E < E_b) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this round's loads
+            fix_starts(K, GS);
             // the current slice is the first one RE holds (row0): its end
             // (a round that closed all 64 slices it held left kFar in e1)
             cur.e1 = cur.i < cur.s_end ? readlane(RE, 0) : kFar;
@@ -475,9 +502,7 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
             static_for<NWR>([&](auto k_c) {
                 constexpr int k = decltype(k_c)::value;
                 if (k >= nwin) return;
-                if constexpr (k + 1 < NWR) {
-                    if (k + 1 < nwin) issue(std::integral_constant<int, k + 1>{});
-                }
+                if constexpr (k + 1 < NWR) issue(std::integral_constant<int, k + 1>{});
                 const int wbase = E + 64 * k;
                 if constexpr ((k & 1) == 0) pace(wbase);
                 // (the cursor is the same in every lane; saying so keeps the
@@ -491,10 +516,17 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                 // the slices (lanes of RE) whose last entry is in this window
                 const uint64_t em = (whole >> k) & 1 ? __ballot(wv == k) : ~0ull;
                 if (em == 0) {
-                    // every step inside the current slice and round
+                    // every step inside the current slice and round (the
+                    // last one into fresh registers)
                     static_for<NSTEP>([&](auto t_c) {
                         constexpr int TT = decltype(t_c)::value;
-                        full(bvs[k & 1][TT], group_bcast<LOG_WW, TT>(v));
+                        const T vt = group_bcast<LOG_WW, TT>(v);
+                        if constexpr (TT + 1 < NSTEP) {
+                            full(bvs[k & 1][TT], vt);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) acc[e] = fma_to(vt, bvs[k & 1][TT][e], acc[e]);
+                        }
                     });
                     return;
                 }
@@ -513,8 +545,10 @@ k_vcs_seg(int n_slices, const int *__restrict__ sptr, const int *__restrict__ vp
                     // it is not stored in; qb = G needs no case of its own)
                     auto split = [&](const T(&bv)[VEC], T vt) {
                         const bool mine = slot < qb;
+                        if (mine) {
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e) acc[e] = mine ? fma_t(vt, bv[e], acc[e]) : acc[e];
+                            for (int e = 0; e < VEC; ++e) acc[e] = fma_t(vt, bv[e], acc[e]);
+                        }
                         close_into(bv, vt, !mine);
                     };
                     // one straight run of steps per split step (few steps
