@@ -23,7 +23,12 @@
 //  - a step entirely inside one slice is a gather and VEC fused multiply-adds
 //    per lane, with no masks. A step holding a slice end adds the lanes before
 //    the end, sums the G slots (SlotSum: two permlane swap levels, then DPP),
-//    writes the row, and goes on with the lanes after it.
+//    writes the row, and goes on with the lanes after it;
+//  - each round notes, for every slice that closes in it, the window holding
+//    its last entry; a window's ballot of that number picks its path: no end
+//    (plain steps), one end (a straight-line copy of the window for the step
+//    that holds it), or several ends, empty slices or the round's partial last
+//    window (step by step).
 //
 // A wave's issue priority falls as it gets through its run (3 in the first
 // quarter, 0 in the last): a SIMD otherwise issues from its oldest wave
