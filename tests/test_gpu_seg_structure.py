@@ -13,7 +13,7 @@ groups, empty groups between a slice's groups, and one slice with a run of
 140 empty groups (more than a round's 127 held groups). 20,000 x 2,000,
 about 1.2M entries, so the per-wave runs start and end all over this mix.
 VCSR@B (B staged in LDS) and B@VCSC (the same walk over the other layout) at
-widths 1, 8 and 16."""
+widths 1, 8 and 16; then every direction through its deterministic schedule."""
 
 import numpy as np
 import pytest
@@ -104,3 +104,25 @@ def test_window_paths_exact(orc, mats, layout, width):
     ref = orc.spmm(L, direction, B)
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{layout} {direction} w={width}: {len(bad)} outputs differ, e.g. {bad[:4].tolist()}"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("width", [1, 16])
+@pytest.mark.parametrize("direction", ["AB", "BA"])
+@pytest.mark.parametrize("layout", ["vcsr", "vcsc"])
+def test_schedules_exact(orc, mats, layout, direction, width):
+    """The same matrices through a deterministic schedule in every direction
+    (the regrouped layout, or the tiled copy whose virtual slices cut the
+    slices again), exact on integer data."""
+    dev = need_gpu()
+    L = mats[layout]
+    A = vcs_handle(L, dev)
+    rows, _ = dims(L, direction)
+    B = W.dense_int(np.random.default_rng([width, len(layout), ord(direction[0])]), rows, width)
+    sc = A.schedule(direction, width)
+    got = sc.spmm(to_dev(B, dev)).cpu().numpy().astype(np.float64)
+    ref = orc.spmm(L, direction, B)
+    bad = np.argwhere(got != ref)
+    info = A.plan_info(width, direction, "deterministic")
+    assert bad.size == 0, (f"{layout} {direction} w={width} ({info['kernel_name']}, {info['tiles']} tiles): "
+                           f"{len(bad)} outputs differ, e.g. {bad[:4].tolist()}")
